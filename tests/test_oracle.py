@@ -1,0 +1,428 @@
+"""Pins for the CPU oracle (no GPU needed).
+
+Each test checks the oracle against something other than itself: values the
+pages print (tests/golden), closed forms, exact rational arithmetic, library
+conversions (numpy float16, torch bfloat16, numpy float64 matmul) and brute
+force on tiny inputs.  A plausible slip anywhere in the oracle -- a wrong table
+entry, swapped nibbles, a dropped offset, a fused multiply-add, a wrong
+block/group index, a truncating conversion, a transposed GEMV -- fails at least
+one of them.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+# ----------------------------------------------------------------------------
+# helpers independent of the oracle
+# ----------------------------------------------------------------------------
+
+
+def round_fraction(x: Fraction, mant: int = 23, emin: int = -126) -> Fraction:
+    """Exact round-to-nearest-even of a rational to a binary format with `mant`
+    fraction bits (default: IEEE single), no overflow handling."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    # floor(log2(a)) by integer bit lengths, then fix up
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    q = Fraction(2) ** (e - mant)
+    m = a / q
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * q
+
+
+def f16_value(bits: int) -> Fraction:
+    return Fraction(float(np.array([bits], np.uint16).view(np.float16)[0]))
+
+
+def bf16_bits_torch(a: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def f16_bits_numpy(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, np.float32).astype(np.float16).view(np.uint16)
+
+
+def make_q(packed, absmax_q, absmax2, code2, offset, n, bs, s2):
+    return oracle.Quantized(np.ascontiguousarray(packed, np.uint8),
+                            np.ascontiguousarray(absmax_q, np.uint8),
+                            np.ascontiguousarray(absmax2, np.uint16),
+                            np.ascontiguousarray(code2, np.uint16),
+                            float(np.float32(offset)), n, bs, s2)
+
+
+@pytest.fixture(scope="module")
+def page_table(nf4_literals_8dp):
+    return np.array([np.float32(v) for v in nf4_literals_8dp], np.float32)
+
+
+# ----------------------------------------------------------------------------
+# NF4 table
+# ----------------------------------------------------------------------------
+
+
+def test_nf4_table_equals_blog_literals(page_table):
+    t = oracle.nf4_table()
+    assert t.view(np.uint32).tolist() == page_table.view(np.uint32).tolist()
+
+
+def test_nf4_table_rounds_to_report_values(nf4_literals_4dp):
+    # the two pages print the same table at different precisions
+    t = oracle.nf4_table()
+    for i, s in enumerate(nf4_literals_4dp):
+        assert round(float(t[i]), 4) == pytest.approx(float(s), abs=1e-12), i
+
+
+def test_nf4_table_invariants():
+    t = oracle.nf4_table()
+    assert t.view(np.uint32)[7] == 0          # exactly +0
+    assert t[0] == -1.0 and t[15] == 1.0      # endpoints
+    assert np.all(np.diff(t) > 0)             # strictly increasing
+    assert (t < 0).sum() == 7 and (t > 0).sum() == 8
+
+
+def test_largest_nf4_gap():
+    t = oracle.nf4_table().astype(np.float64)
+    gaps = np.diff(t)
+    assert int(np.argmax(gaps)) == 0          # between -1 and the next code
+    assert gaps.max() == pytest.approx(0.3038072, abs=1e-7)
+
+
+# ----------------------------------------------------------------------------
+# 16-bit conversions
+# ----------------------------------------------------------------------------
+
+EDGE_F32 = np.array([
+    0.0, -0.0, 1.0, -1.0, 65504.0, 65519.996, 65520.0, -65520.0, 65536.0, 1e30, -1e30,
+    2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 2.0 ** -15,
+    1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8,
+    1.0 + 2.0 ** -8 + 2.0 ** -20, 3.3895314e38, 3.4028235e38, 1e-40, -1e-45, 1e-38,
+    np.inf, -np.inf, 0.1, -0.3, 1234.5678,
+], np.float32)
+
+
+def _random_f32(n, seed):
+    bits = np.random.default_rng(seed).integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    return f[np.isfinite(f)]
+
+
+def test_fp16_rne_matches_numpy():
+    with np.errstate(over="ignore"):
+        for a in (EDGE_F32, _random_f32(1_000_000, 11),
+                  np.random.default_rng(12).standard_normal(200_000).astype(np.float32) * 1e3):
+            assert np.array_equal(oracle.f16_from_f32(a), f16_bits_numpy(a))
+
+
+def test_bf16_rne_matches_torch():
+    for a in (EDGE_F32, _random_f32(1_000_000, 13)):
+        assert np.array_equal(oracle.bf16_from_f32(a), bf16_bits_torch(a))
+
+
+def test_fp16_decode_exhaustive():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float64)
+    got = oracle.f16_to_f64(h)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    assert np.all(np.isinf(got[np.isinf(ref)])) and np.all(np.isnan(got[np.isnan(ref)]))
+
+
+def test_bf16_decode_matches_torch():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_f64_scalar(int(v)) for v in b[::37]])
+    r = ref[::37]
+    fin = np.isfinite(r)
+    assert np.array_equal(got[fin], r[fin])
+
+
+# ----------------------------------------------------------------------------
+# code2
+# ----------------------------------------------------------------------------
+
+
+def test_code2_linear_is_nearest_fp16_of_even_grid():
+    c = oracle.code2_linear()
+    vals = c.view(np.float16).astype(np.float64)
+    assert vals[0] == -1.0 and vals[255] == 1.0
+    assert np.all(np.diff(vals) > 0)
+    for i in range(256):
+        target = Fraction(-1) + Fraction(2 * i, 255)
+        here = Fraction(float(vals[i]))
+        up = Fraction(float(np.nextafter(np.float16(vals[i]), np.float16(2))))
+        dn = Fraction(float(np.nextafter(np.float16(vals[i]), np.float16(-2))))
+        assert abs(here - target) <= abs(up - target) and abs(here - target) <= abs(dn - target)
+
+
+# ----------------------------------------------------------------------------
+# dequant
+# ----------------------------------------------------------------------------
+
+F16_ONE = 0x3C00
+
+
+def test_exhaustive_byte_decode(page_table):
+    """All 256 packed bytes with absmax_real = 1: the even element is the high
+    nibble, the odd element the low nibble (NF4 report §2.2, step 1)."""
+    code2 = np.zeros(256, np.uint16)
+    code2[200] = F16_ONE
+    packed = np.arange(256, dtype=np.uint8)
+    q = make_q(packed, np.full(8, 200, np.uint8), np.array([F16_ONE], np.uint16), code2, 0.0,
+               512, 64, 256)
+    v = oracle.dequant_f32(q)
+    expect = np.empty(512, np.float32)
+    expect[0::2] = page_table[np.arange(256) >> 4]
+    expect[1::2] = page_table[np.arange(256) & 15]
+    assert np.array_equal(v.view(np.uint32), expect.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,bs,s2", [(4096, 64, 4), (1000, 64, 4), (777, 32, 2), (65, 64, 256),
+                                     (2, 64, 256), (64 * 256 * 3 + 64, 64, 256), (300, 2, 8),
+                                     (513, 128, 2)])
+def test_dequant_index_math_closed_form(n, bs, s2):
+    """code2[i] = i, absmax2[g] = 2^g, offset = 1/2 and every code = 15 (value
+    1): element e must read exactly absmax_q[e // bs] * 2^((e // bs) // s2) + 1/2."""
+    nb = (n + bs - 1) // bs
+    ng = (nb + s2 - 1) // s2
+    code2 = np.arange(256, dtype=np.float32).astype(np.float16).view(np.uint16)
+    absmax2 = (2.0 ** (np.arange(ng) % 12)).astype(np.float16).view(np.uint16)
+    rng = np.random.default_rng(n)
+    absmax_q = rng.integers(0, 256, nb).astype(np.uint8)
+    packed = np.full((n + 1) // 2, 0xFF, np.uint8)
+    q = make_q(packed, absmax_q, absmax2, code2, 0.5, n, bs, s2)
+    v = oracle.dequant_f32(q).astype(np.float64)
+    e = np.arange(n)
+    blk = e // bs
+    expect = absmax_q[blk].astype(np.float64) * 2.0 ** ((blk // s2) % 12) + 0.5
+    assert np.array_equal(v, expect)
+    # code 0 is -1 and code 7 is +0 times the same scale
+    q0 = make_q(np.zeros_like(packed), absmax_q, absmax2, code2, 0.5, n, bs, s2)
+    assert np.array_equal(oracle.dequant_f32(q0).astype(np.float64), -expect)
+    q7 = make_q(np.full_like(packed, 0x77), absmax_q, absmax2, code2, 0.5, n, bs, s2)
+    assert np.all(oracle.dequant_f32(q7).view(np.uint32) == 0)
+
+
+def _random_format(rng, n, bs, s2):
+    nb = (n + bs - 1) // bs
+    ng = (nb + s2 - 1) // s2
+    packed = rng.integers(0, 256, (n + 1) // 2).astype(np.uint8)
+    absmax_q = rng.integers(0, 256, nb).astype(np.uint8)
+    # fp16 scales spread over many binades, including subnormals and negatives
+    a2 = (rng.standard_normal(ng) * 2.0 ** rng.integers(-20, 8, ng)).astype(np.float16)
+    code2 = (rng.standard_normal(256) * 2.0 ** rng.integers(-6, 3, 256)).astype(np.float16)
+    off = np.float32(rng.standard_normal() * 0.05)
+    return packed, absmax_q, a2.view(np.uint16), code2.view(np.uint16), off
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_dequant_matches_exact_rational(seed, page_table):
+    """Brute force in exact rationals: product rounded to fp32, plus offset
+    rounded to fp32, times the NF4 value rounded to fp32; then the 16-bit
+    outputs equal numpy's (fp16) and torch's (bf16) RNE casts of that value."""
+    rng = np.random.default_rng(100 + seed)
+    n, bs, s2 = 1501, 64, 4
+    packed, absmax_q, absmax2, code2, off = _random_format(rng, n, bs, s2)
+    q = make_q(packed, absmax_q, absmax2, code2, off, n, bs, s2)
+    got = oracle.dequant_f32(q)
+    offF = Fraction(float(off))
+    expect = np.empty(n, np.float32)
+    for e in range(n):
+        blk = e // bs
+        c = f16_value(int(code2[absmax_q[blk]]))
+        g = f16_value(int(absmax2[blk // s2]))
+        a = round_fraction(round_fraction(c * g) + offF)
+        byte = int(packed[e // 2])
+        nib = byte >> 4 if e % 2 == 0 else byte & 15
+        prod = round_fraction(Fraction(float(page_table[nib])) * a)
+        if prod == 0:   # IEEE: +0 times a negative scale is -0
+            prod_f = np.float32(-0.0) if a < 0 else np.float32(0.0)
+        else:
+            prod_f = np.float32(float(prod))
+        expect[e] = prod_f
+    assert np.array_equal(got.view(np.uint32), expect.view(np.uint32))
+    assert np.array_equal(oracle.dequant(q, oracle.BF16), bf16_bits_torch(expect))
+    with np.errstate(over="ignore"):
+        assert np.array_equal(oracle.dequant(q, oracle.FP16), f16_bits_numpy(expect))
+
+
+def test_dequant_special_cases(page_table):
+    n, bs, s2 = 640, 64, 4
+    rng = np.random.default_rng(7)
+    packed = rng.integers(0, 256, n // 2).astype(np.uint8)
+    nib = np.empty(n, np.int64)
+    nib[0::2] = packed >> 4
+    nib[1::2] = packed & 15
+    nb, ng = n // bs, (n // bs + s2 - 1) // s2
+    absmax_q = rng.integers(0, 256, nb).astype(np.uint8)
+    code2 = oracle.code2_linear()
+    # absmax2 = 0: only the offset survives
+    off = np.float32(0.0371)
+    q = make_q(packed, absmax_q, np.zeros(ng, np.uint16), code2, off, n, bs, s2)
+    assert np.array_equal(oracle.dequant_f32(q), page_table[nib] * off)
+    # offset = 0, code2 = +-1, absmax2 = power of two: plain two-level product
+    c2 = np.where(np.arange(256) < 128, -1.0, 1.0).astype(np.float16).view(np.uint16)
+    a2 = (2.0 ** -np.arange(1, ng + 1)).astype(np.float16).view(np.uint16)
+    q = make_q(packed, absmax_q, a2, c2, 0.0, n, bs, s2)
+    blk = np.arange(n) // bs
+    sgn = np.where(absmax_q[blk] < 128, -1.0, 1.0)
+    expect = page_table[nib].astype(np.float64) * sgn * 2.0 ** -((blk // s2) + 1)
+    assert np.array_equal(oracle.dequant_f32(q).astype(np.float64), expect)
+    # a negative absmax_real turns the zero code into -0
+    c2n = np.full(256, 0xBC00, np.uint16)  # -1
+    q = make_q(np.full(n // 2, 0x77, np.uint8), absmax_q, np.full(ng, F16_ONE, np.uint16), c2n,
+               0.0, n, bs, s2)
+    assert np.all(oracle.dequant_f32(q).view(np.uint32) == 0x80000000)
+    assert np.all(oracle.dequant(q, oracle.BF16) == 0x8000)
+    assert np.all(oracle.dequant(q, oracle.FP16) == 0x8000)
+
+
+def test_dequant_sampled_and_ranges_agree():
+    w = synth.weights(5, 10_000)
+    q = oracle.quantize(w)
+    full = oracle.dequant(q, oracle.FP16)
+    idx = np.random.default_rng(0).integers(0, q.n, 500)
+    assert np.array_equal(oracle.dequant_at(q, idx, oracle.FP16), full[idx])
+    assert np.array_equal(oracle.dequant(q, oracle.FP16, 1234, 5678), full[1234:5678])
+
+
+# ----------------------------------------------------------------------------
+# quantizer
+# ----------------------------------------------------------------------------
+
+
+def _nibbles(q):
+    nib = np.empty(2 * q.packed.size, np.int64)
+    nib[0::2] = q.packed >> 4
+    nib[1::2] = q.packed & 15
+    return nib[: q.n]
+
+
+@pytest.mark.parametrize("n,bs,s2,seed", [(4096, 64, 4, 1), (3001, 64, 8, 2), (255, 32, 2, 3),
+                                          (64 * 256 + 5, 64, 256, 4)])
+def test_quantizer_brute_force(n, bs, s2, seed, page_table):
+    w = synth.weights(seed, n, outliers=True)
+    q = oracle.quantize(w, bs, s2, keep_absmax=True)
+    nb = (n + bs - 1) // bs
+    wp = np.concatenate([w, np.zeros(nb * bs - n, np.float32)]).reshape(nb, bs)
+    absmax = np.abs(wp).max(axis=1)
+    assert np.array_equal(q.block_absmax, absmax)
+    assert q.offset == pytest.approx(math.fsum(absmax.astype(np.float64)) / nb, rel=2 ** -23)
+    off = np.float32(q.offset)
+    c = absmax - off
+    code2f = q.code2.view(np.float16).astype(np.float32)
+    for g in range(q.ngroups):
+        cg = c[g * s2:(g + 1) * s2]
+        a2 = np.float32(np.abs(cg).max()).astype(np.float16)
+        assert q.absmax2[g] == a2.view(np.uint16)
+        a2f = np.float32(a2)
+        r = cg / a2f if a2f != 0 else np.zeros_like(cg)
+        d = np.abs(r[:, None] - code2f[None, :])   # fp32 distances
+        assert np.array_equal(q.absmax_q[g * s2:(g + 1) * s2], np.argmin(d, axis=1))
+    r = w / np.repeat(absmax, bs)[:n]
+    d = np.abs(r[:, None] - page_table[None, :])
+    assert np.array_equal(_nibbles(q), np.argmin(d, axis=1))
+    if n % 2:
+        assert q.packed[-1] & 15 == 0   # pad nibble
+
+
+def test_quantizer_roundtrip_bound():
+    """|w - NF4[idx] * absmax| <= half the largest gap * absmax, and at the
+    value level the double-quantized scale adds |absmax - absmax_real|."""
+    w = synth.weights(21, 1 << 16, outliers=True)
+    q = oracle.quantize(w, keep_absmax=True)
+    t = oracle.nf4_table().astype(np.float64)
+    half_gap = np.diff(t).max() / 2
+    absmax = np.repeat(q.block_absmax, 64)[: q.n].astype(np.float64)
+    lvl1 = t[_nibbles(q)] * absmax
+    assert np.all(np.abs(w - lvl1) <= half_gap * absmax * (1 + 2 ** -20))
+    v = oracle.dequant_f32(q).astype(np.float64)
+    a_real = np.abs(v / np.where(t[_nibbles(q)] == 0, np.nan, t[_nibbles(q)]))
+    a_real = np.where(np.isnan(a_real), absmax, a_real)
+    bound = half_gap * a_real + np.abs(absmax - a_real) + 1e-7
+    assert np.all(np.abs(w - v) <= bound)
+
+
+def test_quantizer_gridpoints_are_stable():
+    rng = np.random.default_rng(9)
+    t = oracle.nf4_table()
+    nb = 200
+    A = np.float32(0.01) + rng.random(nb, dtype=np.float32)
+    j = rng.integers(0, 16, (nb, 64))
+    j[:, 0] = 15                      # every block holds +A, so its absmax is A
+    w = (t[j] * A[:, None]).astype(np.float32).reshape(-1)
+    q = oracle.quantize(w)
+    assert np.array_equal(_nibbles(q), j.reshape(-1))
+
+
+def test_quantizer_ties_go_to_smaller_index():
+    """Where the fp32 midpoint of two neighbouring codes is an exact tie in fp32
+    distance, the smaller index wins."""
+    t = oracle.nf4_table()
+    ties = []
+    for j in range(15):
+        mid = np.float32((np.float64(t[j]) + np.float64(t[j + 1])) / 2)
+        if abs(mid - t[j]) == abs(mid - t[j + 1]):
+            ties.append((j, mid))
+    assert len(ties) >= 4
+    w = np.zeros(64, np.float32)
+    w[0] = 1.0                      # block absmax 1: w / absmax == w
+    for i, (j, mid) in enumerate(ties):
+        w[1 + i] = mid
+    q = oracle.quantize(w)
+    assert [int(v) for v in _nibbles(q)[1:1 + len(ties)]] == [j for j, _ in ties]
+
+
+def test_quantizer_zero_tensor():
+    q = oracle.quantize(np.zeros(1000, np.float32))
+    assert np.all(q.packed == 0x77)
+    assert np.all(oracle.dequant_f32(q) == 0.0)
+    assert q.offset == 0.0 and np.all(q.absmax2 == 0)
+
+
+# ----------------------------------------------------------------------------
+# GEMV reference
+# ----------------------------------------------------------------------------
+
+
+def test_gemv_one_hot_reproduces_columns():
+    N, K = 48, 256
+    q = oracle.quantize(synth.weights(3, N * K), 64, 4)
+    W = oracle.dequant_f32(q).reshape(N, K)
+    for k in (0, 1, 63, 64, 200, 255):
+        x = np.zeros((1, K), np.float32)
+        x[0, k] = 1.0
+        y, S = oracle.gemv(q, N, K, synth.to_bf16_bits(x))
+        assert np.array_equal(y[0], W[:, k].astype(np.float64))
+        assert np.array_equal(S[0], np.abs(W[:, k]).astype(np.float64))
+
+
+@pytest.mark.parametrize("N,K,B", [(64, 512, 1), (33, 1536, 4), (7, 128, 8)])
+def test_gemv_matches_float64_matmul(N, K, B):
+    q = oracle.quantize(synth.weights(N + K, N * K), 64, 8)
+    W = oracle.dequant_f32(q).reshape(N, K).astype(np.float64)
+    xb = synth.activations(7, B, K)
+    xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    y, S = oracle.gemv(q, N, K, xb)
+    assert np.allclose(y, xf @ W.T, rtol=1e-12, atol=1e-12 * np.abs(xf) @ np.abs(W).T)
+    assert np.allclose(S, np.abs(xf) @ np.abs(W).T, rtol=1e-12)
+    rows = np.array([N - 1, 0, N // 2])
+    y2, S2 = oracle.gemv(q, N, K, xb, rows)
+    assert np.array_equal(y2, y[:, rows]) and np.array_equal(S2, S[:, rows])

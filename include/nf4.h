@@ -1,0 +1,131 @@
+/*
+ * nf4.h -- C ABI of libnf4: NF4 double-quantization dequant and fused
+ * W4A16 dequant-GEMV for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *  [blog]     "NF4反量化算子优化" (roundaboutt.github.io): "双量化", "反量化".
+ *  [report]   "NF4 双重量化反量化 CUDA Kernel 实现报告" (InfiniTensor
+ *             Learning-CUDA 03_nf4_dequant): §1.1-§1.3, §2.2, §3.3.
+ *  [quanttax] "RTX 4060 上的 LLM 量化实测" (akiliu.vercel.app): "Kernel 实现".
+ *  [handbook] "量化与 GEMV" (anrans.github.io): "GEMV kernel 的写法".
+ *
+ * ---------------------------------------------------------------------------
+ * The quantized tensor format (one flattened tensor of n elements)
+ * ---------------------------------------------------------------------------
+ *  packed    uint8[ceil(n/2)]   two 4-bit NF4 indices per byte; element 2i
+ *                               in the HIGH nibble, element 2i+1 in the LOW
+ *                               nibble ([report] §1.1 and §2.2 step 1).  For
+ *                               odd n the low nibble of the last byte is
+ *                               padding and is never read.
+ *  absmax_q  uint8[ceil(n/blocksize)]          per-block index into code2.
+ *  absmax2   fp16[ceil(nblocks/s2_blocksize)]  per-group second-level scale.
+ *  code2     fp16[256]                          second-level code table.
+ *  offset    fp32                               global offset (by value).
+ * ([report] §1.2 names these arrays and their types.)
+ *
+ * Element e belongs to block e / blocksize and group block / s2_blocksize;
+ * both sizes must be powers of two, so the library uses shifts ([report]
+ * §3.3).  The dequantized value is ([report] §1.3):
+ *
+ *     absmax_real = fp32(fp32(code2[absmax_q[block]]) * fp32(absmax2[group]))
+ *                   + offset                    (rounded to fp32 again)
+ *     value       = fp32(NF4[index(e)] * absmax_real)
+ *
+ * with each product and the sum rounded to fp32 separately (no fused
+ * multiply-add), NF4 the 16-entry table printed in [blog] "naive".
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ---------------------------------------------------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller; the library
+ *    keeps no pointer after the call returns and allocates nothing (except
+ *    nf4_quantize, which uses the caller's workspace).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
+ *    stream) and runs asynchronously; results are valid once the stream has
+ *    been synchronized.  No entry point synchronizes.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    validation error nothing is launched.  n == 0 (or N*K == 0) returns
+ *    NF4_OK without launching.
+ *  - Calls are thread-safe: the library holds no mutable global state.
+ *  - Pointers need only natural alignment; 16-byte aligned buffers take the
+ *    vectorized kernels, other alignments a slower kernel with identical bits.
+ */
+#ifndef NF4_H_
+#define NF4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NF4_OK = 0,
+  NF4_EINVAL = 1,        /* bad argument; nothing was launched */
+  NF4_EUNSUPPORTED = 2,  /* valid but outside the supported range (e.g. n >= 2^40) */
+  NF4_EHIP = 3           /* the HIP runtime reported an error at launch */
+} nf4_status;
+
+typedef enum { NF4_BF16 = 0, NF4_FP16 = 1 } nf4_dtype;
+
+/* Version of this ABI (incremented on incompatible change). */
+int nf4_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* nf4_status_string(int status);
+
+/*
+ * nf4_dequant -- standalone dequant of n elements to bf16 or fp16.
+ * Defined by [report] §1.3 (formula) and [blog] "反量化".
+ *
+ *  packed, absmax_q, absmax2, code2, offset : the format above (device).
+ *  n             : number of elements, 0 <= n < 2^40.
+ *  blocksize     : elements per first-level block, power of two in [1, 2^30].
+ *  s2_blocksize  : blocks per second-level group, power of two in [1, 2^30].
+ *  out           : device, n 16-bit values (bf16 or fp16 bits), element
+ *                  order = flat element order.  Written with round to
+ *                  nearest even; -0 is kept; fp16 overflow gives +-inf.
+ *  out_dtype     : NF4_BF16 or NF4_FP16.
+ *  stream        : hipStream_t.
+ * Returns NF4_EINVAL for a NULL pointer with n > 0, n < 0, a block size that
+ * is not a power of two or out of range, or an unknown dtype.
+ */
+nf4_status nf4_dequant(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
+                       const uint16_t* code2, float offset, int64_t n, int32_t blocksize,
+                       int32_t s2_blocksize, void* out, int32_t out_dtype, void* stream);
+
+/*
+ * nf4_gemv -- fused dequant + matrix-vector product for batch 1..8 (W4A16
+ * decode): y[b][r] = sum_k value(r*K + k) * x[b][k].
+ * Defined by [quanttax] "Kernel 实现" (decode on chip, fp32 accumulation) and
+ * [handbook] "GEMV kernel 的写法" (y = W x with W of shape N x K, row-major).
+ *
+ *  packed, absmax_q, absmax2, code2, offset : the format above for the
+ *                  N*K elements of W flattened row-major; blocks and groups
+ *                  follow the flat index r*K + k (they may span rows).
+ *  N, K          : output and input features; K must be even (rows start on
+ *                  a byte); N*K < 2^40.
+ *  blocksize, s2_blocksize : as for nf4_dequant.
+ *  x             : device bf16 bits [batch][K], row-major.
+ *  batch         : 1..8.
+ *  y             : device bf16 bits [batch][N], row-major; each output is
+ *                  the fp32 sum rounded to nearest even.
+ *  stream        : hipStream_t.
+ * Weights are used at full fp32 precision (never rounded to 16 bits) and the
+ * sum is accumulated in fp32; the result matches an fp64 reference within
+ * 2e-3*|y| + 2^-14 * sum_k |w x|.  Deterministic: the summation order depends
+ * only on N, K and batch.
+ * Returns NF4_EINVAL for NULL pointers with N*K > 0, N < 0, K < 0, odd K,
+ * batch outside 1..8, or bad block sizes.
+ */
+nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
+                    const uint16_t* code2, float offset, int64_t N, int64_t K,
+                    int32_t blocksize, int32_t s2_blocksize, const uint16_t* x, int32_t batch,
+                    uint16_t* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4_H_ */

@@ -46,6 +46,7 @@ def _load():
         "oracle_f16_from_float_array": (None, [p, i64, p]),
         "oracle_bf16_from_float_array": (None, [p, i64, p]),
         "oracle_f16_to_double_array": (None, [p, i64, p]),
+        "oracle_bf16_from_double_array": (None, [p, i64, p]),
         "oracle_code2_linear": (None, [p]),
         "oracle_quantize": (C.c_int, [p, i64, i32, i32, p, p, p, p, p, p]),
         "oracle_dequant_f32": (None, [p, p, p, p, f32, i64, i32, i32, i64, i64, p]),
@@ -99,6 +100,14 @@ def bf16_from_f32(a: np.ndarray) -> np.ndarray:
     a = np.ascontiguousarray(a, np.float32)
     out = np.empty(a.shape, np.uint16)
     _load().oracle_bf16_from_float_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def bf16_from_f64(a: np.ndarray) -> np.ndarray:
+    """bf16 bits of fp64 values, rounded once (nearest, ties to even)."""
+    a = np.ascontiguousarray(a, np.float64)
+    out = np.empty(a.shape, np.uint16)
+    _load().oracle_bf16_from_double_array(_ptr(a), a.size, _ptr(out))
     return out
 
 

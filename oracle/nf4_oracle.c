@@ -152,6 +152,9 @@ void oracle_f16_from_float_array(const float* in, int64_t n, uint16_t* out) {
 void oracle_bf16_from_float_array(const float* in, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_from_float(in[i]);
 }
+void oracle_bf16_from_double_array(const double* in, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_from_double(in[i]);
+}
 void oracle_f16_to_double_array(const uint16_t* in, int64_t n, double* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_double(in[i]);
 }

@@ -1,0 +1,88 @@
+"""The C ABI library loads and exports what include/nf4.h declares; host-side
+argument validation rejects bad arguments before anything is launched.  No
+compute call is made here (these run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import w4a16_gemv_amd as nf4
+    if not os.path.exists(nf4.LIB_PATH):
+        from w4a16_gemv_amd import build
+        build.build()
+    return nf4.load()
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn), encoding="utf-8").read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(nf4_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("nf4_dequant", "nf4_gemv", "nf4_abi_version", "nf4_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import w4a16_gemv_amd as nf4
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(nf4.EXPORTED) >= set(declared_functions())
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.nf4_abi_version() == 1
+    for st in range(4):
+        assert lib.nf4_status_string(st).decode().startswith("NF4_")
+    assert b"unknown" in lib.nf4_status_string(99)
+
+
+FAKE = C.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _dq(lib, n=16, bs=64, s2=256, dtype=0, packed=FAKE, out=FAKE):
+    return lib.nf4_dequant(packed, FAKE, FAKE, FAKE, C.c_float(0.0), n, bs, s2, out, dtype, None)
+
+
+def _gv(lib, N=4, K=64, bs=64, s2=256, batch=1, x=FAKE, y=FAKE, packed=FAKE):
+    return lib.nf4_gemv(packed, FAKE, FAKE, FAKE, C.c_float(0.0), N, K, bs, s2, x, batch, y, None)
+
+
+@pytest.mark.parametrize("kw", [dict(n=-1), dict(bs=0), dict(bs=48), dict(bs=-64),
+                                dict(s2=0), dict(s2=3), dict(bs=3), dict(bs=2 ** 31 - 1),
+                                dict(dtype=2), dict(dtype=-1), dict(packed=None), dict(out=None)])
+def test_dequant_rejects_bad_arguments(lib, kw):
+    assert _dq(lib, **kw) == 1
+
+
+def test_dequant_empty_is_a_no_op(lib):
+    assert lib.nf4_dequant(None, None, None, None, C.c_float(0.0), 0, 64, 256, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(N=-1), dict(K=-2), dict(K=63), dict(batch=0), dict(batch=9),
+                                dict(bs=24), dict(s2=0), dict(x=None), dict(y=None),
+                                dict(packed=None)])
+def test_gemv_rejects_bad_arguments(lib, kw):
+    assert _gv(lib, **kw) == 1
+
+
+def test_gemv_empty_is_a_no_op(lib):
+    assert lib.nf4_gemv(None, None, None, None, C.c_float(0.0), 0, 64, 64, 256, None, 1, None,
+                        None) == 0
+
+
+def test_oversized_requests_are_unsupported(lib):
+    assert _dq(lib, n=1 << 41) == 2
+    assert _gv(lib, N=1 << 30, K=1 << 12) == 2

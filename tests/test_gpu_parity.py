@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Dequant must be bit-exact for every element, including the sign of zero.
+GEMV outputs (bf16) must each be the round-to-nearest-even bf16 value of some
+real within 2^-14 sum_k |w x| of the fp64 oracle result (tests/_gpu.py); this
+implies |y - y_ref| <= 2^-8 |y_ref| + (1 + 2^-8) 2^-14 sum_k |w x|.  Output
+buffers sit between guard regions that must come back untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w4a16_gemv_amd as nf4
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+DT = {oracle.BF16: torch.bfloat16, oracle.FP16: torch.float16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    nf4.load()
+
+
+def run_dequant(q, out_dtype=oracle.BF16, offset_elems=0, packed_offset=0):
+    d = G.fmt_to_device(q)
+    if packed_offset:
+        buf = torch.zeros(q.packed.size + packed_offset, dtype=torch.uint8, device=G.dev())
+        buf[packed_offset:] = d["packed"]
+        d["packed"] = buf[packed_offset:]
+    base, out = G.guarded(q.n, DT[out_dtype], offset_elems)
+    print(f"[dequant] n={q.n} bs={q.blocksize} s2={q.s2_blocksize} dtype={out_dtype} "
+          f"out_off={offset_elems} packed_off={packed_offset}", flush=True)
+    nf4.nf4_dequant(d["packed"], d["absmax_q"], d["absmax2"], d["code2"], q.offset, q.n,
+                    q.blocksize, q.s2_blocksize, out=out)
+    torch.cuda.synchronize()
+    assert G.guards_intact(base, q.n, offset_elems), "write outside the output buffer"
+    return G.bits16(out)
+
+
+def assert_bits_equal(got, ref):
+    if not np.array_equal(got, ref):
+        bad = np.nonzero(got != ref)[0]
+        raise AssertionError(f"{bad.size} of {ref.size} elements differ; first at {bad[:8]}: "
+                             f"gpu {got[bad[:8]]} oracle {ref[bad[:8]]}")
+
+
+# ---------------------------------------------------------------------------
+# dequant
+# ---------------------------------------------------------------------------
+
+def test_dequant_1024x1024_bf16():
+    cfg = synth.DEQUANT_1K
+    q = oracle.quantize(synth.weights(cfg.seed, cfg.n))
+    assert_bits_equal(run_dequant(q, oracle.BF16), oracle.dequant(q, oracle.BF16))
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP16])
+def test_dequant_4096x4096_outliers(dtype):
+    cfg = synth.DEQUANT_4K
+    q = oracle.quantize(synth.weights(cfg.seed, cfg.n, outliers=True))
+    assert_bits_equal(run_dequant(q, dtype), oracle.dequant(q, dtype))
+
+
+EDGE = [
+    (1, 64, 256), (2, 64, 256), (7, 64, 256), (8, 64, 256), (9, 64, 256), (63, 64, 256),
+    (65, 64, 256), (12345, 64, 256), (2047 * 4096, 64, 256), (64 * 256 * 3 + 64, 64, 256),
+    (100_003, 64, 256), (2048 * 8 * 3 + 5, 64, 256), (4096, 8, 2), (4099, 16, 1),
+    (5000, 32, 4), (5000, 128, 256), (3001, 4, 8), (3001, 2, 1), (777, 1, 4),
+    (70_000, 1 << 14, 1), (1 << 16, 64, 1 << 12),
+]
+
+
+@pytest.mark.parametrize("n,bs,s2", EDGE)
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP16])
+def test_dequant_edge_shapes(n, bs, s2, dtype):
+    q = oracle.quantize(synth.weights(n + bs + s2, n, outliers=True), bs, s2)
+    assert_bits_equal(run_dequant(q, dtype), oracle.dequant(q, dtype))
+
+
+@pytest.mark.parametrize("offset_elems,packed_offset", [(1, 0), (0, 1), (3, 2), (4, 0)])
+def test_dequant_unaligned_buffers(offset_elems, packed_offset):
+    q = oracle.quantize(synth.weights(31, 50_001))
+    for dtype in (oracle.BF16, oracle.FP16):
+        assert_bits_equal(run_dequant(q, dtype, offset_elems, packed_offset),
+                          oracle.dequant(q, dtype))
+
+
+def _hand_format(n, bs, s2, code2_vals, absmax2_vals, absmax_q, packed, offset):
+    return oracle.Quantized(np.ascontiguousarray(packed, np.uint8),
+                            np.ascontiguousarray(absmax_q, np.uint8),
+                            np.asarray(absmax2_vals, np.float16).view(np.uint16),
+                            np.asarray(code2_vals, np.float16).view(np.uint16),
+                            float(np.float32(offset)), n, bs, s2)
+
+
+@pytest.mark.parametrize("case", ["neg_zero", "subnormal", "huge", "random_scales"])
+def test_dequant_special_values(case):
+    """Negative absmax_real (zero code -> -0), results in the subnormal range
+    of bf16/fp16, fp16 overflow, and random fp16 scales over many binades:
+    rounding on the GPU must match the oracle's round-to-nearest-even."""
+    rng = np.random.default_rng({"neg_zero": 1, "subnormal": 2, "huge": 3, "random_scales": 4}[case])
+    n, bs, s2 = 64 * 1024, 64, 4
+    nb, ng = n // bs, n // bs // s2
+    packed = rng.integers(0, 256, n // 2).astype(np.uint8)
+    absmax_q = rng.integers(0, 256, nb).astype(np.uint8)
+    if case == "neg_zero":
+        q = _hand_format(n, bs, s2, np.full(256, -1.0), np.ones(ng), absmax_q,
+                         np.full(n // 2, 0x77, np.uint8), 0.25)
+    elif case == "subnormal":
+        code2 = rng.standard_normal(256) * 2.0 ** -14
+        code2[:16] = 0.0          # absmax_real = offset: bf16 subnormal outputs
+        q = _hand_format(n, bs, s2, code2, 2.0 ** -rng.integers(5, 14, ng), absmax_q, packed,
+                         -1e-39)
+    elif case == "huge":
+        q = _hand_format(n, bs, s2, rng.uniform(-1, 1, 256) * 60000, rng.uniform(0.5, 2.0, ng),
+                         absmax_q, packed, 3e4)
+    else:
+        code2 = rng.standard_normal(256) * 2.0 ** rng.integers(-12, 4, 256)
+        a2 = rng.standard_normal(ng) * 2.0 ** rng.integers(-12, 8, ng)
+        q = _hand_format(n, bs, s2, code2, a2, absmax_q, packed, rng.standard_normal() * 1e-3)
+    for dtype in (oracle.BF16, oracle.FP16):
+        with np.errstate(over="ignore"):
+            assert_bits_equal(run_dequant(q, dtype), oracle.dequant(q, dtype))
+
+
+def test_dequant_8192x28672():
+    cfg = synth.DEQUANT_BIG
+    q = oracle.quantize(synth.weights(cfg.seed, cfg.n))
+    assert_bits_equal(run_dequant(q, oracle.BF16), oracle.dequant(q, oracle.BF16))
+
+
+def test_dequant_is_deterministic():
+    q = oracle.quantize(synth.weights(77, 1 << 20))
+    a = run_dequant(q)
+    b = run_dequant(q)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# GEMV
+# ---------------------------------------------------------------------------
+
+def run_gemv(q, N, K, xbits, x_offset=0):
+    d = G.fmt_to_device(q)
+    B = xbits.shape[0]
+    x = G.x_to_device(xbits)
+    if x_offset:
+        buf = torch.zeros(B * K + x_offset, dtype=torch.bfloat16, device=G.dev())
+        buf[x_offset:] = x.reshape(-1)
+        x = buf[x_offset:].view(B, K)
+    base, yv = G.guarded(B * N, torch.bfloat16)
+    print(f"[gemv] N={N} K={K} B={B} bs={q.blocksize} s2={q.s2_blocksize} x_off={x_offset}",
+          flush=True)
+    nf4.nf4_gemv(d["packed"], d["absmax_q"], d["absmax2"], d["code2"], q.offset, N, K, x,
+                 q.blocksize, q.s2_blocksize, y=yv.view(B, N))
+    torch.cuda.synchronize()
+    assert G.guards_intact(base, B * N), "write outside y"
+    return G.bf16_to_f64(G.bits16(yv)).reshape(B, N)
+
+
+def check_gemv(q, N, K, xbits, rows=None, x_offset=0):
+    y = run_gemv(q, N, K, xbits, x_offset)
+    yr, S = oracle.gemv(q, N, K, xbits, rows)
+    if rows is not None:
+        y = y[:, rows]
+    ok, worst = G.gemv_within_tolerance(y, yr, S)
+    assert ok, f"GEMV N={N} K={K} B={xbits.shape[0]}: worst error/bound = {worst:.3g}"
+    return worst
+
+
+@pytest.mark.parametrize("g", synth.QWEN_GEMVS, ids=lambda g: g.name)
+def test_gemv_qwen_batch1(g):
+    q = oracle.quantize(synth.weights(g.seed, g.N * g.K))
+    check_gemv(q, g.N, g.K, synth.activations(synth.QWEN_X_SEED, 1, g.K))
+
+
+@pytest.mark.parametrize("batch", synth.LLAMA_BATCHES)
+@pytest.mark.parametrize("g", synth.LLAMA_GEMVS, ids=lambda g: g.name)
+def test_gemv_llama(g, batch):
+    q = oracle.quantize(synth.weights(g.seed, g.N * g.K))
+    check_gemv(q, g.N, g.K, synth.activations(synth.llama_x_seed(batch), batch, g.K))
+
+
+@pytest.mark.parametrize("g", synth.sweep_layer(0), ids=lambda g: g.name)
+def test_gemv_decode_sweep_layer0(g):
+    q = oracle.quantize(synth.weights(g.seed, g.N * g.K))
+    rows = np.random.default_rng(g.seed).choice(g.N, 512, replace=False)
+    check_gemv(q, g.N, g.K, synth.activations(synth.SWEEP_X_SEED, 1, g.K), rows=np.sort(rows))
+
+
+GEMV_EDGE = [
+    # N, K, bs, s2
+    (1, 64, 64, 256), (3, 64, 64, 256), (5, 2048, 64, 256), (7, 2080, 64, 256),
+    (33, 32, 32, 1), (17, 96, 32, 4), (9, 16384, 64, 256), (3, 16416, 64, 256),
+    (11, 1000, 64, 256), (13, 2, 64, 256), (6, 130, 2, 8), (300, 1536, 128, 2),
+    (257, 1536, 16, 256), (64, 4096, 1 << 12, 1), (2, 40000, 64, 256),
+]
+
+
+@pytest.mark.parametrize("N,K,bs,s2", GEMV_EDGE)
+@pytest.mark.parametrize("batch", [1, 2, 3, 5, 8])
+def test_gemv_edge_shapes(N, K, bs, s2, batch):
+    q = oracle.quantize(synth.weights(N * 7 + K, N * K, outliers=True), bs, s2)
+    check_gemv(q, N, K, synth.activations(N + K + batch, batch, K))
+
+
+@pytest.mark.parametrize("batch", [1, 4, 6, 7, 8])
+def test_gemv_unaligned_x(batch):
+    N, K = 40, 4096
+    q = oracle.quantize(synth.weights(5, N * K))
+    check_gemv(q, N, K, synth.activations(6, batch, K), x_offset=1)
+
+
+@pytest.mark.parametrize("batch", [1, 4, 8])
+def test_gemv_one_hot_is_exact(batch):
+    """x = e_k in every batch row: y[r] must be the bf16 rounding of the fp32
+    dequant value W[r][k] exactly (a single non-zero term, no accumulation
+    error)."""
+    N, K = 256, 4096
+    q = oracle.quantize(synth.weights(8, N * K))
+    W = oracle.dequant_f32(q).reshape(N, K)
+    ks = [0, 31, 32, 2047, 2048, 4095][:batch] + [1000] * max(0, batch - 6)
+    x = np.zeros((batch, K), np.float32)
+    for b, k in enumerate(ks):
+        x[b, k] = 1.0
+    y = run_gemv(q, N, K, synth.to_bf16_bits(x))
+    for b, k in enumerate(ks):
+        expect = G.bf16_to_f64(oracle.bf16_from_f32(W[:, k]))
+        assert np.array_equal(y[b], expect), f"batch row {b}, k={k}"
+
+
+def test_gemv_empty_k_gives_zeros():
+    N, B = 100, 3
+    y = torch.full((B, N), 7.0, dtype=torch.bfloat16, device=G.dev())
+    z8 = torch.zeros(1, dtype=torch.uint8, device=G.dev())
+    z16 = torch.zeros(256, dtype=torch.int16, device=G.dev())
+    x = torch.zeros((B, 0), dtype=torch.bfloat16, device=G.dev())
+    nf4.nf4_gemv(z8, z8, z16, z16, 0.0, N, 0, x, y=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
+def test_gemv_is_deterministic():
+    N, K, B = 4096, 4096, 4
+    q = oracle.quantize(synth.weights(9, N * K))
+    xb = synth.activations(10, B, K)
+    a = run_gemv(q, N, K, xb)
+    b = run_gemv(q, N, K, xb)
+    assert np.array_equal(a, b)

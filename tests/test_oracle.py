@@ -135,6 +135,20 @@ def test_bf16_rne_matches_torch():
         assert np.array_equal(oracle.bf16_from_f32(a), bf16_bits_torch(a))
 
 
+def test_bf16_from_f64_is_correctly_rounded():
+    """fp64 -> bf16 rounds once: checked against exact rational rounding."""
+    rng = np.random.default_rng(14)
+    v = rng.standard_normal(3000) * 2.0 ** rng.integers(-140, 120, 3000)
+    v = np.concatenate([v, [1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, 1 + 3 * 2.0 ** -8,
+                            -(1 + 2.0 ** -8 - 2.0 ** -45), 2.0 ** -133, 2.0 ** -134,
+                            3 * 2.0 ** -135]])
+    got = oracle.bf16_from_f64(v)
+    for val, b in zip(v, got):
+        exp = round_fraction(Fraction(float(val)), mant=7, emin=-126)
+        gotv = Fraction(oracle.bf16_to_f64_scalar(int(b)))
+        assert gotv == exp, (val, b)
+
+
 def test_fp16_decode_exhaustive():
     h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     ref = h.view(np.float16).astype(np.float64)

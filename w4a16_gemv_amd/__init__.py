@@ -1,0 +1,22 @@
+"""w4a16_gemv_amd: NF4 double-quantization dequant and fused W4A16 GEMV for
+AMD Instinct MI355X (gfx950).
+
+The compute lives in libnf4.so (HIP, C ABI in include/nf4.h); this package is
+its Python binding.  See nf4_dequant / nf4_gemv.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    NF4_BF16,
+    NF4_EHIP,
+    NF4_EINVAL,
+    NF4_EUNSUPPORTED,
+    NF4_FP16,
+    NF4_OK,
+    NF4Error,
+    format_sizes,
+    load,
+    nf4_dequant,
+    nf4_gemv,
+    status_string,
+)

@@ -1,0 +1,51 @@
+"""Build libnf4.so (the gfx950 HIP library) in-tree with hipcc.
+
+Flags:
+  --offload-arch=gfx950     CDNA4 only; no other targets, no host fallback.
+  -ffp-contract=off         the dequant formula rounds each product and sum to
+                            fp32 on its own; GEMV code uses explicit fmaf.
+  -target-feature -packed-fp32-ops
+                            no packed fp32 VALU instructions.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "nf4_kernels.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libnf4.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libnf4)")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", LIB + ".tmp", SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed to build libnf4.so")
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,729 @@
+// nf4_kernels.hip -- gfx950 kernels and the C ABI of libnf4.
+//
+// NF4 double-quantization dequant ([report] §1.3) and the fused W4A16
+// dequant-GEMV ([quanttax] "Kernel 实现"; [handbook] "GEMV kernel 的写法"),
+// written for CDNA4: wave64, LDS-resident NF4 table, shift-based block/group
+// indexing, one absmax_real per 64-element block, packed 128-bit stores,
+// DPP wave reductions.  No MFMA: at batch <= 8 the GEMV is bound by HBM
+// (batch 1) or by vector ALU issue (batch 4-8), not by a dense contraction.
+//
+// Pages (by title): [blog] "NF4反量化算子优化"; [report] "NF4 双重量化反量化
+// CUDA Kernel 实现报告"; [quanttax] "RTX 4060 上的 LLM 量化实测";
+// [handbook] "量化与 GEMV".
+//
+// Numerics.  This file is compiled with -ffp-contract=off: every product and
+// sum of the dequant formula is rounded to fp32 on its own.  GEMV products are
+// accumulated with explicit fmaf (fp32).  16-bit outputs use the gfx950 packed
+// conversions v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32, which round to nearest
+// even under the default rounding mode.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nf4.h"
+
+namespace {
+
+// The 16 NF4 code values, as the 8-decimal literals printed in [blog] "naive";
+// each literal is rounded to the nearest fp32 by the compiler.
+__device__ const float kNF4[16] = {
+    -1.00000000f, -0.69619280f, -0.52507305f, -0.39491749f,
+    -0.28444138f, -0.18477343f, -0.09105004f, 0.00000000f,
+    0.07958030f,  0.16093020f,  0.24611230f,  0.33791524f,
+    0.44070983f,  0.56261700f,  0.72295684f,  1.00000000f,
+};
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));  // exact widening
+}
+
+// Pin a value as an fp32 register.  Without it the compiler may fold an fp32
+// multiply and the following 16-bit conversion into one mixed-precision fma
+// (v_fma_mixlo_f16), which rounds the exact product straight to fp16 and skips
+// the fp32 rounding the method prescribes (a double-rounding difference).
+__device__ __forceinline__ float as_fp32(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Two 16-bit outputs in one dword: the even element in the low half (lower
+// address), the odd element in the high half.  Both inputs are first pinned as
+// rounded fp32 values.
+template <int OUT>
+__device__ __forceinline__ uint32_t pack_pair(float even, float odd) {
+  even = as_fp32(even);
+  odd = as_fp32(odd);
+  if constexpr (OUT == NF4_BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){even, odd}, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){even, odd}, f16x2));
+  }
+}
+
+template <int OUT>
+__device__ __forceinline__ uint16_t to_half_bits(float v) {
+  return static_cast<uint16_t>(pack_pair<OUT>(v, 0.0f) & 0xFFFFu);
+}
+
+// absmax_real of one first-level block: fp32 product, then fp32 sum.
+__device__ __forceinline__ float block_scale(const uint8_t* __restrict__ absmax_q,
+                                             const uint16_t* __restrict__ absmax2,
+                                             const uint16_t* __restrict__ code2, float offset,
+                                             int64_t blk, int log2s2) {
+  const float c = f16_to_f32(code2[absmax_q[blk]]);
+  const float g = f16_to_f32(absmax2[blk >> log2s2]);
+  const float s = c * g;
+  return s + offset;
+}
+
+// ---------------------------------------------------------------------------
+// Dequant, vectorized path.
+//
+// A workgroup of 256 lanes owns a tile of 256*U "steps"; a step is one packed
+// dword (8 elements) in, one 16-byte store out.  Lane t handles steps
+// tile0 + u*256 + t, so every wave-wide load covers 256 contiguous bytes and
+// every wave-wide store 1 KiB of contiguous output.
+//
+// Every global load of the tile is issued before the first wait: the packed
+// dwords, the tile's absmax_q bytes and absmax2 halves, and the 256-entry
+// code2 table (staged in LDS as fp32, so that the code2[absmax_q] lookup is an
+// LDS read instead of a second, dependent global load).  The workgroup then
+// computes one absmax_real per first-level block into LDS (a 64-element block
+// is shared by 8 lanes) and decodes with the NF4 table in LDS (lanes index it
+// divergently; 16 distinct words never conflict on LDS banks).
+// Requirements (checked on the host): packed 4-byte aligned, out 16-byte
+// aligned, blocksize >= 8 so that a step never straddles a block.
+// ---------------------------------------------------------------------------
+constexpr int kDqThreads = 256;
+
+template <int OUT, int U>
+__global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
+    const uint32_t* __restrict__ packed32, const uint8_t* __restrict__ packed8,
+    const uint8_t* __restrict__ absmax_q, const uint16_t* __restrict__ absmax2,
+    const uint16_t* __restrict__ code2, float offset, int64_t n, int log2bs, int log2s2,
+    uint4* __restrict__ out16, uint16_t* __restrict__ out2) {
+  __shared__ float s_nf4[16];
+  __shared__ float s_code2[256];
+  __shared__ float s_scale[kDqThreads * U];
+  const int t = threadIdx.x;
+  const int64_t full_steps = n >> 3;
+  const int64_t step0 = static_cast<int64_t>(blockIdx.x) * (kDqThreads * U);
+
+  // 1. all global loads of the tile, issued back to back
+  uint32_t w[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t s = step0 + u * kDqThreads + t;
+    w[u] = s < full_steps ? packed32[s] : 0u;
+  }
+  const uint16_t c2 = code2[t];
+  const int64_t e_begin = step0 * 8;
+  const int64_t e_end = (step0 + kDqThreads * U) * 8 < n ? (step0 + kDqThreads * U) * 8 : n;
+  const int64_t blk0 = e_begin >> log2bs;
+  const int nblk = static_cast<int>(((e_end - 1) >> log2bs) - blk0 + 1);  // <= 256 * U
+  uint32_t qv[U];
+  uint16_t gv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = t + u * kDqThreads;
+    qv[u] = i < nblk ? absmax_q[blk0 + i] : 0u;
+    gv[u] = i < nblk ? absmax2[(blk0 + i) >> log2s2] : uint16_t(0);
+  }
+
+  // 2. tables, then one absmax_real per block
+  s_code2[t] = f16_to_f32(c2);
+  if (t < 16) s_nf4[t] = kNF4[t];
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = t + u * kDqThreads;
+    if (i < nblk) {
+      const float prod = s_code2[qv[u]] * f16_to_f32(gv[u]);
+      s_scale[i] = prod + offset;
+    }
+  }
+  __syncthreads();
+
+  // 3. decode 8 nibbles per step and store 16 bytes
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t s = step0 + u * kDqThreads + t;
+    if (s < full_steps) {
+      const float a = s_scale[((s * 8) >> log2bs) - blk0];
+      const uint32_t wd = w[u];
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float ve = s_nf4[(wd >> (8 * j + 4)) & 15u] * a;
+        const float vo = s_nf4[(wd >> (8 * j)) & 15u] * a;
+        o[j] = pack_pair<OUT>(ve, vo);
+      }
+      uint4 v;
+      v.x = o[0];
+      v.y = o[1];
+      v.z = o[2];
+      v.w = o[3];
+      out16[s] = v;
+    } else if (s == full_steps) {
+      // ragged tail: the last n % 8 elements, one at a time
+      for (int64_t e = s * 8; e < n; ++e) {
+        const uint8_t byte = packed8[e >> 1];
+        const uint32_t nib = (e & 1) ? (byte & 15u) : (byte >> 4);
+        const float a = s_scale[(e >> log2bs) - blk0];
+        out2[e] = to_half_bits<OUT>(s_nf4[nib] * a);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequant, general path: one element per lane, byte loads, 16-bit stores.
+// Used for unaligned buffers and block sizes below 8.  Same arithmetic, same
+// bits.
+// ---------------------------------------------------------------------------
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_any_kernel(
+    const uint8_t* __restrict__ packed8, const uint8_t* __restrict__ absmax_q,
+    const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
+    int64_t n, int log2bs, int log2s2, uint16_t* __restrict__ out2) {
+  __shared__ float s_nf4[16];
+  if (threadIdx.x < 16) s_nf4[threadIdx.x] = kNF4[threadIdx.x];
+  __syncthreads();
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
+       e += stride) {
+    const uint8_t byte = packed8[e >> 1];
+    const uint32_t nib = (e & 1) ? (byte & 15u) : (byte >> 4);
+    const float a = block_scale(absmax_q, absmax2, code2, offset, e >> log2bs, log2s2);
+    out2[e] = to_half_bits<OUT>(s_nf4[nib] * a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 sum with DPP: after the six steps lane 63 holds the total.
+// quad_perm [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror and
+// row_mirror each row of 16, row_bcast:15 / row_bcast:31 carry row sums up.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int src = __builtin_bit_cast(int, v);
+  const int moved = __builtin_amdgcn_update_dpp(0, src, CTRL, ROW_MASK, 0xF, false);
+  return v + __builtin_bit_cast(float, moved);
+}
+
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_add<0x140, 0xF>(v);  // row_mirror
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Fused dequant-GEMV, streaming path (batch 1-2).
+//
+// Decode table.  One packed byte holds two weights, so the workgroup builds in
+// LDS a 256-entry table: entry b = (NF4[b >> 4], NF4[b & 15]) as two fp32 (the
+// even element first).  The table is replicated 32 times with copy c of entry
+// b at byte address 256 b + 8 c; lane l reads copy l % 32, so the 32 lanes
+// that LDS serves together always hit distinct bank pairs whatever bytes they
+// hold (a single copy loses about half the LDS throughput to bank conflicts).
+// The address of byte i of a packed dword d is then one v_perm_b32: byte i of
+// d becomes address bits 8..15 and the lane's copy offset bits 0..7.  Per
+// weight: half a VALU op of addressing, half a 64-bit LDS read, one fma.
+//
+// Work split.  A workgroup has T teams of nw waves, nw = ceil(K / 2048): wave
+// s of a team owns the 32-column chunks [2048 s + 32 l, +32) (lane l) for the
+// whole kernel and keeps their activations in registers as fp32.  Each team
+// walks groups of R consecutive rows (grid-stride); for each row a lane reads
+// one 16-byte packed chunk, which lies inside one first-level block
+// (blocksize >= 32, K % 32 == 0), so its absmax_real is applied once, after
+// the lane's 32 products are summed (scale after accumulate).  The loads of
+// the team's next row group are issued before the current group is computed.
+// Lane partials are summed with DPP and a team's wave partials through LDS in
+// a fixed order (one barrier per group, double-buffered): deterministic.
+// Requirements (checked on the host): K % 32 == 0, K <= 16384, blocksize >=
+// 32, packed and x 16-byte aligned, blockDim = 64 * nw * T <= 512.
+// ---------------------------------------------------------------------------
+constexpr int kSlab = 2048;
+constexpr int kPairCopies = 32;
+
+template <int R>
+struct RowGroup {
+  uint4 pk[R];
+  uint32_t q[R];
+  float a2[R];
+};
+
+template <int R>
+__device__ __forceinline__ void load_row_group(RowGroup<R>& rg, int g, bool active, int N, int K,
+                                               int k0, const uint4* __restrict__ packed16,
+                                               const uint8_t* __restrict__ absmax_q,
+                                               const uint16_t* __restrict__ absmax2, int log2bs,
+                                               int log2s2) {
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int r = g * R + rr;
+    if (active && r < N) {
+      const int64_t e = static_cast<int64_t>(r) * K + k0;
+      const int64_t blk = e >> log2bs;
+      rg.pk[rr] = packed16[e >> 5];
+      rg.q[rr] = absmax_q[blk];
+      rg.a2[rr] = f16_to_f32(absmax2[blk >> log2s2]);
+    } else {
+      rg.pk[rr] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);  // zeros
+      rg.q[rr] = 0;
+      rg.a2[rr] = 0.0f;
+    }
+  }
+}
+
+// part[b] += sum over the 8 weights of dword d (columns 8 j .. 8 j + 7 of the
+// lane's chunk) of weight * x.
+template <int B>
+__device__ __forceinline__ void dot_dword_pairs(uint32_t d, uint32_t copy_off,
+                                                const float (&xv)[B][32], int j,
+                                                const float2* s_pairs, float (&part)[B]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // address bits 15..8 = byte i of d, bits 7..0 = copy offset (selector
+    // 0x0C = zero byte, 4 = byte 0 of the first operand, i = byte i of d)
+    const uint32_t addr = __builtin_amdgcn_perm(copy_off, d, 0x0C0C0004u | (uint32_t(i) << 8));
+    const float2 t = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(s_pairs) + addr);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      part[b] = __builtin_fmaf(t.x, xv[b][8 * j + 2 * i], part[b]);
+      part[b] = __builtin_fmaf(t.y, xv[b][8 * j + 2 * i + 1], part[b]);
+    }
+  }
+}
+
+template <int B, int R>
+__global__ __launch_bounds__(512) void gemv_stream_kernel(
+    const uint4* __restrict__ packed16, const uint8_t* __restrict__ absmax_q,
+    const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
+    int N, int K, int log2bs, int log2s2, int nw, const uint16_t* __restrict__ x,
+    uint16_t* __restrict__ y) {
+  __shared__ float2 s_pairs[256 * kPairCopies];  // 64 KiB
+  __shared__ float s_nf4[16];
+  __shared__ float s_code2[256];
+  __shared__ float s_red[2][8][R * B];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int team = wave / nw;
+  const int slab = wave - team * nw;
+  const int teams = (blockDim.x >> 6) / nw;
+  const int k0 = slab * kSlab + lane * 32;
+  const bool active = k0 < K;
+  const int ngroups = (N + R - 1) / R;
+  const int gstride = static_cast<int>(gridDim.x) * teams;
+
+  // global loads first: activations, tables, the team's first row group
+  uint4 xr[B][4];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xr[b][j] = active ? *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(b) * K + k0 + 8 * j)
+                        : make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
+  if (tid < 16) s_nf4[tid] = kNF4[tid];
+  int g = blockIdx.x * teams + team;
+  RowGroup<R> cur;
+  load_row_group<R>(cur, g, active, N, K, k0, packed16, absmax_q, absmax2, log2bs, log2s2);
+  __syncthreads();
+  for (int e = tid; e < 256 * kPairCopies; e += blockDim.x) {
+    const int b = e / kPairCopies;
+    s_pairs[e] = make_float2(s_nf4[b >> 4], s_nf4[b & 15]);
+  }
+
+  float xv[B][32];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w4[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[b][8 * j + 2 * i] = __builtin_bit_cast(float, w4[i] << 16);
+        xv[b][8 * j + 2 * i + 1] = __builtin_bit_cast(float, w4[i] & 0xFFFF0000u);
+      }
+    }
+  const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
+  __syncthreads();
+
+  // every team runs the same number of iterations (barriers inside)
+  const int iters = (ngroups - static_cast<int>(blockIdx.x) * teams + gstride - 1) / gstride;
+  int buf = 0;
+  for (int it = 0; it < iters; ++it, g += gstride) {
+    RowGroup<R> nxt;
+    load_row_group<R>(nxt, g + gstride, active, N, K, k0, packed16, absmax_q, absmax2, log2bs,
+                      log2s2);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      float part[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) part[b] = 0.0f;
+      dot_dword_pairs<B>(cur.pk[rr].x, copy_off, xv, 0, s_pairs, part);
+      dot_dword_pairs<B>(cur.pk[rr].y, copy_off, xv, 1, s_pairs, part);
+      dot_dword_pairs<B>(cur.pk[rr].z, copy_off, xv, 2, s_pairs, part);
+      dot_dword_pairs<B>(cur.pk[rr].w, copy_off, xv, 3, s_pairs, part);
+      const float prod = s_code2[cur.q[rr]] * cur.a2[rr];
+      const float a = prod + offset;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float tot = wave_sum_to_lane63(a * part[b]);
+        if (lane == 63) s_red[buf][wave][rr * B + b] = tot;
+      }
+    }
+    __syncthreads();
+    if (slab == 0 && lane < R * B) {
+      const int rr = lane / B, b = lane % B;
+      float acc = s_red[buf][wave][lane];
+      for (int w = 1; w < nw; ++w) acc += s_red[buf][wave + w][lane];
+      const int r = g * R + rr;
+      if (g < ngroups && r < N) y[static_cast<int64_t>(b) * N + r] = to_half_bits<NF4_BF16>(acc);
+    }
+    buf ^= 1;
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused dequant-GEMV, batched path (batch 3-8).
+//
+// A workgroup owns R consecutive rows and has one wave per 2048-column slab
+// of K (W = ceil(K / 2048) waves, at most 8).  Lane l of wave s covers the 32
+// columns [2048 s + 32 l, +32): one 16-byte packed load per row, lying inside
+// one first-level block (blocksize >= 32, K % 32 == 0), so the lane computes
+// one absmax_real per row and applies it after summing its 32 products
+// (scale after accumulate).  The lane's 32 activations per batch row are
+// loaded once and reused for all R rows.  Lane partials are reduced with DPP,
+// the W wave partials in LDS in a fixed order; one bf16 store per output.
+// Requirements (checked on the host): K % 32 == 0, K <= 16384, blocksize >=
+// 32, packed 16-byte aligned, x 16-byte aligned.
+// ---------------------------------------------------------------------------
+template <int B, int R>
+__global__ __launch_bounds__(512) void gemv_vec_kernel(
+    const uint4* __restrict__ packed16, const uint8_t* __restrict__ absmax_q,
+    const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
+    int N, int K, int log2bs, int log2s2, const uint16_t* __restrict__ x,
+    uint16_t* __restrict__ y) {
+  __shared__ float s_nf4[16];
+  __shared__ float s_code2[256];
+  __shared__ float s_red[8][R * B];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int r0 = blockIdx.x * R;
+  const int k0 = wave * kSlab + lane * 32;
+  const bool active = k0 < K;
+
+  uint4 pk[R];
+  uint32_t qv[R];
+  float a2v[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int r = r0 + rr;
+    if (active && r < N) {
+      const int64_t e = static_cast<int64_t>(r) * K + k0;
+      const int64_t blk = e >> log2bs;
+      pk[rr] = packed16[e >> 5];
+      qv[rr] = absmax_q[blk];
+      a2v[rr] = f16_to_f32(absmax2[blk >> log2s2]);
+    } else {
+      pk[rr] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
+      qv[rr] = 0;
+      a2v[rr] = 0.0f;
+    }
+  }
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
+  if (threadIdx.x < 16) s_nf4[threadIdx.x] = kNF4[threadIdx.x];
+  __syncthreads();
+  float a[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const float prod = s_code2[qv[rr]] * a2v[rr];
+    a[rr] = prod + offset;
+  }
+
+  float part[R][B];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+    for (int b = 0; b < B; ++b) part[rr][b] = 0.0f;
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // 8 columns per sub-step
+    uint32_t xw[B][4];            // raw bf16 pairs of the 8 columns
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      uint4 xr = make_uint4(0u, 0u, 0u, 0u);
+      if (active) xr = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(b) * K + k0 + 8 * j);
+      xw[b][0] = xr.x;
+      xw[b][1] = xr.y;
+      xw[b][2] = xr.z;
+      xw[b][3] = xr.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // one packed byte = two columns
+      float xe[B], xo[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        xe[b] = __builtin_bit_cast(float, xw[b][i] << 16);
+        xo[b] = __builtin_bit_cast(float, xw[b][i] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const uint32_t wd = j == 0 ? pk[rr].x : j == 1 ? pk[rr].y : j == 2 ? pk[rr].z : pk[rr].w;
+        const float te = s_nf4[(wd >> (8 * i + 4)) & 15u];
+        const float to = s_nf4[(wd >> (8 * i)) & 15u];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          part[rr][b] = __builtin_fmaf(te, xe[b], part[rr][b]);
+          part[rr][b] = __builtin_fmaf(to, xo[b], part[rr][b]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float tot = wave_sum_to_lane63(a[rr] * part[rr][b]);
+      if (lane == 63) s_red[wave][rr * B + b] = tot;
+    }
+  __syncthreads();
+  if (threadIdx.x < R * B) {
+    const int rr = threadIdx.x / B, b = threadIdx.x % B;
+    float acc = s_red[0][threadIdx.x];
+    for (int w = 1; w < nwaves; ++w) acc += s_red[w][threadIdx.x];
+    const int r = r0 + rr;
+    if (r < N) y[static_cast<int64_t>(b) * N + r] = to_half_bits<NF4_BF16>(acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused dequant-GEMV, general path: one wave per row, lanes stride over the
+// row two elements (one byte) at a time, per-element scales.  Any even K,
+// any power-of-two block sizes, any alignment.
+// ---------------------------------------------------------------------------
+template <int B>
+__global__ __launch_bounds__(256) void gemv_any_kernel(
+    const uint8_t* __restrict__ packed8, const uint8_t* __restrict__ absmax_q,
+    const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
+    int64_t N, int64_t K, int log2bs, int log2s2, const uint16_t* __restrict__ x,
+    uint16_t* __restrict__ y) {
+  __shared__ float s_nf4[16];
+  if (threadIdx.x < 16) s_nf4[threadIdx.x] = kNF4[threadIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (r >= N) return;
+  float acc[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+  for (int64_t k = 2 * lane; k < K; k += 128) {
+    const int64_t e = r * K + k;
+    const uint8_t byte = packed8[e >> 1];
+    const float ve = s_nf4[byte >> 4] *
+                     block_scale(absmax_q, absmax2, code2, offset, e >> log2bs, log2s2);
+    const float vo = s_nf4[byte & 15u] *
+                     block_scale(absmax_q, absmax2, code2, offset, (e + 1) >> log2bs, log2s2);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float x0 = __builtin_bit_cast(float, static_cast<uint32_t>(x[b * K + k]) << 16);
+      const float x1 = __builtin_bit_cast(float, static_cast<uint32_t>(x[b * K + k + 1]) << 16);
+      acc[b] = __builtin_fmaf(ve, x0, acc[b]);
+      acc[b] = __builtin_fmaf(vo, x1, acc[b]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const float tot = wave_sum_to_lane63(acc[b]);
+    if (lane == 63) y[b * N + r] = to_half_bits<NF4_BF16>(tot);
+  }
+}
+
+// y = 0 for an empty reduction (K == 0).
+__global__ void fill_zero_kernel(uint16_t* __restrict__ y, int64_t count) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+       i += stride)
+    y[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool pow2_log2(int32_t v, int* lg) {
+  if (v < 1 || v > (1 << 30) || (v & (v - 1)) != 0) return false;
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  *lg = l;
+  return true;
+}
+
+// Compute units of the current device (cached per device id; a benign race
+// writes the same value).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+nf4_status launch_status() {
+  return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+template <int OUT>
+nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
+                          const uint16_t* code2, float offset, int64_t n, int lbs, int ls2,
+                          void* out, hipStream_t st) {
+  const bool vec = lbs >= 3 && aligned(packed, 4) && aligned(out, 16);
+  if (vec) {
+    const int64_t steps = (n >> 3) + ((n & 7) ? 1 : 0);
+    constexpr int U = 8;
+    const int64_t tiles = (steps + kDqThreads * U - 1) / (kDqThreads * U);
+    if (tiles > 0x7FFFFFFF) return NF4_EUNSUPPORTED;
+    hipLaunchKernelGGL((dequant_vec_kernel<OUT, U>), dim3(static_cast<uint32_t>(tiles)),
+                       dim3(kDqThreads), 0, st, reinterpret_cast<const uint32_t*>(packed), packed,
+                       absmax_q, absmax2, code2, offset, n, lbs, ls2, reinterpret_cast<uint4*>(out),
+                       reinterpret_cast<uint16_t*>(out));
+  } else {
+    const int64_t blocks = (n + 255) / 256;
+    const uint32_t grid = static_cast<uint32_t>(blocks < 65536 ? blocks : 65536);
+    hipLaunchKernelGGL((dequant_any_kernel<OUT>), dim3(grid), dim3(256), 0, st, packed, absmax_q,
+                       absmax2, code2, offset, n, lbs, ls2, reinterpret_cast<uint16_t*>(out));
+  }
+  return launch_status();
+}
+
+template <int B>
+nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
+                         const uint16_t* code2, float offset, int64_t N, int64_t K, int lbs,
+                         int ls2, const uint16_t* x, uint16_t* y, hipStream_t st) {
+  const bool vec = lbs >= 5 && K % 32 == 0 && K <= 8 * kSlab && N <= 0x7FFFFFFF &&
+                   aligned(packed, 16) && aligned(x, 16);
+  if constexpr (B <= 2) {
+    if (vec) {
+      constexpr int R = 4;
+      const int nw = static_cast<int>((K + kSlab - 1) / kSlab);
+      const int teams = 8 / nw;
+      const int64_t ngroups = (N + R - 1) / R;
+      // two 512-lane workgroups per CU (the decode table takes 64 KiB of LDS)
+      const int64_t max_wg = static_cast<int64_t>(device_cus()) * 2;
+      const int64_t per_wg = (ngroups + max_wg * teams - 1) / (max_wg * teams);  // groups per team
+      const int64_t grid = (ngroups + per_wg * teams - 1) / (per_wg * teams);
+      hipLaunchKernelGGL((gemv_stream_kernel<B, R>), dim3(static_cast<uint32_t>(grid)),
+                         dim3(64 * nw * teams), 0, st, reinterpret_cast<const uint4*>(packed),
+                         absmax_q, absmax2, code2, offset, static_cast<int>(N), static_cast<int>(K),
+                         lbs, ls2, nw, x, y);
+    return launch_status();
+    }
+  }
+  if (vec) {
+    constexpr int R = B <= 4 ? 2 : 1;
+    const int nw = static_cast<int>((K + kSlab - 1) / kSlab);
+    const int64_t grid = (N + R - 1) / R;
+    hipLaunchKernelGGL((gemv_vec_kernel<B, R>), dim3(static_cast<uint32_t>(grid)), dim3(64 * nw),
+                       0, st, reinterpret_cast<const uint4*>(packed), absmax_q, absmax2, code2,
+                       offset, static_cast<int>(N), static_cast<int>(K), lbs, ls2, x, y);
+  } else {
+    const int64_t grid = (N + 3) / 4;
+    if (grid > 0x7FFFFFFF) return NF4_EUNSUPPORTED;
+    hipLaunchKernelGGL((gemv_any_kernel<B>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st,
+                       packed, absmax_q, absmax2, code2, offset, N, K, lbs, ls2, x, y);
+  }
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int nf4_abi_version(void) { return 1; }
+
+const char* nf4_status_string(int status) {
+  switch (status) {
+    case NF4_OK: return "NF4_OK";
+    case NF4_EINVAL: return "NF4_EINVAL: invalid argument";
+    case NF4_EUNSUPPORTED: return "NF4_EUNSUPPORTED: size outside the supported range";
+    case NF4_EHIP: return "NF4_EHIP: HIP launch error";
+    default: return "unknown nf4 status";
+  }
+}
+
+nf4_status nf4_dequant(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
+                       const uint16_t* code2, float offset, int64_t n, int32_t blocksize,
+                       int32_t s2_blocksize, void* out, int32_t out_dtype, void* stream) {
+  int lbs = 0, ls2 = 0;
+  if (n < 0 || !pow2_log2(blocksize, &lbs) || !pow2_log2(s2_blocksize, &ls2)) return NF4_EINVAL;
+  if (out_dtype != NF4_BF16 && out_dtype != NF4_FP16) return NF4_EINVAL;
+  if (n == 0) return NF4_OK;
+  if (!packed || !absmax_q || !absmax2 || !code2 || !out) return NF4_EINVAL;
+  if (n >= kMaxElems) return NF4_EUNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (out_dtype == NF4_BF16)
+    return dequant_launch<NF4_BF16>(packed, absmax_q, absmax2, code2, offset, n, lbs, ls2, out, st);
+  return dequant_launch<NF4_FP16>(packed, absmax_q, absmax2, code2, offset, n, lbs, ls2, out, st);
+}
+
+nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
+                    const uint16_t* code2, float offset, int64_t N, int64_t K,
+                    int32_t blocksize, int32_t s2_blocksize, const uint16_t* x, int32_t batch,
+                    uint16_t* y, void* stream) {
+  int lbs = 0, ls2 = 0;
+  if (N < 0 || K < 0 || (K & 1) || batch < 1 || batch > 8) return NF4_EINVAL;
+  if (!pow2_log2(blocksize, &lbs) || !pow2_log2(s2_blocksize, &ls2)) return NF4_EINVAL;
+  if (N == 0) return NF4_OK;
+  if (!y) return NF4_EINVAL;
+  if (K == 0) {  // empty sums: y = +0
+    if (N > kMaxElems) return NF4_EUNSUPPORTED;
+    const int64_t count = N * batch;
+    const int64_t blocks = (count + 255) / 256;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>(blocks < 4096 ? blocks : 4096)), dim3(256),
+                       0, reinterpret_cast<hipStream_t>(stream), y, count);
+    return launch_status();
+  }
+  if (!packed || !absmax_q || !absmax2 || !code2 || !x) return NF4_EINVAL;
+  if (N > kMaxElems / K) return NF4_EUNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  switch (batch) {
+#define NF4_GEMV_CASE(BB) \
+  case BB:                \
+    return gemv_launch_b<BB>(packed, absmax_q, absmax2, code2, offset, N, K, lbs, ls2, x, y, st);
+    NF4_GEMV_CASE(1)
+    NF4_GEMV_CASE(2)
+    NF4_GEMV_CASE(3)
+    NF4_GEMV_CASE(4)
+    NF4_GEMV_CASE(5)
+    NF4_GEMV_CASE(6)
+    NF4_GEMV_CASE(7)
+    NF4_GEMV_CASE(8)
+#undef NF4_GEMV_CASE
+  }
+  return NF4_EINVAL;
+}
+
+}  // extern "C"

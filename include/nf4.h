@@ -38,8 +38,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------------------------------------------
  *  - All array arguments are DEVICE pointers owned by the caller; the library
- *    keeps no pointer after the call returns and allocates nothing (except
- *    nf4_quantize, which uses the caller's workspace).
+ *    keeps no pointer after the call returns and allocates nothing
+ *    (nf4_quantize uses a workspace the caller provides).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
  *    stream) and runs asynchronously; results are valid once the stream has
  *    been synchronized.  No entry point synchronizes.
@@ -113,9 +113,10 @@ nf4_status nf4_dequant(const uint8_t* packed, const uint8_t* absmax_q, const uin
  *                  the fp32 sum rounded to nearest even.
  *  stream        : hipStream_t.
  * Weights are used at full fp32 precision (never rounded to 16 bits) and the
- * sum is accumulated in fp32; the result matches an fp64 reference within
- * 2e-3*|y| + 2^-14 * sum_k |w x|.  Deterministic: the summation order depends
- * only on N, K and batch.
+ * sum is accumulated in fp32: each output is the bf16 rounding (nearest even)
+ * of a value within 2^-14 * sum_k |w x| of the exact sum, so
+ * |y - exact| <= 2^-8 |exact| + (1 + 2^-8) 2^-14 sum_k |w x|.  Deterministic:
+ * the summation order depends only on N, K and batch.
  * Returns NF4_EINVAL for NULL pointers with N*K > 0, N < 0, K < 0, odd K,
  * batch outside 1..8, or bad block sizes.
  */
@@ -123,6 +124,89 @@ nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16
                     const uint16_t* code2, float offset, int64_t N, int64_t K,
                     int32_t blocksize, int32_t s2_blocksize, const uint16_t* x, int32_t batch,
                     uint16_t* y, void* stream);
+
+/*
+ * One matrix of a grouped GEMV (64 bytes; all pointers are device pointers).
+ */
+typedef struct nf4_gemv_desc {
+  const uint8_t* packed;      /* packed codes of W [N][K], 16-byte aligned */
+  const uint8_t* absmax_q;    /* per-block code2 index */
+  const uint16_t* absmax2;    /* per-group fp16 scale */
+  const uint16_t* x;          /* bf16 [batch][K], 16-byte aligned */
+  uint16_t* y;                /* bf16 [batch][N] output */
+  int64_t N;                  /* rows of W */
+  int64_t row_begin;          /* sum of N over the preceding descriptors */
+  float offset;               /* fp32 offset of this tensor */
+  int32_t reserved;           /* set to 0 */
+} nf4_gemv_desc;
+
+/*
+ * nf4_gemv_grouped -- nf4_gemv over a list of matrices in one launch, for
+ * independent products that share K, the block sizes, code2 and the batch
+ * (e.g. the q/k/v or gate/up projections of a decoder layer, or a whole weight
+ * sweep).  Same arithmetic and tolerance as nf4_gemv; each y is written once.
+ * The launch streams the concatenated rows of all matrices through one
+ * persistent grid, so the per-launch ramp-up and drain are paid once.
+ *
+ *  descs         : DEVICE array of `count` descriptors (8-byte aligned), built
+ *                  by the caller; row_begin must be the running sum of N.
+ *  count         : 1..1024 descriptors (0 is a no-op).
+ *  total_rows    : sum of N over all descriptors, < 2^31.
+ *  K             : input features shared by all matrices; K % 32 == 0 and
+ *                  K <= 16384.
+ *  blocksize     : power of two >= 32; s2_blocksize: power of two.
+ *  code2         : device fp16 bits [256] shared by all matrices.
+ *  batch         : 1 or 2.
+ * Returns NF4_EINVAL for a NULL or misaligned descs / code2, odd K or bad
+ * block sizes; NF4_EUNSUPPORTED outside the ranges above.  The descriptors are
+ * read on the device: a matrix whose packed or x pointer is not 16-byte
+ * aligned, whose pointers are NULL, or whose N disagrees with the row_begin
+ * sequence is skipped (its y is left unwritten).
+ */
+nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t total_rows,
+                            int64_t K, int32_t blocksize, int32_t s2_blocksize,
+                            const uint16_t* code2, int32_t batch, void* stream);
+
+/*
+ * nf4_code2_linear -- the linear second-level code table: out[i] = the fp16
+ * nearest to -1 + 2 i / 255, i = 0..255 (host function, no GPU work).  The
+ * report's §1.2 fixes code2 as fp16[256]; evenly spaced values are this
+ * library's default table.
+ */
+void nf4_code2_linear(uint16_t out[256]);
+
+/*
+ * nf4_quantize_workspace_size -- bytes of device workspace nf4_quantize needs
+ * for n elements at this blocksize (0 for n <= 0).
+ */
+size_t nf4_quantize_workspace_size(int64_t n, int32_t blocksize);
+
+/*
+ * nf4_quantize -- encode n fp32 weights into the format above on the GPU.
+ * Follows [blog] "双量化" and [report] §1.1-§1.2: per block absmax, nearest
+ * NF4 code of w / absmax (two codes per byte, even element high); the block
+ * absmax values are centred by offset (their mean), grouped by s2_blocksize,
+ * absmax2 = fp16 of the group's largest |centred value|, absmax_q = index of
+ * the nearest code2 entry to centred / absmax2.  Ties go to the smaller
+ * index; an all-zero block gets code 7 (exact zero).  The mean is an fp64 sum
+ * over chunks of 1024 consecutive blocks, each chunk and then the chunk sums
+ * in index order, rounded once to fp32: the result does not depend on the
+ * launch and is bit-identical on every run.
+ *
+ *  w             : device fp32[n] (flattened weights).
+ *  code2         : device fp16 bits [256] (e.g. nf4_code2_linear uploaded).
+ *  packed, absmax_q, absmax2 : device outputs, sizes as in the format above.
+ *  offset        : device fp32[1] output (read it back to pass it by value to
+ *                  nf4_dequant / nf4_gemv).
+ *  workspace     : device scratch of at least nf4_quantize_workspace_size()
+ *                  bytes, 256-byte aligned, owned by the caller.
+ * Returns NF4_EINVAL on NULL pointers (n > 0), bad block sizes, a short or
+ * unaligned workspace.
+ */
+nf4_status nf4_quantize(const float* w, int64_t n, int32_t blocksize, int32_t s2_blocksize,
+                        const uint16_t* code2, uint8_t* packed, uint8_t* absmax_q,
+                        uint16_t* absmax2, float* offset, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -86,3 +86,29 @@ def test_gemv_empty_is_a_no_op(lib):
 def test_oversized_requests_are_unsupported(lib):
     assert _dq(lib, n=1 << 41) == 2
     assert _gv(lib, N=1 << 30, K=1 << 12) == 2
+
+
+def test_code2_linear_table_matches_oracle(lib):
+    """The library's host-side code2 table (independent code) equals the
+    oracle's: fp16 nearest to -1 + 2 i / 255."""
+    import numpy as np
+
+    import oracle
+    import w4a16_gemv_amd as nf4
+    assert np.array_equal(nf4.nf4_code2_linear().numpy().view(np.uint16), oracle.code2_linear())
+
+
+def test_quantize_workspace_size(lib):
+    assert lib.nf4_quantize_workspace_size(0, 64) == 0
+    ws = lib.nf4_quantize_workspace_size(1 << 20, 64)
+    assert ws >= (1 << 14) * 4 + 16 * 8
+
+
+@pytest.mark.parametrize("kw", [dict(n=-1), dict(bs=3), dict(s2=0), dict(w=None),
+                                dict(ws_bytes=16), dict(ws=C.c_void_p(0x1010))])
+def test_quantize_rejects_bad_arguments(lib, kw):
+    n = kw.get("n", 4096)
+    ws_bytes = kw.get("ws_bytes", 1 << 20)
+    rc = lib.nf4_quantize(kw.get("w", FAKE), n, kw.get("bs", 64), kw.get("s2", 256), FAKE, FAKE,
+                          FAKE, FAKE, FAKE, kw.get("ws", FAKE), ws_bytes, None)
+    assert rc == 1

@@ -253,3 +253,61 @@ def test_gemv_is_deterministic():
     a = run_gemv(q, N, K, xb)
     b = run_gemv(q, N, K, xb)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# grouped GEMV (one launch over several matrices)
+# ---------------------------------------------------------------------------
+
+def _group_case(shapes_seeds, K, batch, x_seed):
+    qs, items, ys = [], [], []
+    for N, seed in shapes_seeds:
+        q = oracle.quantize(synth.weights(seed, N * K))
+        d = G.fmt_to_device(q)
+        w = nf4.NF4Tensor(d["packed"], d["absmax_q"], d["absmax2"], d["code2"], q.offset, q.n)
+        xb = synth.activations(x_seed + seed, batch, K)
+        base, yv = G.guarded(batch * N, torch.bfloat16)
+        items.append((w, N, G.x_to_device(xb), yv.view(batch, N)))
+        qs.append((q, N, xb, base))
+    return qs, items
+
+
+@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("K,shapes", [
+    (4096, [(4096, 600), (4096, 601), (11008, 602), (256, 603), (1, 604), (37, 605)]),
+    (1536, [(1536, 610), (256, 611), (256, 612), (8960, 613)]),
+    (11008, [(4096, 620), (3, 621)]),
+    (96, [(5, 630)]),
+])
+def test_gemv_grouped_matches_oracle(K, shapes, batch):
+    qs, items = _group_case(shapes, K, batch, 700)
+    grp = nf4.GemvGroup(items, K)
+    print(f"[gemv_grouped] K={K} B={batch} N={[n for n, _ in shapes]}", flush=True)
+    grp.launch()
+    torch.cuda.synchronize()
+    for (q, N, xb, base), (_, _, _, yv) in zip(qs, items):
+        assert G.guards_intact(base, batch * N), "write outside y"
+        y = G.bf16_to_f64(G.bits16(yv)).reshape(batch, N)
+        yr, S = oracle.gemv(q, N, K, xb)
+        ok, worst = G.gemv_within_tolerance(y, yr, S)
+        assert ok, f"grouped N={N} K={K}: worst {worst:.3g}"
+
+
+def test_gemv_grouped_skips_bad_descriptors():
+    """A descriptor whose N disagrees with the row offsets is skipped: its y
+    keeps its old contents; the others are still computed."""
+    import numpy as np
+    K = 512
+    qs, items = _group_case([(64, 640), (32, 641)], K, 1, 750)
+    grp = nf4.GemvGroup(items, K)
+    tab = grp.table.cpu().numpy().copy().view(np.int64).reshape(len(items), 8)
+    tab[1, 5] = 31                                    # N of item 1 no longer matches
+    grp.table.copy_(torch.from_numpy(tab.view(np.uint8).reshape(-1)))
+    items[1][3].fill_(3.0)
+    grp.launch()
+    torch.cuda.synchronize()
+    assert torch.all(items[1][3] == 3.0)
+    q, N, xb, base = qs[0]
+    y = G.bf16_to_f64(G.bits16(items[0][3])).reshape(1, N)
+    yr, S = oracle.gemv(q, N, K, xb)
+    assert G.gemv_within_tolerance(y, yr, S)[0]

@@ -6,6 +6,7 @@ its Python binding.  See nf4_dequant / nf4_gemv.
 """
 from ._binding import (  # noqa: F401
     EXPORTED,
+    GemvGroup,
     LIB_PATH,
     NF4_BF16,
     NF4_EHIP,
@@ -14,9 +15,12 @@ from ._binding import (  # noqa: F401
     NF4_FP16,
     NF4_OK,
     NF4Error,
+    NF4Tensor,
     format_sizes,
     load,
+    nf4_code2_linear,
     nf4_dequant,
     nf4_gemv,
+    nf4_quantize,
     status_string,
 )

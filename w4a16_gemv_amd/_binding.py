@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(_PKG, "libnf4.so")
 NF4_OK, NF4_EINVAL, NF4_EUNSUPPORTED, NF4_EHIP = 0, 1, 2, 3
 NF4_BF16, NF4_FP16 = 0, 1
 
-EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv")
+EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv",
+            "nf4_gemv_grouped", "nf4_code2_linear", "nf4_quantize_workspace_size",
+            "nf4_quantize")
 
 _lib = None
 
@@ -47,6 +49,14 @@ def load() -> C.CDLL:
     lib.nf4_dequant.argtypes = [p, p, p, p, f32, i64, i32, i32, p, i32, p]
     lib.nf4_gemv.restype = C.c_int
     lib.nf4_gemv.argtypes = [p, p, p, p, f32, i64, i64, i32, i32, p, i32, p, p]
+    lib.nf4_gemv_grouped.restype = C.c_int
+    lib.nf4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, i32, p]
+    lib.nf4_code2_linear.restype = None
+    lib.nf4_code2_linear.argtypes = [p]
+    lib.nf4_quantize_workspace_size.restype = C.c_size_t
+    lib.nf4_quantize_workspace_size.argtypes = [i64, i32]
+    lib.nf4_quantize.restype = C.c_int
+    lib.nf4_quantize.argtypes = [p, i64, i32, i32, p, p, p, p, p, p, C.c_size_t, p]
     _lib = lib
     return lib
 
@@ -135,3 +145,134 @@ def nf4_gemv(packed, absmax_q, absmax2, code2, offset: float, N: int, K: int, x:
                          int(s2_blocksize), px, int(batch), py, _stream(y))
     _check("nf4_gemv", st)
     return y.view(int(N)) if squeeze and y.dim() == 2 else y
+
+
+def nf4_code2_linear() -> torch.Tensor:
+    """The linear code2 table (CPU int16 tensor of fp16 bit patterns)."""
+    out = torch.empty(256, dtype=torch.int16)
+    load().nf4_code2_linear(out.data_ptr())
+    return out
+
+
+class NF4Tensor:
+    """A flattened tensor in the double-quantized NF4 format, on the GPU."""
+
+    def __init__(self, packed, absmax_q, absmax2, code2, offset: float, n: int,
+                 blocksize: int = 64, s2_blocksize: int = 256):
+        self.packed, self.absmax_q, self.absmax2, self.code2 = packed, absmax_q, absmax2, code2
+        self.offset, self.n = float(offset), int(n)
+        self.blocksize, self.s2_blocksize = int(blocksize), int(s2_blocksize)
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.packed, self.absmax_q, self.absmax2, self.code2)) + 4
+
+    def dequant(self, out=None, out_dtype=torch.bfloat16):
+        return nf4_dequant(self.packed, self.absmax_q, self.absmax2, self.code2, self.offset,
+                           self.n, self.blocksize, self.s2_blocksize, out, out_dtype)
+
+    def gemv(self, N: int, K: int, x, y=None):
+        if N * K != self.n:
+            raise ValueError(f"N*K={N * K} does not match the tensor's {self.n} elements")
+        return nf4_gemv(self.packed, self.absmax_q, self.absmax2, self.code2, self.offset, N, K,
+                        x, self.blocksize, self.s2_blocksize, y)
+
+
+def nf4_quantize(w: torch.Tensor, blocksize: int = 64, s2_blocksize: int = 256,
+                 code2: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 sync_offset: bool = True):
+    """Encode fp32 weights (any shape, flattened) into an NF4Tensor on w's GPU.
+
+    With sync_offset (default) the fp32 offset is read back to the host (one
+    stream synchronization); otherwise NF4Tensor.offset is NaN and the device
+    value is returned as a second result."""
+    if w.dtype != torch.float32:
+        raise ValueError("w must be float32")
+    n = w.numel()
+    nbytes, nb, ng = format_sizes(n, int(blocksize), int(s2_blocksize))
+    devc = w.device
+    if code2 is None:
+        code2 = nf4_code2_linear().to(devc)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=devc)
+    absmax_q = torch.empty(nb, dtype=torch.uint8, device=devc)
+    absmax2 = torch.empty(ng, dtype=torch.int16, device=devc)
+    off = torch.zeros(1, dtype=torch.float32, device=devc)
+    need = int(load().nf4_quantize_workspace_size(n, int(blocksize)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=devc)
+    wc = w.contiguous().view(-1)
+    st = load().nf4_quantize(_dev(wc, "w", (torch.float32,), n), n, int(blocksize),
+                             int(s2_blocksize), _dev(code2, "code2", _HALF_BITS, 256),
+                             packed.data_ptr(), absmax_q.data_ptr(), absmax2.data_ptr(),
+                             off.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                             _stream(wc))
+    _check("nf4_quantize", st)
+    if sync_offset:
+        return NF4Tensor(packed, absmax_q, absmax2, code2, off.item(), n, blocksize, s2_blocksize)
+    return NF4Tensor(packed, absmax_q, absmax2, code2, float("nan"), n, blocksize,
+                     s2_blocksize), off
+
+
+# layout of nf4_gemv_desc (include/nf4.h), 64 bytes
+_DESC_DTYPE = [("packed", "<u8"), ("absmax_q", "<u8"), ("absmax2", "<u8"), ("x", "<u8"),
+               ("y", "<u8"), ("N", "<i8"), ("row_begin", "<i8"), ("offset", "<f4"),
+               ("reserved", "<i4")]
+MAX_GROUP = 1024
+
+
+class GemvGroup:
+    """A reusable list of independent GEMVs y_i = W_i x_i launched as one
+    nf4_gemv_grouped call.  All W_i share K, the block sizes, code2 and the
+    batch (1 or 2).  The descriptor table is built and uploaded once; launch()
+    only enqueues the kernel (so it can be captured in a HIP graph).
+
+    items: list of (w: NF4Tensor, N, x: bf16 [batch][K] tensor, y: bf16 [batch][N] tensor).
+    """
+
+    def __init__(self, items, K: int):
+        import numpy as np
+        if not 1 <= len(items) <= MAX_GROUP:
+            raise ValueError(f"a group holds 1..{MAX_GROUP} matrices")
+        self.K = int(K)
+        self.items = list(items)
+        w0 = items[0][0]
+        self.blocksize, self.s2_blocksize, self.code2 = w0.blocksize, w0.s2_blocksize, w0.code2
+        self.batch = items[0][2].shape[0] if items[0][2].dim() == 2 else 1
+        if self.batch not in (1, 2):
+            raise ValueError("grouped GEMV supports batch 1 or 2")
+        if K % 32 or K <= 0 or K > 16384:
+            raise ValueError("grouped GEMV needs K % 32 == 0 and 0 < K <= 16384")
+        if self.blocksize < 32:
+            raise ValueError("grouped GEMV needs blocksize >= 32")
+        table = np.zeros(len(items), dtype=np.dtype(_DESC_DTYPE))
+        row = 0
+        for i, (w, N, x, y) in enumerate(items):
+            if w.n != N * K:
+                raise ValueError(f"item {i}: tensor has {w.n} elements, expected {N}x{K}")
+            if (w.blocksize, w.s2_blocksize) != (self.blocksize, self.s2_blocksize):
+                raise ValueError(f"item {i}: block sizes differ from the group's")
+            if w.code2.data_ptr() != self.code2.data_ptr() and not torch.equal(w.code2, self.code2):
+                raise ValueError(f"item {i}: code2 differs from the group's")
+            xb = x if x.dim() == 2 else x.unsqueeze(0)
+            if xb.shape != (self.batch, K):
+                raise ValueError(f"item {i}: x must be [{self.batch}, {K}]")
+            nbytes, nb, ng = format_sizes(w.n, w.blocksize, w.s2_blocksize)
+            pp = _dev(w.packed, "packed", _U8, nbytes)
+            px = _dev(xb, "x", _BF16_BITS, self.batch * K)
+            py = _dev(y, "y", _BF16_BITS, self.batch * N)
+            if pp % 16 or px % 16:
+                raise ValueError(f"item {i}: packed and x must be 16-byte aligned")
+            table[i] = (pp, _dev(w.absmax_q, "absmax_q", _U8, nb),
+                        _dev(w.absmax2, "absmax2", _HALF_BITS, ng), px, py, N, row, w.offset, 0)
+            row += N
+        self.total_rows = row
+        dev = items[0][0].packed.device
+        self.table = torch.from_numpy(table.view(np.uint8)).to(dev)
+        _dev(self.code2, "code2", _HALF_BITS, 256)
+
+    def launch(self) -> None:
+        st = load().nf4_gemv_grouped(self.table.data_ptr(), len(self.items), self.total_rows,
+                                     self.K, self.blocksize, self.s2_blocksize,
+                                     self.code2.data_ptr(), self.batch, _stream(self.table))
+        _check("nf4_gemv_grouped", st)

@@ -16,7 +16,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "nf4_kernels.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("nf4_kernels.hip", "nf4_quantize.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnf4.so")
 
@@ -36,7 +36,7 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", LIB + ".tmp", SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", LIB + ".tmp", *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

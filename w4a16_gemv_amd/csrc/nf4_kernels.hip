@@ -21,53 +21,11 @@
 #include <stdint.h>
 
 #include "nf4.h"
+#include "nf4_device.h"
 
 namespace {
 
-// The 16 NF4 code values, as the 8-decimal literals printed in [blog] "naive";
-// each literal is rounded to the nearest fp32 by the compiler.
-__device__ const float kNF4[16] = {
-    -1.00000000f, -0.69619280f, -0.52507305f, -0.39491749f,
-    -0.28444138f, -0.18477343f, -0.09105004f, 0.00000000f,
-    0.07958030f,  0.16093020f,  0.24611230f,  0.33791524f,
-    0.44070983f,  0.56261700f,  0.72295684f,  1.00000000f,
-};
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float f16_to_f32(uint16_t h) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, h));  // exact widening
-}
-
-// Pin a value as an fp32 register.  Without it the compiler may fold an fp32
-// multiply and the following 16-bit conversion into one mixed-precision fma
-// (v_fma_mixlo_f16), which rounds the exact product straight to fp16 and skips
-// the fp32 rounding the method prescribes (a double-rounding difference).
-__device__ __forceinline__ float as_fp32(float v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-// Two 16-bit outputs in one dword: the even element in the low half (lower
-// address), the odd element in the high half.  Both inputs are first pinned as
-// rounded fp32 values.
-template <int OUT>
-__device__ __forceinline__ uint32_t pack_pair(float even, float odd) {
-  even = as_fp32(even);
-  odd = as_fp32(odd);
-  if constexpr (OUT == NF4_BF16) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){even, odd}, bf16x2));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){even, odd}, f16x2));
-  }
-}
-
-template <int OUT>
-__device__ __forceinline__ uint16_t to_half_bits(float v) {
-  return static_cast<uint16_t>(pack_pair<OUT>(v, 0.0f) & 0xFFFFu);
-}
+using namespace nf4dev;
 
 // absmax_real of one first-level block: fp32 product, then fp32 sum.
 __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ absmax_q,
@@ -254,6 +212,8 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
 constexpr int kSlab = 2048;
 constexpr int kPairCopies = 32;
 
+constexpr int kMaxDescs = 1024;  // matrices per grouped launch
+
 template <int R>
 struct RowGroup {
   uint4 pk[R];
@@ -261,27 +221,53 @@ struct RowGroup {
   float a2[R];
 };
 
+// Loads the packed chunk and block-scale inputs of rows [rl, rl + len) of one
+// matrix (len <= R; missing rows read as zero codes).
 template <int R>
-__device__ __forceinline__ void load_row_group(RowGroup<R>& rg, int g, bool active, int N, int K,
-                                               int k0, const uint4* __restrict__ packed16,
-                                               const uint8_t* __restrict__ absmax_q,
-                                               const uint16_t* __restrict__ absmax2, int log2bs,
-                                               int log2s2) {
+__device__ __forceinline__ void load_row_group(RowGroup<R>& rg, const nf4_gemv_desc& d,
+                                               int64_t rl, int len, bool active, int K, int k0,
+                                               int log2bs, int log2s2) {
+  const uint4* __restrict__ packed16 = reinterpret_cast<const uint4*>(d.packed);
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
-    const int r = g * R + rr;
-    if (active && r < N) {
-      const int64_t e = static_cast<int64_t>(r) * K + k0;
+    if (active && rr < len) {
+      const int64_t e = (rl + rr) * K + k0;
       const int64_t blk = e >> log2bs;
       rg.pk[rr] = packed16[e >> 5];
-      rg.q[rr] = absmax_q[blk];
-      rg.a2[rr] = f16_to_f32(absmax2[blk >> log2s2]);
+      rg.q[rr] = d.absmax_q[blk];
+      rg.a2[rr] = f16_to_f32(d.absmax2[blk >> log2s2]);
     } else {
       rg.pk[rr] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);  // zeros
       rg.q[rr] = 0;
       rg.a2[rr] = 0.0f;
     }
   }
+}
+
+template <int B>
+__device__ __forceinline__ void load_x(uint4 (&xr)[B][4], const uint16_t* __restrict__ x, int K,
+                                       int k0, bool active) {
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xr[b][j] = active ? *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(b) * K + k0 + 8 * j)
+                        : make_uint4(0u, 0u, 0u, 0u);
+}
+
+template <int B>
+__device__ __forceinline__ void widen_x(float (&xv)[B][32], const uint4 (&xr)[B][4]) {
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w4[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[b][8 * j + 2 * i] = __builtin_bit_cast(float, w4[i] << 16);
+        xv[b][8 * j + 2 * i + 1] = __builtin_bit_cast(float, w4[i] & 0xFFFF0000u);
+      }
+    }
 }
 
 // part[b] += sum over the 8 weights of dword d (columns 8 j .. 8 j + 7 of the
@@ -304,68 +290,172 @@ __device__ __forceinline__ void dot_dword_pairs(uint32_t d, uint32_t copy_off,
   }
 }
 
+// A descriptor the streaming kernel can read: 16-byte aligned packed weights
+// and activations, and a row count that matches the row offsets.  Matrices
+// that fail this are skipped (their y is not written).
+__device__ __forceinline__ bool desc_usable(const nf4_gemv_desc& d, int rows) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(d.packed) | reinterpret_cast<uintptr_t>(d.x);
+  return (a & 15) == 0 && d.N == rows && d.packed && d.absmax_q && d.absmax2 && d.x && d.y;
+}
+
+// Field-wise copy of descriptor m (or of the by-value descriptor when the
+// list is absent).  m is wave-uniform, so these become scalar loads; copying
+// the struct as a whole would go through scratch memory.
+__device__ __forceinline__ nf4_gemv_desc fetch_desc(const nf4_gemv_desc* __restrict__ descs,
+                                                    const nf4_gemv_desc& single, int m) {
+  nf4_gemv_desc d;
+  if (descs == nullptr || m < 0) {
+    d.packed = single.packed;
+    d.absmax_q = single.absmax_q;
+    d.absmax2 = single.absmax2;
+    d.x = single.x;
+    d.y = single.y;
+    d.N = single.N;
+    d.offset = single.offset;
+  } else {
+    const nf4_gemv_desc* p = descs + m;
+    d.packed = p->packed;
+    d.absmax_q = p->absmax_q;
+    d.absmax2 = p->absmax2;
+    d.x = p->x;
+    d.y = p->y;
+    d.N = p->N;
+    d.offset = p->offset;
+  }
+  d.row_begin = 0;
+  d.reserved = 0;
+  return d;
+}
+
+// Where a team is in the concatenated row space: matrix m, global row r.
+struct RowCursor {
+  int m;
+  int r;
+};
+
+// The next group of at most R rows from cursor c, not crossing a matrix end or
+// the team's range end; advances c.  Returns the group's length (0 when the
+// range is exhausted).
+template <int R>
+__device__ __forceinline__ int next_group(RowCursor& c, int r_end, const int* s_rowbeg, int count,
+                                          int* m_out, int* rl_out) {
+  while (c.m < count && s_rowbeg[c.m + 1] <= c.r) ++c.m;  // skip finished / empty matrices
+  if (c.r >= r_end || c.m >= count) {
+    *m_out = -1;
+    *rl_out = 0;
+    return 0;
+  }
+  const int lim = min(r_end, s_rowbeg[c.m + 1]);
+  const int len = min(R, lim - c.r);
+  *m_out = c.m;
+  *rl_out = c.r - s_rowbeg[c.m];
+  c.r += len;
+  return len;
+}
+
+// ---------------------------------------------------------------------------
+// The streaming GEMV kernel: one launch over a list of matrices that share K,
+// the block sizes, code2 and the batch (a single nf4_gemv is a list of one).
+// The concatenated rows of all matrices are split evenly into contiguous
+// ranges, one per team; a team walks its range in groups of up to R rows
+// (never crossing a matrix), prefetching the next group while computing the
+// current one, and reloads its activations when the matrix changes.
+// ---------------------------------------------------------------------------
 template <int B, int R>
-__global__ __launch_bounds__(512) void gemv_stream_kernel(
-    const uint4* __restrict__ packed16, const uint8_t* __restrict__ absmax_q,
-    const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
-    int N, int K, int log2bs, int log2s2, int nw, const uint16_t* __restrict__ x,
-    uint16_t* __restrict__ y) {
-  __shared__ float2 s_pairs[256 * kPairCopies];  // 64 KiB
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_stream_kernel(
+    const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
+    int K, int log2bs, int log2s2, int nw, const uint16_t* __restrict__ code2) {
+  __shared__ float2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
   __shared__ float s_nf4[16];
   __shared__ float s_code2[256];
   __shared__ float s_red[2][8][R * B];
+  __shared__ int s_rowbeg[kMaxDescs + 1];
+  __shared__ int s_iters;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int team = wave / nw;
-  const int slab = wave - team * nw;
   const int teams = (blockDim.x >> 6) / nw;
+  const int team = wave / nw;           // == teams for helper waves
+  const int slab = wave - team * nw;
+  const bool in_team = team < teams;
   const int k0 = slab * kSlab + lane * 32;
-  const bool active = k0 < K;
-  const int ngroups = (N + R - 1) / R;
-  const int gstride = static_cast<int>(gridDim.x) * teams;
+  const bool active = in_team && k0 < K;
 
-  // global loads first: activations, tables, the team's first row group
-  uint4 xr[B][4];
-#pragma unroll
-  for (int b = 0; b < B; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      xr[b][j] = active ? *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(b) * K + k0 + 8 * j)
-                        : make_uint4(0u, 0u, 0u, 0u);
+  // descriptor row offsets, code2 and the NF4 table into LDS
+  if (descs == nullptr) {
+    if (tid == 0) s_rowbeg[0] = 0;
+  } else {
+    for (int i = tid; i < count; i += blockDim.x) s_rowbeg[i] = static_cast<int>(descs[i].row_begin);
+  }
+  if (tid == 0) {
+    s_rowbeg[count] = total_rows;
+    s_iters = 0;
+  }
   for (int i = tid; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
   if (tid < 16) s_nf4[tid] = kNF4[tid];
-  int g = blockIdx.x * teams + team;
-  RowGroup<R> cur;
-  load_row_group<R>(cur, g, active, N, K, k0, packed16, absmax_q, absmax2, log2bs, log2s2);
   __syncthreads();
+
+  // the team's row range and its first group
+  const int64_t tt = static_cast<int64_t>(gridDim.x) * teams;
+  const int64_t tg = static_cast<int64_t>(blockIdx.x) * teams + team;
+  const int r_begin = in_team ? static_cast<int>(tg * total_rows / tt) : 0;
+  const int r_end = in_team ? static_cast<int>((tg + 1) * total_rows / tt) : 0;
+  RowCursor cur_c;
+  {
+    int lo = 0, hi = count - 1;  // last matrix whose first row is <= r_begin
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_rowbeg[mid] <= r_begin) lo = mid; else hi = mid - 1;
+    }
+    cur_c.m = lo;
+    cur_c.r = r_begin;
+  }
+  // number of groups of this team (per matrix it overlaps), then the
+  // workgroup maximum: every wave runs that many iterations
+  {
+    int ng = 0;
+    for (int mm = cur_c.m; mm < count && s_rowbeg[mm] < r_end; ++mm) {
+      const int lo = max(r_begin, s_rowbeg[mm]);
+      const int hi = min(r_end, s_rowbeg[mm + 1]);
+      if (hi > lo) ng += (hi - lo + R - 1) / R;
+    }
+    if (lane == 0 && slab == 0 && in_team) atomicMax(&s_iters, ng);
+  }
+
+  int m, rl;
+  int len = next_group<R>(cur_c, r_end, s_rowbeg, count, &m, &rl);
+  m = __builtin_amdgcn_readfirstlane(m);
+  nf4_gemv_desc d = fetch_desc(descs, single, m);
+  if (len > 0 && !desc_usable(d, s_rowbeg[m + 1] - s_rowbeg[m])) len = 0;
+  uint4 xr[B][4];
+  load_x<B>(xr, d.x, K, k0, active && len > 0);
+  RowGroup<R> cur;
+  load_row_group<R>(cur, d, rl, len, active, K, k0, log2bs, log2s2);
+
+  // the 256 x 32 pair table
   for (int e = tid; e < 256 * kPairCopies; e += blockDim.x) {
     const int b = e / kPairCopies;
     s_pairs[e] = make_float2(s_nf4[b >> 4], s_nf4[b & 15]);
   }
-
   float xv[B][32];
-#pragma unroll
-  for (int b = 0; b < B; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w4[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xv[b][8 * j + 2 * i] = __builtin_bit_cast(float, w4[i] << 16);
-        xv[b][8 * j + 2 * i + 1] = __builtin_bit_cast(float, w4[i] & 0xFFFF0000u);
-      }
-    }
+  widen_x<B>(xv, xr);
   const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
   __syncthreads();
+  const int iters = s_iters;
 
-  // every team runs the same number of iterations (barriers inside)
-  const int iters = (ngroups - static_cast<int>(blockIdx.x) * teams + gstride - 1) / gstride;
   int buf = 0;
-  for (int it = 0; it < iters; ++it, g += gstride) {
+  for (int it = 0; it < iters; ++it) {
+    // prefetch the next group (and its activations if the matrix changes)
+    int m2, rl2;
+    const int len2 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m2, &rl2);
+    m2 = __builtin_amdgcn_readfirstlane(m2);
+    const nf4_gemv_desc d2 = (len2 > 0 && m2 != m) ? fetch_desc(descs, single, m2) : d;
+    const bool usable = len2 > 0 && desc_usable(d2, s_rowbeg[m2 + 1] - s_rowbeg[m2]);
+    const bool new_x = usable && m2 != m;
+    if (new_x) load_x<B>(xr, d2.x, K, k0, active);
     RowGroup<R> nxt;
-    load_row_group<R>(nxt, g + gstride, active, N, K, k0, packed16, absmax_q, absmax2, log2bs,
-                      log2s2);
+    load_row_group<R>(nxt, d2, rl2, usable ? len2 : 0, active, K, k0, log2bs, log2s2);
+
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       float part[B];
@@ -376,7 +466,7 @@ __global__ __launch_bounds__(512) void gemv_stream_kernel(
       dot_dword_pairs<B>(cur.pk[rr].z, copy_off, xv, 2, s_pairs, part);
       dot_dword_pairs<B>(cur.pk[rr].w, copy_off, xv, 3, s_pairs, part);
       const float prod = s_code2[cur.q[rr]] * cur.a2[rr];
-      const float a = prod + offset;
+      const float a = prod + d.offset;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const float tot = wave_sum_to_lane63(a * part[b]);
@@ -384,15 +474,19 @@ __global__ __launch_bounds__(512) void gemv_stream_kernel(
       }
     }
     __syncthreads();
-    if (slab == 0 && lane < R * B) {
+    if (in_team && slab == 0 && lane < R * B) {
       const int rr = lane / B, b = lane % B;
       float acc = s_red[buf][wave][lane];
       for (int w = 1; w < nw; ++w) acc += s_red[buf][wave + w][lane];
-      const int r = g * R + rr;
-      if (g < ngroups && r < N) y[static_cast<int64_t>(b) * N + r] = to_half_bits<NF4_BF16>(acc);
+      if (rr < len) d.y[static_cast<int64_t>(b) * d.N + rl + rr] = to_half_bits<NF4_BF16>(acc);
     }
     buf ^= 1;
+    if (new_x) widen_x<B>(xv, xr);
     cur = nxt;
+    d = d2;
+    m = len2 > 0 ? m2 : m;
+    rl = rl2;
+    len = usable ? len2 : 0;
   }
 }
 
@@ -619,6 +713,24 @@ nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const 
   return launch_status();
 }
 
+constexpr int kStreamR = 4;
+
+template <int B>
+nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
+                         int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
+                         hipStream_t st) {
+  const int nw = (K + kSlab - 1) / kSlab;
+  const int teams = 8 / nw;
+  // persistent: at most two 512-lane workgroups per CU (the decode table takes
+  // 64 KiB of LDS), at least one row per team
+  const int64_t max_wg = static_cast<int64_t>(device_cus()) * 2;
+  const int64_t want = (static_cast<int64_t>(total_rows) + teams - 1) / teams;
+  const int64_t grid = want < max_wg ? (want > 0 ? want : 1) : max_wg;
+  hipLaunchKernelGGL((gemv_stream_kernel<B, kStreamR>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, nw, code2);
+  return launch_status();
+}
+
 template <int B>
 nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
                          const uint16_t* code2, float offset, int64_t N, int64_t K, int lbs,
@@ -626,20 +738,18 @@ nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const u
   const bool vec = lbs >= 5 && K % 32 == 0 && K <= 8 * kSlab && N <= 0x7FFFFFFF &&
                    aligned(packed, 16) && aligned(x, 16);
   if constexpr (B <= 2) {
-    if (vec) {
-      constexpr int R = 4;
-      const int nw = static_cast<int>((K + kSlab - 1) / kSlab);
-      const int teams = 8 / nw;
-      const int64_t ngroups = (N + R - 1) / R;
-      // two 512-lane workgroups per CU (the decode table takes 64 KiB of LDS)
-      const int64_t max_wg = static_cast<int64_t>(device_cus()) * 2;
-      const int64_t per_wg = (ngroups + max_wg * teams - 1) / (max_wg * teams);  // groups per team
-      const int64_t grid = (ngroups + per_wg * teams - 1) / (per_wg * teams);
-      hipLaunchKernelGGL((gemv_stream_kernel<B, R>), dim3(static_cast<uint32_t>(grid)),
-                         dim3(64 * nw * teams), 0, st, reinterpret_cast<const uint4*>(packed),
-                         absmax_q, absmax2, code2, offset, static_cast<int>(N), static_cast<int>(K),
-                         lbs, ls2, nw, x, y);
-    return launch_status();
+    if (vec && N < 0x7FFFFFFF) {
+      nf4_gemv_desc one{};
+      one.packed = packed;
+      one.absmax_q = absmax_q;
+      one.absmax2 = absmax2;
+      one.x = x;
+      one.y = y;
+      one.N = N;
+      one.row_begin = 0;
+      one.offset = offset;
+      return stream_launch<B>(nullptr, one, 1, static_cast<int>(N), static_cast<int>(K), lbs, ls2,
+                              code2, st);
     }
   }
   if (vec) {
@@ -724,6 +834,26 @@ nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16
 #undef NF4_GEMV_CASE
   }
   return NF4_EINVAL;
+}
+
+nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t total_rows,
+                            int64_t K, int32_t blocksize, int32_t s2_blocksize,
+                            const uint16_t* code2, int32_t batch, void* stream) {
+  int lbs = 0, ls2 = 0;
+  if (!pow2_log2(blocksize, &lbs) || !pow2_log2(s2_blocksize, &ls2)) return NF4_EINVAL;
+  if (count < 0 || total_rows < 0 || K < 0 || (K & 1)) return NF4_EINVAL;
+  if (count == 0 || total_rows == 0) return NF4_OK;
+  if (!descs || !code2 || (reinterpret_cast<uintptr_t>(descs) & 7)) return NF4_EINVAL;
+  if (count > kMaxDescs || total_rows >= 0x7FFFFFFF || K == 0 || K % 32 != 0 ||
+      K > 8 * kSlab || lbs < 5 || batch < 1 || batch > 2)
+    return NF4_EUNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const nf4_gemv_desc none{};
+  if (batch == 1)
+    return stream_launch<1>(descs, none, count, static_cast<int>(total_rows), static_cast<int>(K),
+                            lbs, ls2, code2, st);
+  return stream_launch<2>(descs, none, count, static_cast<int>(total_rows), static_cast<int>(K),
+                          lbs, ls2, code2, st);
 }
 
 }  // extern "C"

@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Throughput of the NF4 double-quant dequant and fused W4A16 GEMV on one GPU.
+
+One step = one pass of the whole hot path over the decode-step workload of a
+32-layer 7B-shaped model: the 224 batch-1 fused GEMVs of the weight sweep
+(per layer 4 x 4096->4096, 2 x 4096->11008, 1 x 11008->4096; 6.48e9 weights,
+3.34 GB of NF4 data) plus the standalone dequant of one 8192 x 28672 weight to
+bf16.  Inputs are synthetic N(0, 0.02) weights drawn on the GPU and encoded by
+the library's own quantizer; they are resident in HBM before timing starts.
+
+Schedules (--schedule):
+  stream   (default) the sweep as one grouped launch per K (all 192 K=4096
+           GEMVs, then the 32 K=11008 ones): every weight byte streams through
+           one persistent grid, as in a weight sweep where the GEMVs are
+           independent.
+  layered  per layer: q/k/v grouped, o, gate/up grouped, down -- the launch
+           order a real decode step with layer dependencies would use.
+The step is captured once in a HIP graph and replayed.
+
+Reported: value = algorithmic bytes per step / step time (GB/s); roofline of
+the dominant kernel (the grouped GEMV) measured with HIP events on the launch
+stream; the CPU oracle timed on a bounded sample of the same workload.
+Algorithmic bytes: dequant ceil(n/2) + ceil(n/64) + 2 ceil(n/16384) + 516 + 2n;
+GEMV ceil(NK/2) + ceil(NK/64) + 2 ceil(NK/16384) + 516 + 2KB + 2NB.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "NF4 dequant & fused GEMV: achieved HBM GB/s and % of MI355X peak (1 GPU)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dequant_bytes(n: int) -> int:
+    return (n + 1) // 2 + -(-n // 64) + 2 * -(-n // 16384) + 516 + 2 * n
+
+
+def gemv_bytes(N: int, K: int, B: int = 1) -> int:
+    n = N * K
+    return (n + 1) // 2 + -(-n // 64) + 2 * -(-n // 16384) + 516 + 2 * K * B + 2 * N * B
+
+
+def build_workload(dev):
+    import torch
+
+    import synth
+    import w4a16_gemv_amd as nf4
+
+    t0 = time.time()
+    code2 = nf4.nf4_code2_linear().to(dev)
+    ws = None
+    xs = {K: synth.activations_device(synth.SWEEP_X_SEED, 1, K, dev) for K in (4096, 11008)}
+    layers = []
+    for L in range(synth.SWEEP_LAYERS):
+        mats = []
+        for g in synth.sweep_layer(L):
+            w = synth.weights_device(g.seed, g.N * g.K, dev)
+            if ws is None:
+                need = nf4.load().nf4_quantize_workspace_size(11008 * 4096, 64)
+                ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            t = nf4.nf4_quantize(w, 64, 256, code2=code2, workspace=ws)
+            del w
+            y = torch.empty(1, g.N, dtype=torch.bfloat16, device=dev)
+            mats.append((g, t, y))
+        layers.append(mats)
+    big = synth.DEQUANT_BIG
+    wb = synth.weights_device(big.seed, big.n, dev)
+    tb = nf4.nf4_quantize(wb, 64, 256, code2=code2,
+                          workspace=torch.empty(nf4.load().nf4_quantize_workspace_size(big.n, 64),
+                                                dtype=torch.uint8, device=dev))
+    del wb
+    out = torch.empty(big.n, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] workload encoded on the GPU in {time.time() - t0:.1f} s")
+    return dict(layers=layers, xs=xs, big=(big, tb, out), code2=code2)
+
+
+def make_step(wl, schedule):
+    """Returns (gemv_fns, dequant_fn, gemv_launches)."""
+    import w4a16_gemv_amd as nf4
+    xs = wl["xs"]
+    groups = []
+    if schedule == "stream":
+        for K in (4096, 11008):
+            items = [(t, g.N, xs[K], y) for mats in wl["layers"] for (g, t, y) in mats if g.K == K]
+            groups.append(nf4.GemvGroup(items, K))
+    else:
+        for mats in wl["layers"]:
+            q, k, v, o, gate, up, down = mats
+            for sel in ((q, k, v), (o,), (gate, up), (down,)):
+                K = sel[0][0].K
+                groups.append(nf4.GemvGroup([(t, g.N, xs[K], y) for (g, t, y) in sel], K))
+    big, tb, out = wl["big"]
+
+    def gemvs():
+        for grp in groups:
+            grp.launch()
+
+    def dequant():
+        tb.dequant(out=out)
+
+    return gemvs, dequant, len(groups)
+
+
+def capture(fn, stream):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()          # eager run on the capture stream first
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps  # ms
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle (plain C, OpenMP over outputs) timed on the host cores on a
+    bounded sample of the same workload: the sweep's GEMVs in order, then a
+    slice of the big dequant, until about `seconds` of CPU time is spent."""
+    import numpy as np
+    import torch
+
+    import oracle
+    threads = oracle.max_threads()
+    xs = {K: x.view(torch.int16).cpu().numpy().view(np.uint16) for K, x in wl["xs"].items()}
+    done_bytes, elapsed, ngemv = 0, 0.0, 0
+    for mats in wl["layers"]:
+        for (g, t, y) in mats:
+            q = oracle.Quantized(t.packed.cpu().numpy(), t.absmax_q.cpu().numpy(),
+                                 t.absmax2.cpu().numpy().view(np.uint16),
+                                 t.code2.cpu().numpy().view(np.uint16), t.offset, t.n)
+            s = time.perf_counter()
+            oracle.gemv(q, g.N, g.K, xs[g.K])
+            elapsed += time.perf_counter() - s
+            done_bytes += gemv_bytes(g.N, g.K)
+            ngemv += 1
+            if elapsed >= 0.8 * seconds:
+                break
+        if elapsed >= 0.8 * seconds:
+            break
+    big, tb, _ = wl["big"]
+    n_slice = min(big.n, 1 << 24)
+    q = oracle.Quantized(tb.packed[: (n_slice + 1) // 2].cpu().numpy(),
+                         tb.absmax_q[: -(-n_slice // 64)].cpu().numpy(),
+                         tb.absmax2[: -(-n_slice // 16384)].cpu().numpy().view(np.uint16),
+                         tb.code2.cpu().numpy().view(np.uint16), tb.offset, n_slice)
+    s = time.perf_counter()
+    oracle.dequant(q)
+    elapsed += time.perf_counter() - s
+    done_bytes += dequant_bytes(n_slice)
+    return {"value": round(done_bytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {ngemv} of the 224 sweep GEMVs (fp64 oracle GEMV) + the first "
+                      f"{n_slice} elements of the 8192x28672 dequant; {elapsed:.1f} s of wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--schedule", choices=("stream", "layered"), default="stream")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the NF4 dequant / GEMV path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import w4a16_gemv_amd as nf4
+    nf4.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = build_workload(dev)
+    stream = torch.cuda.Stream(dev)
+
+    per_step = {}
+    for sched in ("stream", "layered"):
+        gemvs, dequant, nlaunch = make_step(wl, sched)
+        g_step = capture(lambda: (gemvs(), dequant()), stream)
+        g_gemv = capture(gemvs, stream)
+        per_step[sched] = dict(graph=g_step, gemv_graph=g_gemv, launches=nlaunch)
+    _, dequant, _ = make_step(wl, "stream")
+    g_dq = capture(dequant, stream)
+
+    n_gemv_bytes = sum(gemv_bytes(g.N, g.K) for mats in wl["layers"] for (g, _, _) in mats)
+    big = wl["big"][0]
+    n_dq_bytes = dequant_bytes(big.n)
+    step_bytes = n_gemv_bytes + n_dq_bytes
+
+    # timed region: exactly args.steps steps of the chosen schedule
+    torch.cuda.synchronize()
+    ms = time_graph(per_step[args.schedule]["graph"], args.steps, args.warmup, stream)
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    # the dominant kernel (grouped GEMV) and the dequant, each on its own
+    reps = max(10, args.steps)
+    gemv_ms = time_graph(per_step[args.schedule]["gemv_graph"], reps, 3, stream)
+    dq_ms = time_graph(g_dq, reps, 3, stream)
+    other = "layered" if args.schedule == "stream" else "stream"
+    other_ms = time_graph(per_step[other]["graph"], reps, 3, stream)
+    launches = per_step[args.schedule]["launches"]
+    gemv_gbs = n_gemv_bytes / (gemv_ms * 1e-3) / 1e9
+    dq_gbs = n_dq_bytes / (dq_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms:.3f} ms ({value:.0f} GB/s); GEMVs {gemv_ms:.3f} ms ({gemv_gbs:.0f} GB/s, "
+        f"{launches} launches); dequant {dq_ms * 1e3:.1f} us ({dq_gbs:.0f} GB/s); "
+        f"{other} schedule step {other_ms:.3f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_sweep_7b_32layers_224gemv_b1+dequant_8192x28672",
+            "gemv_weights": sum(g.N * g.K for mats in wl["layers"] for (g, _, _) in mats),
+            "batch": 1, "blocksize": 64, "s2_blocksize": 256,
+            "dequant_elems": big.n, "dequant_out": "bf16",
+            "schedule": args.schedule, "gemv_launches_per_step": launches,
+            "bytes_per_step": step_bytes,
+        },
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_stream_kernel<1,2> (nf4_gemv_grouped)",
+            "achieved": round(gemv_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": n_gemv_bytes // launches,
+            "avg_launch_us": round(gemv_ms * 1e3 / launches, 3),
+        },
+        "dequant": {"kernel": "dequant_vec_kernel<bf16,8>", "gbs": round(dq_gbs, 1),
+                    "us": round(dq_ms * 1e3, 2), "frac": round(dq_gbs / HBM_PEAK_GBS, 4)},
+        f"{other}_schedule": {"ms_per_step": round(other_ms, 4),
+                              "value": round(step_bytes / (other_ms * 1e-3) / 1e9, 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

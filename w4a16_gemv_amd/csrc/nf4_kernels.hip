@@ -214,88 +214,154 @@ constexpr int kPairCopies = 32;
 
 constexpr int kMaxDescs = 1024;  // matrices per grouped launch
 
-template <int R>
-struct RowGroup {
-  uint4 pk[R];
-  uint32_t q[R];
-  float a2[R];
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [p, p + bytes): loads beyond `bytes` return zeros and
+// stores beyond it are dropped, so masked lanes need no branch (a branch
+// around a load makes the compiler wait for every load in flight, including
+// the prefetch of the next row group).
+// A resource over a NULL pointer is always empty, so that a skipped matrix
+// (whose descriptor is zeroed) can never be read or written.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                           p ? static_cast<int>(bytes) : 0, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond every resource (< 2^31 bytes)
+
+// Buffer resources a team needs to load row groups of one matrix.
+struct LoadBufs {
+  __amdgpu_buffer_rsrc_t packed, absmax_q, absmax2;
 };
 
-// Loads the packed chunk and block-scale inputs of rows [rl, rl + len) of one
-// matrix (len <= R; missing rows read as zero codes).
-template <int R>
-__device__ __forceinline__ void load_row_group(RowGroup<R>& rg, const nf4_gemv_desc& d,
-                                               int64_t rl, int len, bool active, int K, int k0,
-                                               int log2bs, int log2s2) {
-  const uint4* __restrict__ packed16 = reinterpret_cast<const uint4*>(d.packed);
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    if (active && rr < len) {
-      const int64_t e = (rl + rr) * K + k0;
-      const int64_t blk = e >> log2bs;
-      rg.pk[rr] = packed16[e >> 5];
-      rg.q[rr] = d.absmax_q[blk];
-      rg.a2[rr] = f16_to_f32(d.absmax2[blk >> log2s2]);
-    } else {
-      rg.pk[rr] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);  // zeros
-      rg.q[rr] = 0;
-      rg.a2[rr] = 0.0f;
-    }
-  }
+// What a team needs to finish a row group of one matrix: where y goes, N and
+// the matrix's offset.
+struct OutBufs {
+  __amdgpu_buffer_rsrc_t y;
+  int N;
+  float offset;
+};
+
+__device__ __forceinline__ LoadBufs load_bufs(const nf4_gemv_desc& d, int K, int log2bs,
+                                              int log2s2) {
+  LoadBufs lb;
+  const uint64_t n = d.N > 0 ? static_cast<uint64_t>(d.N) * static_cast<uint64_t>(K) : 0;
+  const uint64_t nb = n ? ((n - 1) >> log2bs) + 1 : 0;
+  const uint64_t ng = nb ? ((nb - 1) >> log2s2) + 1 : 0;
+  lb.packed = rsrc(d.packed, static_cast<uint32_t>(n >> 1));
+  lb.absmax_q = rsrc(d.absmax_q, static_cast<uint32_t>(nb));
+  lb.absmax2 = rsrc(d.absmax2, static_cast<uint32_t>(ng * 2));
+  return lb;
 }
 
 template <int B>
-__device__ __forceinline__ void load_x(uint4 (&xr)[B][4], const uint16_t* __restrict__ x, int K,
-                                       int k0, bool active) {
+__device__ __forceinline__ OutBufs out_bufs(const nf4_gemv_desc& d) {
+  OutBufs ob;
+  ob.y = rsrc(d.y, static_cast<uint32_t>(B * d.N * 2));
+  ob.N = static_cast<int>(d.N);
+  ob.offset = d.offset;
+  return ob;
+}
+
+template <int B>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_buf(const nf4_gemv_desc& d, int K) {
+  return rsrc(d.x, static_cast<uint32_t>(B * K * 2));
+}
+
+// Loads of one row group for one lane: the 16-byte packed chunk, absmax_q
+// and absmax2 of rows [rl, rl + len) (rows past len read as zeros).
+template <int R>
+struct RowGroup {
+  u32x4 pk[R];
+  uint32_t q[R];
+  uint32_t a2[R];
+};
+
+// Per-lane parts of the buffer offsets (constant for the whole kernel): the
+// lane's byte offset inside a packed row and its activation byte offset, both
+// pushed out of range for lanes past K (their activations then read as zero,
+// so whatever codes they see contribute nothing).
+struct LaneOffsets {
+  uint32_t pk;
+  uint32_t x;
+  uint32_t k0;
+};
+constexpr uint32_t kFar = 0x40000000u;  // added to an in-range offset: still < 2^31, never wraps
+
+template <int R>
+__device__ __forceinline__ void load_row_group(RowGroup<R>& rg, const LoadBufs& mb, int rl,
+                                               int len, const LaneOffsets& lo, int K, int log2bs,
+                                               int log2s2) {
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    // row part of the offsets: wave-uniform, so it goes in the scalar offset
+    const uint32_t row = static_cast<uint32_t>(rl + rr);
+    const uint32_t srow = rr < len ? row * static_cast<uint32_t>(K >> 1) : kFar;
+    const uint32_t sfar = rr < len ? 0u : kFar;
+    const uint32_t blk = (row * static_cast<uint32_t>(K) + lo.k0) >> log2bs;
+    rg.pk[rr] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, lo.pk, srow, 0);
+    rg.q[rr] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
+    rg.a2[rr] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, (blk >> log2s2) * 2u, sfar, 0);
+  }
+}
+
+// The lane's 32 activations per batch row (raw bf16 pairs).
+template <int B>
+__device__ __forceinline__ void load_x(u32x4 (&xr)[B][4], __amdgpu_buffer_rsrc_t xb,
+                                       const LaneOffsets& lo, int K) {
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      xr[b][j] = active ? *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(b) * K + k0 + 8 * j)
-                        : make_uint4(0u, 0u, 0u, 0u);
+      xr[b][j] = __builtin_amdgcn_raw_buffer_load_b128(xb, lo.x + 16u * j,
+                                                        static_cast<uint32_t>(b * K * 2), 0);
 }
 
-template <int B>
-__device__ __forceinline__ void widen_x(float (&xv)[B][32], const uint4 (&xr)[B][4]) {
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// part[rr][b] += sum over the 8 weights of dword j of row rr's chunk (columns
+// 8 j .. 8 j + 7 of the lane) of weight * x.  Each table entry holds the two
+// NF4 values of one packed byte as bf16 pairs hi = bf16(v) and lo = bf16(v -
+// hi) (hi + lo is within 2^-16 |v| of v); an activation dword is already the
+// matching bf16 pair (even column low), so two v_dot2c_f32_bf16 per byte do
+// the four products with fp32 accumulation and no conversion.
+template <int B, int R>
+__device__ __forceinline__ void dot_columns(const RowGroup<R>& rg, const u32x4 (&xr)[B][4], int j,
+                                            uint32_t copy_off, const uint2* s_pairs,
+                                            float (&part)[R][B]) {
 #pragma unroll
-  for (int b = 0; b < B; ++b)
+  for (int rr = 0; rr < R; ++rr) {
+    const uint32_t d = rg.pk[rr][j];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w4[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
+    for (int i = 0; i < 4; ++i) {
+      // address bits 15..8 = byte i of d, bits 7..0 = copy offset (selector
+      // 0x0C = zero byte, 4 = byte 0 of the first operand, i = byte i of d)
+      const uint32_t addr = __builtin_amdgcn_perm(copy_off, d, 0x0C0C0004u | (uint32_t(i) << 8));
+      const uint2 t = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_pairs) + addr);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xv[b][8 * j + 2 * i] = __builtin_bit_cast(float, w4[i] << 16);
-        xv[b][8 * j + 2 * i + 1] = __builtin_bit_cast(float, w4[i] & 0xFFFF0000u);
+      for (int b = 0; b < B; ++b) {
+        // copy the element out first: __builtin_bit_cast applied directly to a
+        // vector-element lvalue reads element 0 whatever the index
+        const uint32_t xw = xr[b][j][i];
+        const bf16x2 xp = __builtin_bit_cast(bf16x2, xw);
+        part[rr][b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, t.x), xp,
+                                                      part[rr][b], false);
+        part[rr][b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, t.y), xp,
+                                                      part[rr][b], false);
       }
-    }
-}
-
-// part[b] += sum over the 8 weights of dword d (columns 8 j .. 8 j + 7 of the
-// lane's chunk) of weight * x.
-template <int B>
-__device__ __forceinline__ void dot_dword_pairs(uint32_t d, uint32_t copy_off,
-                                                const float (&xv)[B][32], int j,
-                                                const float2* s_pairs, float (&part)[B]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // address bits 15..8 = byte i of d, bits 7..0 = copy offset (selector
-    // 0x0C = zero byte, 4 = byte 0 of the first operand, i = byte i of d)
-    const uint32_t addr = __builtin_amdgcn_perm(copy_off, d, 0x0C0C0004u | (uint32_t(i) << 8));
-    const float2 t = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(s_pairs) + addr);
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      part[b] = __builtin_fmaf(t.x, xv[b][8 * j + 2 * i], part[b]);
-      part[b] = __builtin_fmaf(t.y, xv[b][8 * j + 2 * i + 1], part[b]);
     }
   }
 }
 
 // A descriptor the streaming kernel can read: 16-byte aligned packed weights
-// and activations, and a row count that matches the row offsets.  Matrices
-// that fail this are skipped (their y is not written).
-__device__ __forceinline__ bool desc_usable(const nf4_gemv_desc& d, int rows) {
+// and activations, non-NULL arrays, a row count that matches the row offsets
+// and N * K < 2^31.  Matrices that fail this are skipped (y is not written).
+__device__ __forceinline__ bool desc_usable(const nf4_gemv_desc& d, int rows, int K) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(d.packed) | reinterpret_cast<uintptr_t>(d.x);
-  return (a & 15) == 0 && d.N == rows && d.packed && d.absmax_q && d.absmax2 && d.x && d.y;
+  // every offset the kernel forms must stay below 2^30 (see kFar)
+  const bool small = d.N >= 0 && static_cast<uint64_t>(d.N) * static_cast<uint64_t>(K) <
+                                     (uint64_t(1) << 31);
+  return (a & 15) == 0 && d.N == rows && small && d.packed && d.absmax_q && d.absmax2 && d.x &&
+         d.y;
 }
 
 // Field-wise copy of descriptor m (or of the by-value descriptor when the
@@ -327,28 +393,53 @@ __device__ __forceinline__ nf4_gemv_desc fetch_desc(const nf4_gemv_desc* __restr
   return d;
 }
 
+// Descriptor m for the kernel: a matrix it cannot use (see desc_usable) is
+// replaced by an empty one, whose loads read zeros and whose stores are
+// dropped.
+__device__ __forceinline__ nf4_gemv_desc open_desc(const nf4_gemv_desc* __restrict__ descs,
+                                                   const nf4_gemv_desc& single, int m, int len,
+                                                   const int* s_rowbeg, int K) {
+  nf4_gemv_desc d = fetch_desc(descs, single, m);
+  if (len <= 0 || m < 0 || !desc_usable(d, s_rowbeg[m + 1] - s_rowbeg[m], K)) {
+    d.packed = nullptr;
+    d.absmax_q = nullptr;
+    d.absmax2 = nullptr;
+    d.x = nullptr;
+    d.y = nullptr;
+    d.N = 0;
+    d.offset = 0.0f;
+  }
+  return d;
+}
+
 // Where a team is in the concatenated row space: matrix m, global row r.
 struct RowCursor {
-  int m;
-  int r;
+  int m;      // current matrix
+  int r;      // next global row
+  int beg;    // first global row of matrix m
+  int end;    // one past its last row
 };
 
 // The next group of at most R rows from cursor c, not crossing a matrix end or
 // the team's range end; advances c.  Returns the group's length (0 when the
-// range is exhausted).
+// range is exhausted).  The row offsets in LDS are read only when the cursor
+// moves to another matrix.
 template <int R>
 __device__ __forceinline__ int next_group(RowCursor& c, int r_end, const int* s_rowbeg, int count,
                                           int* m_out, int* rl_out) {
-  while (c.m < count && s_rowbeg[c.m + 1] <= c.r) ++c.m;  // skip finished / empty matrices
-  if (c.r >= r_end || c.m >= count) {
+  if (c.r >= c.end && c.r < r_end) {  // skip finished / empty matrices
+    while (c.m < count && s_rowbeg[c.m + 1] <= c.r) ++c.m;
+    c.beg = c.m < count ? s_rowbeg[c.m] : c.r;
+    c.end = c.m < count ? s_rowbeg[c.m + 1] : c.r;
+  }
+  if (c.r >= r_end || c.r >= c.end) {
     *m_out = -1;
     *rl_out = 0;
     return 0;
   }
-  const int lim = min(r_end, s_rowbeg[c.m + 1]);
-  const int len = min(R, lim - c.r);
+  const int len = min(R, min(r_end, c.end) - c.r);
   *m_out = c.m;
-  *rl_out = c.r - s_rowbeg[c.m];
+  *rl_out = c.r - c.beg;
   c.r += len;
   return len;
 }
@@ -358,14 +449,15 @@ __device__ __forceinline__ int next_group(RowCursor& c, int r_end, const int* s_
 // the block sizes, code2 and the batch (a single nf4_gemv is a list of one).
 // The concatenated rows of all matrices are split evenly into contiguous
 // ranges, one per team; a team walks its range in groups of up to R rows
-// (never crossing a matrix), prefetching the next group while computing the
-// current one, and reloads its activations when the matrix changes.
+// (never crossing a matrix), issuing the loads of the next group before it
+// computes the current one.  All loads and the y stores are branch-free
+// buffer operations.
 // ---------------------------------------------------------------------------
 template <int B, int R>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_stream_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
     int K, int log2bs, int log2s2, int nw, const uint16_t* __restrict__ code2) {
-  __shared__ float2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
+  __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
   __shared__ float s_nf4[16];
   __shared__ float s_code2[256];
   __shared__ float s_red[2][8][R * B];
@@ -373,7 +465,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __shared__ int s_iters;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform by construction; saying so keeps all per-team bookkeeping
+  // in scalar registers and scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int teams = (blockDim.x >> 6) / nw;
   const int team = wave / nw;           // == teams for helper waves
   const int slab = wave - team * nw;
@@ -395,7 +489,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (tid < 16) s_nf4[tid] = kNF4[tid];
   __syncthreads();
 
-  // the team's row range and its first group
+  // the team's row range
   const int64_t tt = static_cast<int64_t>(gridDim.x) * teams;
   const int64_t tg = static_cast<int64_t>(blockIdx.x) * teams + team;
   const int r_begin = in_team ? static_cast<int>(tg * total_rows / tt) : 0;
@@ -409,6 +503,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     cur_c.m = lo;
     cur_c.r = r_begin;
+    cur_c.beg = s_rowbeg[lo];
+    cur_c.end = s_rowbeg[lo + 1];
   }
   // number of groups of this team (per matrix it overlaps), then the
   // workgroup maximum: every wave runs that many iterations
@@ -422,71 +518,122 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (lane == 0 && slab == 0 && in_team) atomicMax(&s_iters, ng);
   }
 
-  int m, rl;
-  int len = next_group<R>(cur_c, r_end, s_rowbeg, count, &m, &rl);
-  m = __builtin_amdgcn_readfirstlane(m);
-  nf4_gemv_desc d = fetch_desc(descs, single, m);
-  if (len > 0 && !desc_usable(d, s_rowbeg[m + 1] - s_rowbeg[m])) len = 0;
-  uint4 xr[B][4];
-  load_x<B>(xr, d.x, K, k0, active && len > 0);
-  RowGroup<R> cur;
-  load_row_group<R>(cur, d, rl, len, active, K, k0, log2bs, log2s2);
+  // the first two groups (prefetch depth 2: the loads of group i + 2 are
+  // issued before group i is computed).  Scalar state: the load-side buffers
+  // of the newest group's matrix (mL), and the output side of the two groups
+  // in compute order; descriptors are re-read only when the matrix changes.
+  int m0, rl0, m1, rl1;
+  int len0 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m0, &rl0);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  const nf4_gemv_desc d0 = open_desc(descs, single, m0, len0, s_rowbeg, K);
+  int len1 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m1, &rl1);
+  m1 = __builtin_amdgcn_readfirstlane(m1);
+  LoadBufs lb0 = load_bufs(d0, K, log2bs, log2s2);
+  OutBufs ob0 = out_bufs<B>(d0);
+  LaneOffsets lo;
+  lo.pk = active ? static_cast<uint32_t>(k0 >> 1) : kFar;
+  lo.x = active ? static_cast<uint32_t>(k0 * 2) : kFar;
+  lo.k0 = static_cast<uint32_t>(k0);
+  RowGroup<R> g0, g1;
+  load_row_group<R>(g0, lb0, rl0, len0, lo, K, log2bs, log2s2);
+  u32x4 xr[B][4];
+  load_x<B>(xr, x_buf<B>(d0, K), lo, K);
+  int mL = m0;            // matrix of lbL
+  LoadBufs lbL = lb0;
+  OutBufs ob1 = ob0;
+  if (len1 > 0 && m1 != m0) {
+    const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, s_rowbeg, K);
+    lbL = load_bufs(d1, K, log2bs, log2s2);
+    ob1 = out_bufs<B>(d1);
+    mL = m1;
+  }
+  load_row_group<R>(g1, lbL, rl1, len1, lo, K, log2bs, log2s2);
 
-  // the 256 x 32 pair table
+  // the 256 x 32 pair table: (bf16 hi pair, bf16 lo pair) of each byte
   for (int e = tid; e < 256 * kPairCopies; e += blockDim.x) {
     const int b = e / kPairCopies;
-    s_pairs[e] = make_float2(s_nf4[b >> 4], s_nf4[b & 15]);
+    const float ve = s_nf4[b >> 4], vo = s_nf4[b & 15];
+    const uint32_t hi = pack_pair<NF4_BF16>(ve, vo);
+    const float he = __builtin_bit_cast(float, hi << 16);
+    const float ho = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+    const uint32_t lo2 = pack_pair<NF4_BF16>(ve - he, vo - ho);  // exact differences
+    s_pairs[e] = make_uint2(hi, lo2);
   }
-  float xv[B][32];
-  widen_x<B>(xv, xr);
   const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
   __syncthreads();
   const int iters = s_iters;
 
   int buf = 0;
   for (int it = 0; it < iters; ++it) {
-    // prefetch the next group (and its activations if the matrix changes)
+    // issue the loads of the group after next
     int m2, rl2;
     const int len2 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m2, &rl2);
     m2 = __builtin_amdgcn_readfirstlane(m2);
-    const nf4_gemv_desc d2 = (len2 > 0 && m2 != m) ? fetch_desc(descs, single, m2) : d;
-    const bool usable = len2 > 0 && desc_usable(d2, s_rowbeg[m2 + 1] - s_rowbeg[m2]);
-    const bool new_x = usable && m2 != m;
-    if (new_x) load_x<B>(xr, d2.x, K, k0, active);
-    RowGroup<R> nxt;
-    load_row_group<R>(nxt, d2, rl2, usable ? len2 : 0, active, K, k0, log2bs, log2s2);
+    OutBufs ob2 = ob1;
+    if (len2 > 0 && m2 != mL) {
+      const nf4_gemv_desc d2 = open_desc(descs, single, m2, len2, s_rowbeg, K);
+      lbL = load_bufs(d2, K, log2bs, log2s2);
+      ob2 = out_bufs<B>(d2);
+      mL = m2;
+    }
+    RowGroup<R> g2;
+    load_row_group<R>(g2, lbL, rl2, len2, lo, K, log2bs, log2s2);
+    // issue these loads here: sunk below the first wait for the current group
+    // they would turn that wait into a wait for the group after it as well
+    __builtin_amdgcn_sched_barrier(0);
 
+    // compute the current group
+    float c2[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) c2[rr] = s_code2[g0.q[rr]];
+    float part[R][B];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int b = 0; b < B; ++b) part[rr][b] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dot_columns<B, R>(g0, xr, j, copy_off, s_pairs, part);
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      float part[B];
-#pragma unroll
-      for (int b = 0; b < B; ++b) part[b] = 0.0f;
-      dot_dword_pairs<B>(cur.pk[rr].x, copy_off, xv, 0, s_pairs, part);
-      dot_dword_pairs<B>(cur.pk[rr].y, copy_off, xv, 1, s_pairs, part);
-      dot_dword_pairs<B>(cur.pk[rr].z, copy_off, xv, 2, s_pairs, part);
-      dot_dword_pairs<B>(cur.pk[rr].w, copy_off, xv, 3, s_pairs, part);
-      const float prod = s_code2[cur.q[rr]] * cur.a2[rr];
-      const float a = prod + d.offset;
+      const float prod = c2[rr] * f16_to_f32(static_cast<uint16_t>(g0.a2[rr]));
+      const float a = prod + ob0.offset;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float tot = wave_sum_to_lane63(a * part[b]);
+        const float tot = wave_sum_to_lane63(a * part[rr][b]);
         if (lane == 63) s_red[buf][wave][rr * B + b] = tot;
       }
     }
     __syncthreads();
-    if (in_team && slab == 0 && lane < R * B) {
-      const int rr = lane / B, b = lane % B;
-      float acc = s_red[buf][wave][lane];
-      for (int w = 1; w < nw; ++w) acc += s_red[buf][wave + w][lane];
-      if (rr < len) d.y[static_cast<int64_t>(b) * d.N + rl + rr] = to_half_bits<NF4_BF16>(acc);
+    {
+      const int idx = lane < R * B ? lane : 0;
+      const int rr = idx / B, b = idx % B;
+      float acc = s_red[buf][wave][idx];
+      for (int w = 1; w < nw; ++w) acc += s_red[buf][min(wave + w, 7)][idx];
+      const bool store = in_team && slab == 0 && lane < R * B && rr < len0;
+      const uint32_t off = static_cast<uint32_t>((b * ob0.N + rl0 + rr) * 2);
+      __builtin_amdgcn_raw_buffer_store_b16(to_half_bits<NF4_BF16>(acc), ob0.y,
+                                            store ? off : kOutOfRange, 0, 0);
     }
     buf ^= 1;
-    if (new_x) widen_x<B>(xv, xr);
-    cur = nxt;
-    d = d2;
-    m = len2 > 0 ? m2 : m;
-    rl = rl2;
-    len = usable ? len2 : 0;
+    // the next group starts a new matrix: fetch its activations now that the
+    // current ones are no longer needed
+    if (len1 > 0 && m1 != m0) {
+      load_x<B>(xr, x_buf<B>(open_desc(descs, single, m1, len1, s_rowbeg, K), K), lo, K);
+      // drain here (rare: once per matrix change) so that the loads of this
+      // branch are not assumed outstanding on the common path, where they
+      // would make every wait for the current group also wait for the next
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    g0 = g1;
+    g1 = g2;
+    ob0 = ob1;
+    ob1 = ob2;
+    m0 = len1 > 0 ? m1 : m0;
+    m1 = len2 > 0 ? m2 : m1;
+    rl0 = rl1;
+    rl1 = rl2;
+    len0 = len1;
+    len1 = len2;
   }
 }
 
@@ -713,7 +860,10 @@ nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const 
   return launch_status();
 }
 
-constexpr int kStreamR = 4;
+// rows per group: 2 at batch 1 (127 VGPRs with prefetch depth 2, four waves
+// per SIMD), 1 at batch 2
+template <int B>
+constexpr int stream_rows() { return B == 1 ? 2 : 1; }
 
 template <int B>
 nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
@@ -726,7 +876,7 @@ nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   const int64_t max_wg = static_cast<int64_t>(device_cus()) * 2;
   const int64_t want = (static_cast<int64_t>(total_rows) + teams - 1) / teams;
   const int64_t grid = want < max_wg ? (want > 0 ? want : 1) : max_wg;
-  hipLaunchKernelGGL((gemv_stream_kernel<B, kStreamR>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>()>), dim3(static_cast<uint32_t>(grid)),
                      dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, nw, code2);
   return launch_status();
 }
@@ -738,7 +888,7 @@ nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const u
   const bool vec = lbs >= 5 && K % 32 == 0 && K <= 8 * kSlab && N <= 0x7FFFFFFF &&
                    aligned(packed, 16) && aligned(x, 16);
   if constexpr (B <= 2) {
-    if (vec && N < 0x7FFFFFFF) {
+    if (vec && N * K < (int64_t(1) << 31)) {  // the streaming kernel's offset range
       nf4_gemv_desc one{};
       one.packed = packed;
       one.absmax_q = absmax_q;

@@ -173,6 +173,29 @@ __device__ __forceinline__ float dpp_add(float v) {
   return v + __builtin_bit_cast(float, moved);
 }
 
+// Sums of two per-lane values p and q over the 64 lanes at once: afterwards
+// lanes 0-15 hold sum(p) and lanes 32-47 hold sum(q).  v_permlane32_swap
+// pairs lane l with lane l + 32 (p in the low half, q in the high half),
+// v_permlane16_swap against zero then folds rows 1 and 3 into rows 0 and 2,
+// and four in-row DPP steps finish each row: 8 instructions for both sums,
+// and no row broadcasts.
+__device__ __forceinline__ float wave_sum_pair(float p, float q) {
+  // (vector elements are copied to scalars before any bit_cast: a bit_cast
+  // of a vector-element lvalue reads element 0 whatever the index)
+  const auto h = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, p),
+                                                  __builtin_bit_cast(uint32_t, q), false, false);
+  const uint32_t h0 = h[0], h1 = h[1];
+  const float s = __builtin_bit_cast(float, h0) + __builtin_bit_cast(float, h1);
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, s), 0u, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  float t = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+  t = dpp_add<0xB1, 0xF>(t);   // quad_perm [1,0,3,2]
+  t = dpp_add<0x4E, 0xF>(t);   // quad_perm [2,3,0,1]
+  t = dpp_add<0x141, 0xF>(t);  // row_half_mirror
+  t = dpp_add<0x140, 0xF>(t);  // row_mirror
+  return t;
+}
+
 __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
   v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
@@ -393,6 +416,14 @@ __device__ __forceinline__ nf4_gemv_desc fetch_desc(const nf4_gemv_desc* __restr
   return d;
 }
 
+// An LDS read at a wave-uniform index: the value is uniform too.  Saying so
+// keeps the cursor in scalar registers; otherwise the row offsets derived from
+// it are assumed divergent and every buffer load whose scalar offset uses them
+// is wrapped in a loop over distinct values.
+__device__ __forceinline__ int uniform_lds(const int* p, int i) {
+  return __builtin_amdgcn_readfirstlane(p[i]);
+}
+
 // Descriptor m for the kernel: a matrix it cannot use (see desc_usable) is
 // replaced by an empty one, whose loads read zeros and whose stores are
 // dropped.
@@ -400,7 +431,8 @@ __device__ __forceinline__ nf4_gemv_desc open_desc(const nf4_gemv_desc* __restri
                                                    const nf4_gemv_desc& single, int m, int len,
                                                    const int* s_rowbeg, int K) {
   nf4_gemv_desc d = fetch_desc(descs, single, m);
-  if (len <= 0 || m < 0 || !desc_usable(d, s_rowbeg[m + 1] - s_rowbeg[m], K)) {
+  if (len <= 0 || m < 0 ||
+      !desc_usable(d, uniform_lds(s_rowbeg, m + 1) - uniform_lds(s_rowbeg, m), K)) {
     d.packed = nullptr;
     d.absmax_q = nullptr;
     d.absmax2 = nullptr;
@@ -428,9 +460,9 @@ template <int R>
 __device__ __forceinline__ int next_group(RowCursor& c, int r_end, const int* s_rowbeg, int count,
                                           int* m_out, int* rl_out) {
   if (c.r >= c.end && c.r < r_end) {  // skip finished / empty matrices
-    while (c.m < count && s_rowbeg[c.m + 1] <= c.r) ++c.m;
-    c.beg = c.m < count ? s_rowbeg[c.m] : c.r;
-    c.end = c.m < count ? s_rowbeg[c.m + 1] : c.r;
+    while (c.m < count && uniform_lds(s_rowbeg, c.m + 1) <= c.r) ++c.m;
+    c.beg = c.m < count ? uniform_lds(s_rowbeg, c.m) : c.r;
+    c.end = c.m < count ? uniform_lds(s_rowbeg, c.m + 1) : c.r;
   }
   if (c.r >= r_end || c.r >= c.end) {
     *m_out = -1;
@@ -453,10 +485,11 @@ __device__ __forceinline__ int next_group(RowCursor& c, int r_end, const int* s_
 // computes the current one.  All loads and the y stores are branch-free
 // buffer operations.
 // ---------------------------------------------------------------------------
-template <int B, int R>
+template <int B, int R, int NW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_stream_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
-    int K, int log2bs, int log2s2, int nw, const uint16_t* __restrict__ code2) {
+    int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2) {
+  constexpr int nw = NW;  // waves per team: one per 2048-column slab of K
   __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
   __shared__ float s_nf4[16];
   __shared__ float s_code2[256];
@@ -468,7 +501,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // wave-uniform by construction; saying so keeps all per-team bookkeeping
   // in scalar registers and scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int teams = (blockDim.x >> 6) / nw;
+  constexpr int teams = 8 / NW;         // the workgroup has 8 waves
   const int team = wave / nw;           // == teams for helper waves
   const int slab = wave - team * nw;
   const bool in_team = team < teams;
@@ -499,20 +532,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     int lo = 0, hi = count - 1;  // last matrix whose first row is <= r_begin
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_rowbeg[mid] <= r_begin) lo = mid; else hi = mid - 1;
+      if (uniform_lds(s_rowbeg, mid) <= r_begin) lo = mid; else hi = mid - 1;
     }
     cur_c.m = lo;
     cur_c.r = r_begin;
-    cur_c.beg = s_rowbeg[lo];
-    cur_c.end = s_rowbeg[lo + 1];
+    cur_c.beg = uniform_lds(s_rowbeg, lo);
+    cur_c.end = uniform_lds(s_rowbeg, lo + 1);
   }
   // number of groups of this team (per matrix it overlaps), then the
   // workgroup maximum: every wave runs that many iterations
   {
     int ng = 0;
-    for (int mm = cur_c.m; mm < count && s_rowbeg[mm] < r_end; ++mm) {
-      const int lo = max(r_begin, s_rowbeg[mm]);
-      const int hi = min(r_end, s_rowbeg[mm + 1]);
+    for (int mm = cur_c.m; mm < count && uniform_lds(s_rowbeg, mm) < r_end; ++mm) {
+      const int lo = max(r_begin, uniform_lds(s_rowbeg, mm));
+      const int hi = min(r_end, uniform_lds(s_rowbeg, mm + 1));
       if (hi > lo) ng += (hi - lo + R - 1) / R;
     }
     if (lane == 0 && slab == 0 && in_team) atomicMax(&s_iters, ng);
@@ -561,7 +594,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
   const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
   __syncthreads();
-  const int iters = s_iters;
+  const int iters = __builtin_amdgcn_readfirstlane(s_iters);
 
   int buf = 0;
   for (int it = 0; it < iters; ++it) {
@@ -593,14 +626,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       for (int b = 0; b < B; ++b) part[rr][b] = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) dot_columns<B, R>(g0, xr, j, copy_off, s_pairs, part);
+    float val[R * B];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       const float prod = c2[rr] * f16_to_f32(static_cast<uint16_t>(g0.a2[rr]));
       const float a = prod + ob0.offset;
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const float tot = wave_sum_to_lane63(a * part[rr][b]);
-        if (lane == 63) s_red[buf][wave][rr * B + b] = tot;
+      for (int b = 0; b < B; ++b) val[rr * B + b] = a * part[rr][b];
+    }
+    if constexpr (R * B == 2) {
+      const float tot = wave_sum_pair(val[0], val[1]);
+      if ((lane & 31) == 0) s_red[buf][wave][lane >> 5] = tot;
+    } else {
+#pragma unroll
+      for (int v = 0; v < R * B; ++v) {
+        const float tot = wave_sum_to_lane63(val[v]);
+        if (lane == 63) s_red[buf][wave][v] = tot;
       }
     }
     __syncthreads();
@@ -608,7 +649,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       const int idx = lane < R * B ? lane : 0;
       const int rr = idx / B, b = idx % B;
       float acc = s_red[buf][wave][idx];
-      for (int w = 1; w < nw; ++w) acc += s_red[buf][min(wave + w, 7)][idx];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) acc += s_red[buf][min(wave + w, 7)][idx];
       const bool store = in_team && slab == 0 && lane < R * B && rr < len0;
       const uint32_t off = static_cast<uint32_t>((b * ob0.N + rl0 + rr) * 2);
       __builtin_amdgcn_raw_buffer_store_b16(to_half_bits<NF4_BF16>(acc), ob0.y,
@@ -865,6 +907,14 @@ nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const 
 template <int B>
 constexpr int stream_rows() { return B == 1 ? 2 : 1; }
 
+template <int B, int NW>
+void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
+                      int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
+                      int64_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>(), NW>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2);
+}
+
 template <int B>
 nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
@@ -876,8 +926,17 @@ nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   const int64_t max_wg = static_cast<int64_t>(device_cus()) * 2;
   const int64_t want = (static_cast<int64_t>(total_rows) + teams - 1) / teams;
   const int64_t grid = want < max_wg ? (want > 0 ? want : 1) : max_wg;
-  hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>()>), dim3(static_cast<uint32_t>(grid)),
-                     dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, nw, code2);
+  switch (nw) {
+    case 1: stream_launch_nw<B, 1>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 2: stream_launch_nw<B, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 3: stream_launch_nw<B, 3>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 4: stream_launch_nw<B, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 5: stream_launch_nw<B, 5>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 6: stream_launch_nw<B, 6>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 7: stream_launch_nw<B, 7>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 8: stream_launch_nw<B, 8>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    default: return NF4_EUNSUPPORTED;
+  }
   return launch_status();
 }
 

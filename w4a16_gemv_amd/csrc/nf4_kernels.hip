@@ -196,6 +196,31 @@ __device__ __forceinline__ float wave_sum_pair(float p, float q) {
   return t;
 }
 
+// Sums of four per-lane values a, b, c, d over the 64 lanes at once:
+// afterwards every lane of row 0 (lanes 0-15) holds sum(a), row 1 sum(c),
+// row 2 sum(b) and row 3 sum(d).  Two v_permlane32_swap fold the wave halves
+// (a and c into lanes 0-31, b and d into lanes 32-63), one v_permlane16_swap
+// folds rows 1 and 3 into rows 0 and 2 while moving c and d to rows 1 and 3,
+// and four in-row DPP steps finish: 10 instructions for the four sums.
+__device__ __forceinline__ float wave_sum_quad(float a, float b, float c, float d) {
+  const auto hab = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                    __builtin_bit_cast(uint32_t, b), false, false);
+  const auto hcd = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, c),
+                                                    __builtin_bit_cast(uint32_t, d), false, false);
+  const uint32_t ab0 = hab[0], ab1 = hab[1], cd0 = hcd[0], cd1 = hcd[1];
+  const float sab = __builtin_bit_cast(float, ab0) + __builtin_bit_cast(float, ab1);
+  const float scd = __builtin_bit_cast(float, cd0) + __builtin_bit_cast(float, cd1);
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, sab),
+                                                  __builtin_bit_cast(uint32_t, scd), false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  float t = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+  t = dpp_add<0xB1, 0xF>(t);   // quad_perm [1,0,3,2]
+  t = dpp_add<0x4E, 0xF>(t);   // quad_perm [2,3,0,1]
+  t = dpp_add<0x141, 0xF>(t);  // row_half_mirror
+  t = dpp_add<0x140, 0xF>(t);  // row_mirror
+  return t;
+}
+
 __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
   v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
@@ -295,8 +320,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t x_buf(const nf4_gemv_desc& d, 
 template <int R>
 struct RowGroup {
   u32x4 pk[R];
-  uint32_t q[R];
-  uint32_t a2[R];
+  // at the loaded width: widened where they are used, so that the widening
+  // is not hoisted to the loop latch, where it would wait for the loads
+  uint8_t q[R];
+  uint16_t a2[R];
 };
 
 // Per-lane parts of the buffer offsets (constant for the whole kernel): the
@@ -596,9 +623,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __syncthreads();
   const int iters = __builtin_amdgcn_readfirstlane(s_iters);
 
+  // One iteration: issue the loads of the group after next into `fut` (the
+  // buffer the previous iteration computed from), then compute `cur`.  The
+  // loop is unrolled by three so that the three buffers change roles without
+  // register copies: a copy out of a buffer whose loads are in flight would
+  // wait for them, and the prefetch would be lost.
   int buf = 0;
-  for (int it = 0; it < iters; ++it) {
-    // issue the loads of the group after next
+  auto step = [&](RowGroup<R>& cur, RowGroup<R>& fut) {
     int m2, rl2;
     const int len2 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m2, &rl2);
     m2 = __builtin_amdgcn_readfirstlane(m2);
@@ -609,27 +640,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       ob2 = out_bufs<B>(d2);
       mL = m2;
     }
-    RowGroup<R> g2;
-    load_row_group<R>(g2, lbL, rl2, len2, lo, K, log2bs, log2s2);
+    load_row_group<R>(fut, lbL, rl2, len2, lo, K, log2bs, log2s2);
     // issue these loads here: sunk below the first wait for the current group
     // they would turn that wait into a wait for the group after it as well
     __builtin_amdgcn_sched_barrier(0);
 
-    // compute the current group
     float c2[R];
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) c2[rr] = s_code2[g0.q[rr]];
+    for (int rr = 0; rr < R; ++rr) c2[rr] = s_code2[cur.q[rr]];
     float part[R][B];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr)
 #pragma unroll
       for (int b = 0; b < B; ++b) part[rr][b] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dot_columns<B, R>(g0, xr, j, copy_off, s_pairs, part);
+    for (int j = 0; j < 4; ++j) dot_columns<B, R>(cur, xr, j, copy_off, s_pairs, part);
     float val[R * B];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      const float prod = c2[rr] * f16_to_f32(static_cast<uint16_t>(g0.a2[rr]));
+      const float prod = c2[rr] * f16_to_f32(cur.a2[rr]);
       const float a = prod + ob0.offset;
 #pragma unroll
       for (int b = 0; b < B; ++b) val[rr * B + b] = a * part[rr][b];
@@ -637,6 +666,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if constexpr (R * B == 2) {
       const float tot = wave_sum_pair(val[0], val[1]);
       if ((lane & 31) == 0) s_red[buf][wave][lane >> 5] = tot;
+    } else if constexpr (R * B == 4) {
+      const float tot = wave_sum_quad(val[0], val[1], val[2], val[3]);
+      // row 0 holds value 0, row 1 value 2, row 2 value 1, row 3 value 3
+      const int row16 = lane >> 4;
+      if ((lane & 15) == 0) s_red[buf][wave][((row16 & 1) << 1) | (row16 >> 1)] = tot;
     } else {
 #pragma unroll
       for (int v = 0; v < R * B; ++v) {
@@ -666,8 +700,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       // would make every wait for the current group also wait for the next
       __builtin_amdgcn_s_waitcnt(0);
     }
-    g0 = g1;
-    g1 = g2;
     ob0 = ob1;
     ob1 = ob2;
     m0 = len1 > 0 ? m1 : m0;
@@ -676,7 +708,295 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     rl1 = rl2;
     len0 = len1;
     len1 = len2;
+  };
+  // Whole rounds of three steps in the loop, the remaining steps after it: an
+  // exit from the middle of a round would give the compiler a path from that
+  // step back to the loop header, and loads still counted on it would make
+  // the first step wait for the loads it has just issued.
+  RowGroup<R> g2;
+  const int rounds = iters / 3;
+  for (int it = 0; it < rounds; ++it) {
+    step(g0, g2);
+    step(g1, g0);
+    step(g2, g1);
   }
+  const int rest = iters - 3 * rounds;
+  if (rest > 0) step(g0, g2);
+  if (rest > 1) step(g1, g0);
+}
+
+// ---------------------------------------------------------------------------
+// The wave-per-row streaming GEMV (K a multiple of 64, blocksize >= 64).
+//
+// Every wave works alone: lane l owns the 64 columns [64 l + 4096 p, +64) of
+// pass p < P (P = ceil(K / 4096)), which is exactly one 64-aligned piece of a
+// first-level block, so the lane loads 32 contiguous packed bytes and one
+// absmax_q / absmax2 pair per row and pass, and applies one absmax_real to the
+// sum of its 64 products.  A wave reduces its own rows (no cross-wave sums, no
+// barriers), so the waves of a workgroup share only the decode table and
+// code2.  The concatenated rows of all matrices are split evenly into
+// contiguous ranges, one per wave; a wave walks its range in groups of up to R
+// rows with the loads of the group after next issued before the current group
+// is computed (three register buffers, loop unrolled by three).
+// ---------------------------------------------------------------------------
+constexpr int kWaveCols = 4096;  // columns per pass of a wave (64 lanes x 64)
+
+template <int R, int P>
+struct WaveGroup {
+  u32x4 pk[R][P][2];
+  uint8_t q[R][P];
+  uint16_t a2[R][P];
+};
+
+// Per-lane offsets of pass p: packed byte offset inside a row and activation
+// byte offset (pushed out of range when the lane's columns are past K), and
+// the lane's first column.
+template <int P>
+struct WaveLane {
+  uint32_t pk[P];
+  uint32_t x[P];
+  uint32_t c0[P];
+};
+
+template <int R, int P>
+__device__ __forceinline__ void load_wave_group(WaveGroup<R, P>& g, const LoadBufs& mb, int rl,
+                                                int len, const WaveLane<P>& wl, int K, int log2bs,
+                                                int log2s2) {
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const uint32_t row = static_cast<uint32_t>(rl + rr);
+    const uint32_t srow = rr < len ? row * static_cast<uint32_t>(K >> 1) : kFar;
+    const uint32_t sfar = rr < len ? 0u : kFar;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint32_t blk = (row * static_cast<uint32_t>(K) + wl.c0[p]) >> log2bs;
+      g.pk[rr][p][0] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p], srow, 0);
+      g.pk[rr][p][1] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p] + 16u, srow, 0);
+      g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
+      g.a2[rr][p] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, (blk >> log2s2) * 2u, sfar, 0);
+    }
+  }
+}
+
+// The lane's 64 activations per pass and batch row (raw bf16 pairs).
+template <int B, int P>
+__device__ __forceinline__ void load_wave_x(u32x4 (&xr)[B][P][8], __amdgpu_buffer_rsrc_t xb,
+                                            const WaveLane<P>& wl, int K) {
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        xr[b][p][j] = __builtin_amdgcn_raw_buffer_load_b128(xb, wl.x[p] + 16u * j,
+                                                             static_cast<uint32_t>(b * K * 2), 0);
+}
+
+// val[rr * B + b] = sum over the lane's columns of row rr of weight * x.  The
+// lane's R P 8 packed dwords are walked in order with the four table reads of
+// the next dword issued before the eight v_dot2c_f32_bf16 of the current one
+// (same decode table as the team kernel); the scheduling barriers keep the
+// compiler from hoisting more reads, whose results would not fit in
+// registers.  Each (row, pass) piece is one 64-column block piece: its sum is
+// scaled by the block's absmax_real and added to the row's value.
+template <int B, int R, int P>
+__device__ __forceinline__ void wave_rows(const WaveGroup<R, P>& g, const u32x4 (&xr)[B][P][8],
+                                          uint32_t copy_off, const uint2* s_pairs,
+                                          const float* s_code2, float offset,
+                                          const bool (&lane_in)[P], float (&val)[R * B]) {
+  constexpr int U = R * P * 8;
+  const char* tab = reinterpret_cast<const char*>(s_pairs);
+  uint2 t[2][4];
+  auto fetch = [&](int u, uint2 (&tt)[4]) {
+    const int rr = u / (P * 8), p = (u / 8) % P, hj = u % 8;
+    const uint32_t d = g.pk[rr][p][hj >> 2][hj & 3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t addr = __builtin_amdgcn_perm(copy_off, d, 0x0C0C0004u | (uint32_t(i) << 8));
+      tt[i] = *reinterpret_cast<const uint2*>(tab + addr);
+    }
+  };
+#pragma unroll
+  for (int v = 0; v < R * B; ++v) val[v] = 0.0f;
+  float part[B];
+  fetch(0, t[0]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u + 1 < U) fetch(u + 1, t[(u + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int rr = u / (P * 8), p = (u / 8) % P, hj = u % 8;
+    if (hj == 0) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) part[b] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 ti = t[u & 1][i];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        // copied out first: a bit_cast of a vector-element lvalue reads
+        // element 0 whatever the index
+        const uint32_t xw = xr[b][p][hj][i];
+        const bf16x2 xp = __builtin_bit_cast(bf16x2, xw);
+        part[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.x), xp, part[b],
+                                                  false);
+        part[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.y), xp, part[b],
+                                                  false);
+      }
+    }
+    if (hj == 7) {
+      const float prod = s_code2[g.q[rr][p]] * f16_to_f32(g.a2[rr][p]);
+      const float a = prod + offset;
+#pragma unroll
+      for (int b = 0; b < B; ++b) val[rr * B + b] += lane_in[p] ? a * part[b] : 0.0f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int B, int R, int P, int WPE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemv_wave_kernel(
+    const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
+    int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2) {
+  static_assert(R * B <= 2, "one pair reduction per group");
+  __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
+  __shared__ float s_nf4[16];
+  __shared__ float s_code2[256];
+  __shared__ int s_rowbeg[kMaxDescs + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  if (descs == nullptr) {
+    if (tid == 0) s_rowbeg[0] = 0;
+  } else {
+    for (int i = tid; i < count; i += blockDim.x) s_rowbeg[i] = static_cast<int>(descs[i].row_begin);
+  }
+  if (tid == 0) s_rowbeg[count] = total_rows;
+  for (int i = tid; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
+  if (tid < 16) s_nf4[tid] = kNF4[tid];
+  __syncthreads();
+
+  // the wave's row range
+  const int waves = blockDim.x >> 6;
+  const int64_t tw = static_cast<int64_t>(gridDim.x) * waves;
+  const int64_t wg = static_cast<int64_t>(blockIdx.x) * waves + wave;
+  const int r_begin = static_cast<int>(wg * total_rows / tw);
+  const int r_end = static_cast<int>((wg + 1) * total_rows / tw);
+  RowCursor cur_c;
+  {
+    int lo = 0, hi = count - 1;  // last matrix whose first row is <= r_begin
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uniform_lds(s_rowbeg, mid) <= r_begin) lo = mid; else hi = mid - 1;
+    }
+    cur_c.m = lo;
+    cur_c.r = r_begin;
+    cur_c.beg = uniform_lds(s_rowbeg, lo);
+    cur_c.end = uniform_lds(s_rowbeg, lo + 1);
+  }
+  // groups of this wave
+  int iters = 0;
+  for (int mm = cur_c.m; mm < count && uniform_lds(s_rowbeg, mm) < r_end; ++mm) {
+    const int lo = max(r_begin, uniform_lds(s_rowbeg, mm));
+    const int hi = min(r_end, uniform_lds(s_rowbeg, mm + 1));
+    if (hi > lo) iters += (hi - lo + R - 1) / R;
+  }
+
+  WaveLane<P> wl;
+  bool lane_in[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int c0 = kWaveCols * p + 64 * lane;
+    lane_in[p] = c0 < K;
+    wl.pk[p] = lane_in[p] ? static_cast<uint32_t>(c0 >> 1) : kFar;
+    wl.x[p] = lane_in[p] ? static_cast<uint32_t>(c0 * 2) : kFar;
+    wl.c0[p] = static_cast<uint32_t>(c0);
+  }
+
+  // the first two groups
+  int m0, rl0, m1, rl1;
+  int len0 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m0, &rl0);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  const nf4_gemv_desc d0 = open_desc(descs, single, m0, len0, s_rowbeg, K);
+  int len1 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m1, &rl1);
+  m1 = __builtin_amdgcn_readfirstlane(m1);
+  LoadBufs lb0 = load_bufs(d0, K, log2bs, log2s2);
+  OutBufs ob0 = out_bufs<B>(d0);
+  WaveGroup<R, P> g0, g1, g2;
+  load_wave_group<R, P>(g0, lb0, rl0, len0, wl, K, log2bs, log2s2);
+  u32x4 xr[B][P][8];
+  load_wave_x<B, P>(xr, x_buf<B>(d0, K), wl, K);
+  int mL = m0;
+  LoadBufs lbL = lb0;
+  OutBufs ob1 = ob0;
+  if (len1 > 0 && m1 != m0) {
+    const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, s_rowbeg, K);
+    lbL = load_bufs(d1, K, log2bs, log2s2);
+    ob1 = out_bufs<B>(d1);
+    mL = m1;
+  }
+  load_wave_group<R, P>(g1, lbL, rl1, len1, wl, K, log2bs, log2s2);
+
+  for (int e = tid; e < 256 * kPairCopies; e += blockDim.x) {
+    const int b = e / kPairCopies;
+    const float ve = s_nf4[b >> 4], vo = s_nf4[b & 15];
+    const uint32_t hi = pack_pair<NF4_BF16>(ve, vo);
+    const float he = __builtin_bit_cast(float, hi << 16);
+    const float ho = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+    const uint32_t lo2 = pack_pair<NF4_BF16>(ve - he, vo - ho);  // exact differences
+    s_pairs[e] = make_uint2(hi, lo2);
+  }
+  const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
+  __syncthreads();
+
+  auto step = [&](WaveGroup<R, P>& cur, WaveGroup<R, P>& fut) {
+    int m2, rl2;
+    const int len2 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m2, &rl2);
+    m2 = __builtin_amdgcn_readfirstlane(m2);
+    OutBufs ob2 = ob1;
+    if (len2 > 0 && m2 != mL) {
+      const nf4_gemv_desc d2 = open_desc(descs, single, m2, len2, s_rowbeg, K);
+      lbL = load_bufs(d2, K, log2bs, log2s2);
+      ob2 = out_bufs<B>(d2);
+      mL = m2;
+    }
+    load_wave_group<R, P>(fut, lbL, rl2, len2, wl, K, log2bs, log2s2);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float val[R * B];
+    wave_rows<B, R, P>(cur, xr, copy_off, s_pairs, s_code2, ob0.offset, lane_in, val);
+    const float tot = wave_sum_pair(val[0], R * B > 1 ? val[R * B - 1] : 0.0f);
+    {
+      const int v = lane >> 5;
+      const int rr = v / B, b = v % B;
+      const bool store = (lane & 31) == 0 && v < R * B && rr < len0;
+      const uint32_t off = static_cast<uint32_t>((b * ob0.N + rl0 + rr) * 2);
+      __builtin_amdgcn_raw_buffer_store_b16(to_half_bits<NF4_BF16>(tot), ob0.y,
+                                            store ? off : kOutOfRange, 0, 0);
+    }
+    if (len1 > 0 && m1 != m0) {
+      load_wave_x<B, P>(xr, x_buf<B>(open_desc(descs, single, m1, len1, s_rowbeg, K), K), wl, K);
+      __builtin_amdgcn_s_waitcnt(0);  // rare; keeps these loads off the common path's counts
+    }
+    ob0 = ob1;
+    ob1 = ob2;
+    m0 = len1 > 0 ? m1 : m0;
+    m1 = len2 > 0 ? m2 : m1;
+    rl0 = rl1;
+    rl1 = rl2;
+    len0 = len1;
+    len1 = len2;
+  };
+  const int rounds = iters / 3;
+  for (int it = 0; it < rounds; ++it) {
+    step(g0, g2);
+    step(g1, g0);
+    step(g2, g1);
+  }
+  const int rest = iters - 3 * rounds;
+  if (rest > 0) step(g0, g2);
+  if (rest > 1) step(g1, g0);
 }
 
 // ---------------------------------------------------------------------------
@@ -902,10 +1222,11 @@ nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const 
   return launch_status();
 }
 
-// rows per group: 2 at batch 1 (127 VGPRs with prefetch depth 2, four waves
-// per SIMD), 1 at batch 2
+// rows per group: 4 at batch 1, 2 at batch 2 (four values per wave
+// reduction; with prefetch depth 2 this stays within the 128 VGPRs of four
+// waves per SIMD)
 template <int B>
-constexpr int stream_rows() { return B == 1 ? 2 : 1; }
+constexpr int stream_rows() { return B == 1 ? 4 : 2; }
 
 template <int B, int NW>
 void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
@@ -915,10 +1236,49 @@ void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, i
                      dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2);
 }
 
+// The wave-per-row kernel for (B, P): rows per group and waves per SIMD are
+// set by registers: the activations take 32 B P VGPRs, each row group 10 R P,
+// and three groups are in flight.
+template <int B, int R, int P, int WPE>
+nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
+                       int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
+                       hipStream_t st) {
+  // one 512-lane workgroup per CU at two waves per SIMD, two at four
+  const int64_t max_wg = static_cast<int64_t>(device_cus()) * (WPE / 2);
+  const int64_t want = (static_cast<int64_t>(total_rows) + 7) / 8;
+  const int64_t grid = want < max_wg ? (want > 0 ? want : 1) : max_wg;
+  hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE>), dim3(static_cast<uint32_t>(grid)), dim3(512),
+                     0, st, descs, single, count, total_rows, K, lbs, ls2, code2);
+  return launch_status();
+}
+
+// Returns NF4_EUNSUPPORTED (without launching) when no wave-per-row
+// configuration covers (B, K, blocksize).
+template <int B>
+nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
+                         int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
+                         hipStream_t st) {
+  if (K % 64 != 0 || lbs < 6) return NF4_EUNSUPPORTED;
+  const int P = (K + kWaveCols - 1) / kWaveCols;
+  if constexpr (B == 1) {
+    if (P == 1) return wave_launch<1, 2, 1, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 2) return wave_launch<1, 1, 2, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 3) return wave_launch<1, 1, 3, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
+  } else {
+    if (P == 1) return wave_launch<2, 1, 1, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 2) return wave_launch<2, 1, 2, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
+  }
+  return NF4_EUNSUPPORTED;
+}
+
 template <int B>
 nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                          hipStream_t st) {
+  {
+    const nf4_status ws = wave_dispatch<B>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
+    if (ws != NF4_EUNSUPPORTED) return ws;
+  }
   const int nw = (K + kSlab - 1) / kSlab;
   const int teams = 8 / nw;
   // persistent: at most two 512-lane workgroups per CU (the decode table takes

@@ -157,15 +157,33 @@ typedef struct nf4_gemv_desc {
  *  blocksize     : power of two >= 32; s2_blocksize: power of two.
  *  code2         : device fp16 bits [256] shared by all matrices.
  *  batch         : 1 or 2.
- * Returns NF4_EINVAL for a NULL or misaligned descs / code2, odd K or bad
- * block sizes; NF4_EUNSUPPORTED outside the ranges above.  The descriptors are
- * read on the device: a matrix whose packed or x pointer is not 16-byte
- * aligned, whose pointers are NULL, or whose N disagrees with the row_begin
- * sequence is skipped (its y is left unwritten).
+ *  sched         : optional DEVICE scheduling workspace of sched_bytes >=
+ *                  nf4_gemv_sched_size() bytes, 256-byte aligned, filled with
+ *                  zeros before its first use.  With it, the rows of large
+ *                  launches are handed to the waves in small chunks as they
+ *                  free up (better balanced than a fixed split); each launch
+ *                  returns the counters it used to zero when it completes, so
+ *                  one buffer serves any number of launches on one stream.
+ *                  Launches that can run at the same time (other streams)
+ *                  need buffers of their own.  NULL: fixed split.  The
+ *                  results are bit-identical either way.
+ * Returns NF4_EINVAL for a NULL or misaligned descs / code2, odd K, bad block
+ * sizes, or a misaligned / too small sched; NF4_EUNSUPPORTED outside the
+ * ranges above.  The descriptors are read on the device: a matrix whose
+ * packed or x pointer is not 16-byte aligned, whose pointers are NULL, or
+ * whose N disagrees with the row_begin sequence is skipped (its y is left
+ * unwritten).
  */
 nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t total_rows,
                             int64_t K, int32_t blocksize, int32_t s2_blocksize,
-                            const uint16_t* code2, int32_t batch, void* stream);
+                            const uint16_t* code2, int32_t batch, void* sched,
+                            size_t sched_bytes, void* stream);
+
+/*
+ * nf4_gemv_sched_size -- bytes of the scheduling workspace nf4_gemv_grouped
+ * takes (host function).
+ */
+size_t nf4_gemv_sched_size(void);
 
 /*
  * nf4_code2_linear -- the linear second-level code table: out[i] = the fp16

@@ -112,3 +112,24 @@ def test_quantize_rejects_bad_arguments(lib, kw):
     rc = lib.nf4_quantize(kw.get("w", FAKE), n, kw.get("bs", 64), kw.get("s2", 256), FAKE, FAKE,
                           FAKE, FAKE, FAKE, kw.get("ws", FAKE), ws_bytes, None)
     assert rc == 1
+
+
+def test_gemv_sched_size(lib):
+    assert lib.nf4_gemv_sched_size() >= 8 * 4
+
+
+@pytest.mark.parametrize("kw", [dict(sched=C.c_void_p(0x1010)),            # misaligned
+                                dict(sched_bytes=16),                       # too small
+                                dict(K=63), dict(bs=3), dict(count=-1),
+                                dict(descs=None), dict(code2=None)])
+def test_gemv_grouped_rejects_bad_arguments(lib, kw):
+    sched = kw.get("sched", C.c_void_p(0x1000))
+    sched_bytes = kw.get("sched_bytes", lib.nf4_gemv_sched_size())
+    rc = lib.nf4_gemv_grouped(kw.get("descs", FAKE), kw.get("count", 2), 100, kw.get("K", 64),
+                              kw.get("bs", 64), 256, kw.get("code2", FAKE), 1, sched,
+                              sched_bytes, None)
+    assert rc == 1
+
+
+def test_gemv_grouped_empty_is_a_no_op(lib):
+    assert lib.nf4_gemv_grouped(None, 0, 0, 64, 64, 256, None, 1, None, 0, None) == 0

@@ -293,6 +293,43 @@ def test_gemv_grouped_matches_oracle(K, shapes, batch):
         assert ok, f"grouped N={N} K={K}: worst {worst:.3g}"
 
 
+def test_gemv_grouped_dynamic_schedule():
+    """Enough rows (>= 64 per wave) for chunked row distribution: the
+    results match the oracle, are bit-identical to the fixed split, stay the
+    same over repeated launches, and every launch leaves the workspace at
+    zero."""
+    K = 128
+    shapes = [(100003, 680), (150001, 681), (50000, 682)]
+    qs, items = _group_case(shapes, K, 1, 790)
+    ys_static = [torch.empty_like(it[3]) for it in items]
+    grp = nf4.GemvGroup(items, K, dynamic=True)
+    ref = nf4.GemvGroup([(w, N, x, ys) for (w, N, x, _), ys in zip(items, ys_static)], K,
+                        dynamic=False)
+    assert grp.sched is not None and ref.sched is None
+    print(f"[gemv_grouped_dynamic] K={K} rows={sum(n for n, _ in shapes)}", flush=True)
+    ref.launch()
+    first = None
+    for rep in range(3):
+        for it in items:
+            it[3].fill_(float("nan"))
+        grp.launch()
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(grp.sched)) == 0, f"workspace not reset after launch {rep}"
+        ys = [it[3].view(torch.int16).clone() for it in items]
+        if first is None:
+            first = ys
+        for a, b in zip(ys, first):
+            assert torch.equal(a, b), f"launch {rep} differs from launch 0"
+    for a, b in zip(first, ys_static):
+        assert torch.equal(a, b.view(torch.int16)), "dynamic and fixed split differ"
+    for (q, N, xb, base), (_, _, _, yv) in zip(qs, items):
+        assert G.guards_intact(base, N), "write outside y"
+        y = G.bf16_to_f64(G.bits16(yv)).reshape(1, N)
+        yr, S = oracle.gemv(q, N, K, xb)
+        ok, worst = G.gemv_within_tolerance(y, yr, S)
+        assert ok, f"dynamic N={N}: worst {worst:.3g}"
+
+
 def test_gemv_grouped_skips_bad_descriptors():
     """A descriptor whose N disagrees with the row offsets is skipped: its y
     keeps its old contents; the others are still computed."""

@@ -19,7 +19,7 @@ NF4_OK, NF4_EINVAL, NF4_EUNSUPPORTED, NF4_EHIP = 0, 1, 2, 3
 NF4_BF16, NF4_FP16 = 0, 1
 
 EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv",
-            "nf4_gemv_grouped", "nf4_code2_linear", "nf4_quantize_workspace_size",
+            "nf4_gemv_grouped", "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
             "nf4_quantize")
 
 _lib = None
@@ -50,7 +50,9 @@ def load() -> C.CDLL:
     lib.nf4_gemv.restype = C.c_int
     lib.nf4_gemv.argtypes = [p, p, p, p, f32, i64, i64, i32, i32, p, i32, p, p]
     lib.nf4_gemv_grouped.restype = C.c_int
-    lib.nf4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, i32, p]
+    lib.nf4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, i32, p, C.c_size_t, p]
+    lib.nf4_gemv_sched_size.restype = C.c_size_t
+    lib.nf4_gemv_sched_size.argtypes = []
     lib.nf4_code2_linear.restype = None
     lib.nf4_code2_linear.argtypes = [p]
     lib.nf4_quantize_workspace_size.restype = C.c_size_t
@@ -228,9 +230,13 @@ class GemvGroup:
     only enqueues the kernel (so it can be captured in a HIP graph).
 
     items: list of (w: NF4Tensor, N, x: bf16 [batch][K] tensor, y: bf16 [batch][N] tensor).
+    dynamic: give the launch a scheduling workspace (owned by the group), so
+    that rows go to the waves in chunks as they free up; False: fixed split.
+    The results are bit-identical either way.  The group's workspace serves
+    one launch at a time: do not run the same group on two streams at once.
     """
 
-    def __init__(self, items, K: int):
+    def __init__(self, items, K: int, dynamic: bool = True):
         import numpy as np
         if not 1 <= len(items) <= MAX_GROUP:
             raise ValueError(f"a group holds 1..{MAX_GROUP} matrices")
@@ -270,9 +276,17 @@ class GemvGroup:
         dev = items[0][0].packed.device
         self.table = torch.from_numpy(table.view(np.uint8)).to(dev)
         _dev(self.code2, "code2", _HALF_BITS, 256)
+        self.sched = None
+        if dynamic:
+            nbytes = int(load().nf4_gemv_sched_size())
+            self.sched = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=dev)
+            if self.sched.data_ptr() % 256:
+                raise RuntimeError("scheduling workspace is not 256-byte aligned")
 
     def launch(self) -> None:
+        sp, sn = (self.sched.data_ptr(), self.sched.numel() * 4) if self.sched is not None else (None, 0)
         st = load().nf4_gemv_grouped(self.table.data_ptr(), len(self.items), self.total_rows,
                                      self.K, self.blocksize, self.s2_blocksize,
-                                     self.code2.data_ptr(), self.batch, _stream(self.table))
+                                     self.code2.data_ptr(), self.batch, sp, sn,
+                                     _stream(self.table))
         _check("nf4_gemv_grouped", st)

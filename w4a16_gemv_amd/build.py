@@ -24,6 +24,10 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the scheduling claims are single-lane atomics whose result is read much
+    # later; the atomic optimizer would broadcast the result right away and
+    # make the wave wait for every load issued before the atomic
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 

@@ -854,11 +854,63 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P>& g, const u32x4 
   }
 }
 
-template <int B, int R, int P, int WPE>
+// Dynamic row distribution.  The rows are split into `nreg` equal regions
+// (workgroup b serves region b % nreg: with the usual round-robin placement
+// of workgroups on the XCDs, one region per XCD, so the claims of a region
+// stay on one L2).  Inside a region the rows go out in chunks of C: wave w of
+// the region starts with chunk w, and the chunks after the first W go to
+// whichever wave claims them from the region's counter.  Each wave claims one
+// chunk ahead (the claim's result is read only when the current chunk is
+// done), so the atomic's latency is hidden.  Waves on one SIMD are not issued
+// fairly (the older wave wins), so a static split leaves the younger waves
+// with the tail; claiming evens out the finishing times.
+struct SchedRegion {
+  unsigned* claims;  // claims made on this region (kept by the workspace)
+  unsigned* done;    // waves of this region that have finished
+  int lo, hi;        // rows of the region
+  int W;             // waves serving the region
+};
+constexpr int kSchedStride = 64;  // uint32 per region (256 bytes): counters on separate lines
+constexpr int kSchedRegions = 8;
+
+// The claim of the next chunk, issued by lane 0 only; the other lanes keep
+// their value, so nothing else writes the register while the atomic is in
+// flight.
+__device__ __forceinline__ void claim_chunk(uint32_t& claim, unsigned* claims, int lane) {
+  if (lane == 0) claim = atomicAdd(claims, 1u);
+}
+
+// next_group over a chunked range: when the current chunk [c.r, r_end) is
+// used up, the pre-claimed chunk W + claim is taken (and the next one
+// claimed), or the wave's range ends at the region's end.
+template <int R>
+__device__ __forceinline__ int next_group_dyn(RowCursor& c, int& r_end, uint32_t& claim,
+                                              const SchedRegion& sr, int C, const int* s_rowbeg,
+                                              int count, int lane, int* m_out, int* rl_out) {
+  if (c.r >= r_end && r_end < sr.hi) {
+    // read at the use, not hoisted next to the atomic: an early read would
+    // wait for every load issued before the atomic
+    uint32_t cl;
+    asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(cl) : "v"(claim));
+    const uint32_t ch = static_cast<uint32_t>(sr.W) + cl;
+    const uint32_t nch = (static_cast<uint32_t>(sr.hi - sr.lo) + static_cast<uint32_t>(C) - 1u) /
+                         static_cast<uint32_t>(C);
+    if (ch >= nch) {
+      c.r = r_end = sr.hi;
+    } else {
+      c.r = sr.lo + static_cast<int>(ch * static_cast<uint32_t>(C));
+      r_end = min(c.r + C, sr.hi);
+      if (r_end < sr.hi) claim_chunk(claim, sr.claims, lane);
+    }
+  }
+  return next_group<R>(c, r_end, s_rowbeg, count, m_out, rl_out);
+}
+
+template <int B, int R, int P, int WPE, bool DYN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemv_wave_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
-    int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2) {
-  static_assert(R * B <= 2, "one pair reduction per group");
+    int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2, unsigned* sched, int C) {
+  static_assert(R * B <= 4, "one pair or quad reduction per group");
   __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
   __shared__ float s_nf4[16];
   __shared__ float s_code2[256];
@@ -877,12 +929,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   if (tid < 16) s_nf4[tid] = kNF4[tid];
   __syncthreads();
 
-  // the wave's row range
+  // the wave's rows: a fixed share, or its first chunk (DYN)
   const int waves = blockDim.x >> 6;
-  const int64_t tw = static_cast<int64_t>(gridDim.x) * waves;
-  const int64_t wg = static_cast<int64_t>(blockIdx.x) * waves + wave;
-  const int r_begin = static_cast<int>(wg * total_rows / tw);
-  const int r_end = static_cast<int>((wg + 1) * total_rows / tw);
+  int r_begin, r_end;
+  SchedRegion sr{};
+  uint32_t claim = 0;
+  if constexpr (DYN) {
+    const int nreg = min(kSchedRegions, static_cast<int>(gridDim.x));
+    const int region = static_cast<int>(blockIdx.x) % nreg;
+    sr.claims = sched + region * kSchedStride;
+    sr.done = sr.claims + 1;
+    sr.lo = static_cast<int>(static_cast<int64_t>(total_rows) * region / nreg);
+    sr.hi = static_cast<int>(static_cast<int64_t>(total_rows) * (region + 1) / nreg);
+    sr.W = waves * ((static_cast<int>(gridDim.x) - 1 - region) / nreg + 1);
+    const int wr = (static_cast<int>(blockIdx.x) / nreg) * waves + wave;  // index in the region
+    const int64_t first = static_cast<int64_t>(wr) * C;
+    const int rows = sr.hi - sr.lo;
+    r_begin = sr.lo + static_cast<int>(min(first, static_cast<int64_t>(rows)));
+    r_end = sr.lo + static_cast<int>(min(first + C, static_cast<int64_t>(rows)));
+    if (r_end < sr.hi) claim_chunk(claim, sr.claims, lane);
+  } else {
+    const int64_t tw = static_cast<int64_t>(gridDim.x) * waves;
+    const int64_t wg = static_cast<int64_t>(blockIdx.x) * waves + wave;
+    r_begin = static_cast<int>(wg * total_rows / tw);
+    r_end = static_cast<int>((wg + 1) * total_rows / tw);
+  }
   RowCursor cur_c;
   {
     int lo = 0, hi = count - 1;  // last matrix whose first row is <= r_begin
@@ -895,9 +966,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     cur_c.beg = uniform_lds(s_rowbeg, lo);
     cur_c.end = uniform_lds(s_rowbeg, lo + 1);
   }
-  // groups of this wave
+  // groups of this wave (static split only)
   int iters = 0;
-  for (int mm = cur_c.m; mm < count && uniform_lds(s_rowbeg, mm) < r_end; ++mm) {
+  for (int mm = cur_c.m; !DYN && mm < count && uniform_lds(s_rowbeg, mm) < r_end; ++mm) {
     const int lo = max(r_begin, uniform_lds(s_rowbeg, mm));
     const int hi = min(r_end, uniform_lds(s_rowbeg, mm + 1));
     if (hi > lo) iters += (hi - lo + R - 1) / R;
@@ -914,12 +985,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     wl.c0[p] = static_cast<uint32_t>(c0);
   }
 
+  auto advance = [&](int* m_out, int* rl_out) {
+    if constexpr (DYN)
+      return next_group_dyn<R>(cur_c, r_end, claim, sr, C, s_rowbeg, count, lane, m_out, rl_out);
+    else
+      return next_group<R>(cur_c, r_end, s_rowbeg, count, m_out, rl_out);
+  };
+
   // the first two groups
   int m0, rl0, m1, rl1;
-  int len0 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m0, &rl0);
+  int len0 = advance(&m0, &rl0);
   m0 = __builtin_amdgcn_readfirstlane(m0);
   const nf4_gemv_desc d0 = open_desc(descs, single, m0, len0, s_rowbeg, K);
-  int len1 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m1, &rl1);
+  int len1 = advance(&m1, &rl1);
   m1 = __builtin_amdgcn_readfirstlane(m1);
   LoadBufs lb0 = load_bufs(d0, K, log2bs, log2s2);
   OutBufs ob0 = out_bufs<B>(d0);
@@ -927,6 +1005,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   load_wave_group<R, P>(g0, lb0, rl0, len0, wl, K, log2bs, log2s2);
   u32x4 xr[B][P][8];
   load_wave_x<B, P>(xr, x_buf<B>(d0, K), wl, K);
+  const void* x_cur = d0.x;  // activations held in xr
   int mL = m0;
   LoadBufs lbL = lb0;
   OutBufs ob1 = ob0;
@@ -952,7 +1031,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 
   auto step = [&](WaveGroup<R, P>& cur, WaveGroup<R, P>& fut) {
     int m2, rl2;
-    const int len2 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m2, &rl2);
+    const int len2 = advance(&m2, &rl2);
     m2 = __builtin_amdgcn_readfirstlane(m2);
     OutBufs ob2 = ob1;
     if (len2 > 0 && m2 != mL) {
@@ -964,20 +1043,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     load_wave_group<R, P>(fut, lbL, rl2, len2, wl, K, log2bs, log2s2);
     __builtin_amdgcn_sched_barrier(0);
 
-    float val[R * B];
-    wave_rows<B, R, P>(cur, xr, copy_off, s_pairs, s_code2, ob0.offset, lane_in, val);
-    const float tot = wave_sum_pair(val[0], R * B > 1 ? val[R * B - 1] : 0.0f);
-    {
-      const int v = lane >> 5;
+    // (a chunked range may end inside a round: empty groups skip the work)
+    if (len0 > 0) {
+      float val[R * B];
+      wave_rows<B, R, P>(cur, xr, copy_off, s_pairs, s_code2, ob0.offset, lane_in, val);
+      // value v of the group ends up in lane 32 v (pair) or in row 16-lane
+      // row r with v = 2 (r & 1) + (r >> 1) (quad)
+      float tot;
+      int v;
+      bool first;
+      if constexpr (R * B <= 2) {
+        tot = wave_sum_pair(val[0], R * B > 1 ? val[R * B - 1] : 0.0f);
+        v = lane >> 5;
+        first = (lane & 31) == 0;
+      } else {
+        tot = wave_sum_quad(val[0], val[1], val[2], R * B > 3 ? val[3] : 0.0f);
+        const int row16 = lane >> 4;
+        v = ((row16 & 1) << 1) | (row16 >> 1);
+        first = (lane & 15) == 0;
+      }
       const int rr = v / B, b = v % B;
-      const bool store = (lane & 31) == 0 && v < R * B && rr < len0;
+      const bool store = first && v < R * B && rr < len0;
       const uint32_t off = static_cast<uint32_t>((b * ob0.N + rl0 + rr) * 2);
       __builtin_amdgcn_raw_buffer_store_b16(to_half_bits<NF4_BF16>(tot), ob0.y,
                                             store ? off : kOutOfRange, 0, 0);
     }
+    // the next group starts a matrix with other activations: fetch them now
+    // that the current ones are no longer needed
     if (len1 > 0 && m1 != m0) {
-      load_wave_x<B, P>(xr, x_buf<B>(open_desc(descs, single, m1, len1, s_rowbeg, K), K), wl, K);
-      __builtin_amdgcn_s_waitcnt(0);  // rare; keeps these loads off the common path's counts
+      const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, s_rowbeg, K);
+      if (d1.x != x_cur) {
+        load_wave_x<B, P>(xr, x_buf<B>(d1, K), wl, K);
+        x_cur = d1.x;
+        __builtin_amdgcn_s_waitcnt(0);  // rare; keeps these loads off the common path's counts
+      }
     }
     ob0 = ob1;
     ob1 = ob2;
@@ -988,15 +1087,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     len0 = len1;
     len1 = len2;
   };
-  const int rounds = iters / 3;
-  for (int it = 0; it < rounds; ++it) {
-    step(g0, g2);
-    step(g1, g0);
-    step(g2, g1);
+  // Whole rounds of three steps (see gemv_stream_kernel for why no step ends
+  // the loop); with DYN the number of groups is not known in advance, and
+  // the at most two empty steps of the last round skip their work.
+  if constexpr (DYN) {
+    while (len0 > 0) {
+      step(g0, g2);
+      step(g1, g0);
+      step(g2, g1);
+    }
+    // the last wave of the region returns its counters to zero, so the
+    // workspace is ready for the next launch: every claim of this launch has
+    // returned by now (each wave read its last one before stopping)
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) {
+      const unsigned prev = atomicAdd(sr.done, 1u);
+      if (prev == static_cast<unsigned>(sr.W - 1)) {
+        atomicExch(sr.claims, 0u);
+        atomicExch(sr.done, 0u);
+      }
+    }
+  } else {
+    const int rounds = iters / 3;
+    for (int it = 0; it < rounds; ++it) {
+      step(g0, g2);
+      step(g1, g0);
+      step(g2, g1);
+    }
+    const int rest = iters - 3 * rounds;
+    if (rest > 0) step(g0, g2);
+    if (rest > 1) step(g1, g0);
   }
-  const int rest = iters - 3 * rounds;
-  if (rest > 0) step(g0, g2);
-  if (rest > 1) step(g1, g0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1238,17 +1359,29 @@ void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, i
 
 // The wave-per-row kernel for (B, P): rows per group and waves per SIMD are
 // set by registers: the activations take 32 B P VGPRs, each row group 10 R P,
-// and three groups are in flight.
+// and three groups are in flight.  With a scheduling workspace, four waves per
+// SIMD and at least 64 rows per wave, rows are handed out in chunks (see
+// SchedRegion): about 16 chunks per wave, 4 to 32 rows each.
 template <int B, int R, int P, int WPE>
 nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                        int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
-                       hipStream_t st) {
+                       unsigned* sched, hipStream_t st) {
   // one 512-lane workgroup per CU at two waves per SIMD, two at four
   const int64_t max_wg = static_cast<int64_t>(device_cus()) * (WPE / 2);
   const int64_t want = (static_cast<int64_t>(total_rows) + 7) / 8;
   const int64_t grid = want < max_wg ? (want > 0 ? want : 1) : max_wg;
-  hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE>), dim3(static_cast<uint32_t>(grid)), dim3(512),
-                     0, st, descs, single, count, total_rows, K, lbs, ls2, code2);
+  const int64_t rows_per_wave = (static_cast<int64_t>(total_rows) + grid * 8 - 1) / (grid * 8);
+  if (WPE == 4 && sched != nullptr && rows_per_wave >= 64) {
+    int C = 4;
+    while (C < 32 && C * 2 * 16 <= rows_per_wave) C *= 2;
+    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, true>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2, sched,
+                       C);
+  } else {
+    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, false>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2,
+                       nullptr, 0);
+  }
   return launch_status();
 }
 
@@ -1257,16 +1390,16 @@ nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, 
 template <int B>
 nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
-                         hipStream_t st) {
+                         unsigned* sched, hipStream_t st) {
   if (K % 64 != 0 || lbs < 6) return NF4_EUNSUPPORTED;
   const int P = (K + kWaveCols - 1) / kWaveCols;
   if constexpr (B == 1) {
-    if (P == 1) return wave_launch<1, 2, 1, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
-    if (P == 2) return wave_launch<1, 1, 2, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
-    if (P == 3) return wave_launch<1, 1, 3, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 1) return wave_launch<1, 2, 1, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 2) return wave_launch<1, 1, 2, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 3) return wave_launch<1, 1, 3, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
   } else {
-    if (P == 1) return wave_launch<2, 1, 1, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
-    if (P == 2) return wave_launch<2, 1, 2, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 1) return wave_launch<2, 1, 1, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 2) return wave_launch<2, 1, 2, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
   }
   return NF4_EUNSUPPORTED;
 }
@@ -1274,9 +1407,10 @@ nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
 template <int B>
 nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
-                         hipStream_t st) {
+                         unsigned* sched, hipStream_t st) {
   {
-    const nf4_status ws = wave_dispatch<B>(descs, single, count, total_rows, K, lbs, ls2, code2, st);
+    const nf4_status ws =
+        wave_dispatch<B>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
     if (ws != NF4_EUNSUPPORTED) return ws;
   }
   const int nw = (K + kSlab - 1) / kSlab;
@@ -1318,7 +1452,7 @@ nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const u
       one.row_begin = 0;
       one.offset = offset;
       return stream_launch<B>(nullptr, one, 1, static_cast<int>(N), static_cast<int>(K), lbs, ls2,
-                              code2, st);
+                              code2, nullptr, st);
     }
   }
   if (vec) {
@@ -1405,12 +1539,19 @@ nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16
   return NF4_EINVAL;
 }
 
+size_t nf4_gemv_sched_size(void) {
+  return sizeof(unsigned) * kSchedRegions * kSchedStride;
+}
+
 nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t total_rows,
                             int64_t K, int32_t blocksize, int32_t s2_blocksize,
-                            const uint16_t* code2, int32_t batch, void* stream) {
+                            const uint16_t* code2, int32_t batch, void* sched,
+                            size_t sched_bytes, void* stream) {
   int lbs = 0, ls2 = 0;
   if (!pow2_log2(blocksize, &lbs) || !pow2_log2(s2_blocksize, &ls2)) return NF4_EINVAL;
   if (count < 0 || total_rows < 0 || K < 0 || (K & 1)) return NF4_EINVAL;
+  if (sched != nullptr && (!aligned(sched, 256) || sched_bytes < nf4_gemv_sched_size()))
+    return NF4_EINVAL;
   if (count == 0 || total_rows == 0) return NF4_OK;
   if (!descs || !code2 || (reinterpret_cast<uintptr_t>(descs) & 7)) return NF4_EINVAL;
   if (count > kMaxDescs || total_rows >= 0x7FFFFFFF || K == 0 || K % 32 != 0 ||
@@ -1418,11 +1559,12 @@ nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t t
     return NF4_EUNSUPPORTED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const nf4_gemv_desc none{};
+  unsigned* sc = static_cast<unsigned*>(sched);
   if (batch == 1)
     return stream_launch<1>(descs, none, count, static_cast<int>(total_rows), static_cast<int>(K),
-                            lbs, ls2, code2, st);
+                            lbs, ls2, code2, sc, st);
   return stream_launch<2>(descs, none, count, static_cast<int>(total_rows), static_cast<int>(K),
-                          lbs, ls2, code2, st);
+                          lbs, ls2, code2, sc, st);
 }
 
 }  // extern "C"

@@ -17,13 +17,24 @@ Schedules (--schedule):
            order a real decode step with layer dependencies would use.
 The step is captured once in a HIP graph and replayed.
 
+The timed steps are launched eagerly on one stream (three launches per step
+in the stream schedule), with HIP events bracketing the dominant kernel -- the
+K=4096 grouped GEMV, 192 matrices, 1.33 GB per launch -- in every step.  Before
+the W warm-up steps, the captured step is replayed for at least --prewarm
+seconds: a cold GPU runs this path about 10% slower for its first few hundred
+milliseconds of load while its clocks settle.
+
 Reported: value = algorithmic bytes per step / step time (GB/s); roofline of
-the dominant kernel (the grouped GEMV) measured with HIP events on the launch
-stream; the CPU oracle timed on a bounded sample of the same workload.
+the dominant kernel = its algorithmic bytes per launch / its average duration
+over the timed steps; traffic = its HBM bytes per launch from the committed
+rocprofv3 counter summary (profiles/), given only when that summary was taken
+on the current kernel source; the CPU oracle timed on a bounded sample of the
+same workload.
 Algorithmic bytes: dequant ceil(n/2) + ceil(n/64) + 2 ceil(n/16384) + 516 + 2n;
 GEMV ceil(NK/2) + ceil(NK/64) + 2 ceil(NK/16384) + 516 + 2KB + 2NB.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -85,6 +96,35 @@ def build_workload(dev):
     return dict(layers=layers, xs=xs, big=(big, tb, out), code2=code2)
 
 
+DOMINANT_K = 4096
+DOMINANT_KERNEL = "gemv_wave_kernel<1, 2, 1, 4, true> (nf4_gemv_grouped, K=4096, 192 matrices)"
+KERNEL_SOURCE = os.path.join(ROOT, "w4a16_gemv_amd", "csrc", "nf4_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_wave_k4096_sweep_traffic.txt")
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when there is none or it was taken on other kernel
+    source.  The file holds `key: value` lines (see its header)."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256_16") != source_digest():
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def make_step(wl, schedule):
     """Returns (gemv_fns, dequant_fn, gemv_launches)."""
     import w4a16_gemv_amd as nf4
@@ -109,6 +149,7 @@ def make_step(wl, schedule):
     def dequant():
         tb.dequant(out=out)
 
+    gemvs.groups = groups
     return gemvs, dequant, len(groups)
 
 
@@ -188,6 +229,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--schedule", choices=("stream", "layered"), default="stream")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--prewarm", type=float, default=1.0,
+                    help="seconds of untimed steps before the W warm-up steps")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context timings (all GEMVs, dequant, other schedule)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the timed steps, run an elementwise copy of exactly 1 GiB "
+                         "(1 GiB read, 1 GiB written): the reference for scaling the HBM "
+                         "byte counters of a profiler run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -217,21 +266,69 @@ def main():
     n_dq_bytes = dequant_bytes(big.n)
     step_bytes = n_gemv_bytes + n_dq_bytes
 
-    # timed region: exactly args.steps steps of the chosen schedule
-    torch.cuda.synchronize()
-    ms = time_graph(per_step[args.schedule]["graph"], args.steps, args.warmup, stream)
-    value = step_bytes / (ms * 1e-3) / 1e9
+    # pre-warm (clocks to steady state), then W warm-up steps
+    t0 = time.time()
+    with torch.cuda.stream(stream):
+        while time.time() - t0 < args.prewarm:
+            per_step[args.schedule]["graph"].replay()
+            torch.cuda.synchronize()
+    gemvs, dequant, launches = make_step(wl, args.schedule)
+    dom = [g for g in gemvs.groups if g.K == DOMINANT_K] if args.schedule == "stream" else []
+    dom_bytes = sum(gemv_bytes(it[1], DOMINANT_K) for it in dom[0].items) if dom else 0
 
-    # the dominant kernel (grouped GEMV) and the dequant, each on its own
-    reps = max(10, args.steps)
-    gemv_ms = time_graph(per_step[args.schedule]["gemv_graph"], reps, 3, stream)
-    dq_ms = time_graph(g_dq, reps, 3, stream)
+    def step(ev=None):
+        for grp in gemvs.groups:
+            if ev is not None and dom and grp is dom[0]:
+                ev[0].record(stream)
+                grp.launch()
+                ev[1].record(stream)
+            else:
+                grp.launch()
+        dequant()
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly args.steps steps, events around the dominant kernel
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(args.steps):
+            step(evs[i])
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    value = step_bytes / (ms * 1e-3) / 1e9
+    dom_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / args.steps if dom else None
+
+    if args.calibration_copy:
+        src = torch.full((1 << 30,), 0x5A, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # context (not the metric): all GEMVs, the dequant and the other schedule,
+    # each replayed as a captured graph
     other = "layered" if args.schedule == "stream" else "stream"
-    other_ms = time_graph(per_step[other]["graph"], reps, 3, stream)
-    launches = per_step[args.schedule]["launches"]
+    if args.no_context:
+        gemv_ms = dq_ms = other_ms = float("nan")
+    else:
+        reps = max(10, args.steps)
+        gemv_ms = time_graph(per_step[args.schedule]["gemv_graph"], reps, 3, stream)
+        dq_ms = time_graph(g_dq, reps, 3, stream)
+        other_ms = time_graph(per_step[other]["graph"], reps, 3, stream)
     gemv_gbs = n_gemv_bytes / (gemv_ms * 1e-3) / 1e9
     dq_gbs = n_dq_bytes / (dq_ms * 1e-3) / 1e9
-    log(f"[bench] step {ms:.3f} ms ({value:.0f} GB/s); GEMVs {gemv_ms:.3f} ms ({gemv_gbs:.0f} GB/s, "
+    dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9 if dom else None
+    log(f"[bench] step {ms:.3f} ms ({value:.0f} GB/s); dominant kernel {dom_us or 0:.1f} us "
+        f"({dom_gbs or 0:.0f} GB/s); all GEMVs {gemv_ms:.3f} ms ({gemv_gbs:.0f} GB/s, "
         f"{launches} launches); dequant {dq_ms * 1e3:.1f} us ({dq_gbs:.0f} GB/s); "
         f"{other} schedule step {other_ms:.3f} ms")
 
@@ -259,24 +356,29 @@ def main():
             "batch": 1, "blocksize": 64, "s2_blocksize": 256,
             "dequant_elems": big.n, "dequant_out": "bf16",
             "schedule": args.schedule, "gemv_launches_per_step": launches,
-            "bytes_per_step": step_bytes,
+            "bytes_per_step": step_bytes, "prewarm_s": args.prewarm,
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {
+        "roofline": None if not dom else {
             "bound": "hbm",
-            "kernel": "gemv_stream_kernel<1,2> (nf4_gemv_grouped)",
-            "achieved": round(gemv_gbs, 1),
+            "kernel": DOMINANT_KERNEL,
+            "achieved": round(dom_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "bytes_per_launch": n_gemv_bytes // launches,
-            "avg_launch_us": round(gemv_ms * 1e3 / launches, 3),
+            "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+            "traffic": committed_traffic(),
+            "bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_us, 3),
+            "kernel_source_sha256_16": source_digest(),
         },
-        "dequant": {"kernel": "dequant_vec_kernel<bf16,8>", "gbs": round(dq_gbs, 1),
-                    "us": round(dq_ms * 1e3, 2), "frac": round(dq_gbs / HBM_PEAK_GBS, 4)},
-        f"{other}_schedule": {"ms_per_step": round(other_ms, 4),
-                              "value": round(step_bytes / (other_ms * 1e-3) / 1e9, 1)},
+        "all_gemvs": None if args.no_context else {"gbs": round(gemv_gbs, 1), "ms": round(gemv_ms, 4),
+                                                   "launches": launches},
+        "dequant": None if args.no_context else {
+            "kernel": "dequant_vec_kernel<bf16,8>", "gbs": round(dq_gbs, 1),
+            "us": round(dq_ms * 1e3, 2), "frac": round(dq_gbs / HBM_PEAK_GBS, 4)},
+        f"{other}_schedule": None if args.no_context else {
+            "ms_per_step": round(other_ms, 4),
+            "value": round(step_bytes / (other_ms * 1e-3) / 1e9, 1)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

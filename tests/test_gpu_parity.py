@@ -200,6 +200,10 @@ GEMV_EDGE = [
     (33, 32, 32, 1), (17, 96, 32, 4), (9, 16384, 64, 256), (3, 16416, 64, 256),
     (11, 1000, 64, 256), (13, 2, 64, 256), (6, 130, 2, 8), (300, 1536, 128, 2),
     (257, 1536, 16, 256), (64, 4096, 1 << 12, 1), (2, 40000, 64, 256),
+    # an 8-way shard of a 4096 -> 11008 projection (rows) and of 11008 -> 4096 (columns)
+    (1376, 4096, 64, 256), (4096, 1376, 64, 256),
+    # two and three 4096-column passes per wave, at their upper ends
+    (100, 8192, 64, 256), (50, 12288, 64, 256), (40, 12352, 64, 256),
 ]
 
 

@@ -24,6 +24,14 @@ the W warm-up steps, the captured step is replayed for at least --prewarm
 seconds: a cold GPU runs this path about 10% slower for its first few hundred
 milliseconds of load while its clocks settle.
 
+--workload picks another configuration as a context measurement (the default
+`sweep` is the headline): dequant_1k / dequant_4k (1024^2 and 4096^2 bf16
+dequant), qwen_b1 (the 7 Qwen2.5-1.5B-shaped GEMVs), llama_b1 / llama_b4 /
+llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8).  These run one
+nf4_dequant / nf4_gemv call per matrix over copies of the encoded data rotated
+so that every step reads past the 256 MB MALL (cold HBM), timed from HIP
+graphs, and report the kernel of their largest matrix as the dominant one.
+
 Reported: value = algorithmic bytes per step / step time (GB/s); roofline of
 the dominant kernel = its algorithmic bytes per launch / its average duration
 over the timed steps; traffic = its HBM bytes per launch from the committed
@@ -181,6 +189,116 @@ def time_graph(g, reps, warmup, stream):
     return e0.elapsed_time(e1) / reps  # ms
 
 
+MALL_BYTES = 256 << 20
+VALU_PEAK_TFLOPS = 157.3
+
+
+def build_context(dev, name):
+    """One of the smaller configurations, encoded once and copied into enough
+    sets that one pass over all sets reads more than twice the MALL.
+    Returns dict(sets, step_bytes, flops, launches, dominant, run)."""
+    import torch
+
+    import synth
+    import w4a16_gemv_amd as nf4
+    code2 = nf4.nf4_code2_linear().to(dev)
+
+    def encode(seed, n, outliers=False):
+        w = synth.weights_device(seed, n, dev, outliers=outliers)
+        ws = torch.empty(nf4.load().nf4_quantize_workspace_size(n, 64), dtype=torch.uint8, device=dev)
+        t = nf4.nf4_quantize(w, 64, 256, code2=code2, workspace=ws)
+        del w, ws
+        return t
+
+    def clone(t):
+        return nf4.NF4Tensor(t.packed.clone(), t.absmax_q.clone(), t.absmax2.clone(), t.code2,
+                             t.offset, t.n, t.blocksize, t.s2_blocksize)
+
+    if name.startswith("dequant"):
+        cfg = synth.DEQUANT_1K if name == "dequant_1k" else synth.DEQUANT_4K
+        base = encode(cfg.seed, cfg.n, cfg.outliers)
+        set_bytes = dequant_bytes(cfg.n)
+        nsets = max(2, -(-2 * MALL_BYTES // set_bytes))
+        sets = []
+        for _ in range(nsets):
+            sets.append((clone(base), torch.empty(cfg.n, dtype=torch.bfloat16, device=dev)))
+
+        def run(st, dominant_only=False):
+            t, out = st
+            t.dequant(out=out)
+        return dict(sets=sets, step_bytes=set_bytes, flops=0, launches=1, run=run,
+                    dominant=f"dequant_vec_kernel<bf16,8> ({cfg.rows}x{cfg.cols})",
+                    dominant_bytes=set_bytes, dominant_flops=0)
+
+    if name == "qwen_b1":
+        gemvs, batch, xseed = synth.QWEN_GEMVS, 1, synth.QWEN_X_SEED
+    else:
+        batch = int(name.split("_b")[1])
+        gemvs, xseed = synth.LLAMA_GEMVS, synth.llama_x_seed(batch)
+    xs = {K: synth.activations_device(xseed, batch, K, dev) for K in {g.K for g in gemvs}}
+    base = [(g, encode(g.seed, g.N * g.K)) for g in gemvs]
+    set_bytes = sum(gemv_bytes(g.N, g.K, batch) for g in gemvs)
+    nsets = max(2, -(-2 * MALL_BYTES // set_bytes))
+    sets = []
+    for _ in range(nsets):
+        sets.append([(g, clone(t), torch.empty(batch, g.N, dtype=torch.bfloat16, device=dev))
+                     for g, t in base])
+    dom = max(range(len(gemvs)), key=lambda i: gemvs[i].N * gemvs[i].K)
+    gd = gemvs[dom]
+
+    def run(st, dominant_only=False):
+        for i, (g, t, y) in enumerate(st):
+            if not dominant_only or i == dom:
+                t.gemv(g.N, g.K, xs[g.K], y)
+    return dict(sets=sets, step_bytes=set_bytes, flops=sum(2 * g.N * g.K * batch for g in gemvs),
+                launches=len(gemvs), run=run, batch=batch,
+                dominant=f"nf4_gemv {gd.N}x{gd.K} batch {batch}",
+                dominant_bytes=gemv_bytes(gd.N, gd.K, batch), dominant_flops=2 * gd.N * gd.K * batch)
+
+
+def bench_context(args, dev):
+    """Small kernels are timed from HIP graphs (eager launches from Python
+    cannot keep the GPU busy at 5-20 us per kernel): one graph holds one step
+    over every rotating set, a second one only the dominant kernel's launches
+    over every set.  Per step / per launch = graph time / number of sets."""
+    import torch
+    wl = build_context(dev, args.workload)
+    sets = wl["sets"]
+    stream = torch.cuda.Stream(dev)
+
+    def all_steps():
+        for st in sets:
+            wl["run"](st)
+
+    def all_dominant():
+        for st in sets:
+            wl["run"](st, dominant_only=True)
+
+    g_steps = capture(all_steps, stream)
+    g_dom = capture(all_dominant, stream)
+    t0 = time.time()
+    with torch.cuda.stream(stream):
+        while time.time() - t0 < args.prewarm:
+            g_steps.replay()
+            torch.cuda.synchronize()
+    reps = max(1, -(-args.steps // len(sets)))      # at least args.steps steps
+    ms = time_graph(g_steps, reps, args.warmup, stream) / len(sets)
+    dom_us = 1e3 * time_graph(g_dom, reps, args.warmup, stream) / len(sets)
+    value = wl["step_bytes"] / (ms * 1e-3) / 1e9
+    dom_gbs = wl["dominant_bytes"] / (dom_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "kernel": wl["dominant"], "achieved": round(dom_gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None, "bytes_per_launch": wl["dominant_bytes"], "avg_launch_us": round(dom_us, 3)}
+    if wl["dominant_flops"]:
+        tf = wl["dominant_flops"] / (dom_us * 1e-6) / 1e12
+        roof["alu"] = {"achieved_tflops": round(tf, 2), "peak_tflops": VALU_PEAK_TFLOPS,
+                       "frac": round(tf / VALU_PEAK_TFLOPS, 4)}
+    log(f"[bench] {args.workload}: step {ms * 1e3:.1f} us ({value:.0f} GB/s); dominant "
+        f"{dom_us:.1f} us ({dom_gbs:.0f} GB/s); {len(sets)} rotating sets, {reps} graph replays")
+    return dict(value=value, ms=ms, roofline=roof, sets=len(sets), launches=wl["launches"],
+                step_bytes=wl["step_bytes"], batch=wl.get("batch", 1), steps=reps * len(sets))
+
+
 def cpu_baseline(wl, seconds: float):
     """The oracle (plain C, OpenMP over outputs) timed on the host cores on a
     bounded sample of the same workload: the sweep's GEMVs in order, then a
@@ -228,6 +346,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--schedule", choices=("stream", "layered"), default="stream")
+    ap.add_argument("--workload", default="sweep",
+                    choices=("sweep", "dequant_1k", "dequant_4k", "qwen_b1", "llama_b1",
+                             "llama_b4", "llama_b8"))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--prewarm", type=float, default=1.0,
                     help="seconds of untimed steps before the W warm-up steps")
@@ -249,6 +370,20 @@ def main():
     nf4.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload != "sweep":
+        r = bench_context(args, dev)
+        print(json.dumps({
+            "metric": METRIC, "value": round(r["value"], 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": r["steps"], "warmup": args.warmup, "ms_per_step": round(r["ms"], 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": args.workload, "batch": r["batch"], "blocksize": 64,
+                       "s2_blocksize": 256, "launches_per_step": r["launches"],
+                       "bytes_per_step": r["step_bytes"], "rotating_sets": r["sets"],
+                       "prewarm_s": args.prewarm},
+            "pct_of_peak": round(100 * r["value"] / HBM_PEAK_GBS, 2),
+            "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
+        return
     wl = build_workload(dev)
     stream = torch.cuda.Stream(dev)
 

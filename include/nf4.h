@@ -156,7 +156,7 @@ typedef struct nf4_gemv_desc {
  *                  K <= 16384.
  *  blocksize     : power of two >= 32; s2_blocksize: power of two.
  *  code2         : device fp16 bits [256] shared by all matrices.
- *  batch         : 1 or 2.
+ *  batch         : 1..8.
  *  sched         : optional DEVICE scheduling workspace of sched_bytes >=
  *                  nf4_gemv_sched_size() bytes, 256-byte aligned, filled with
  *                  zeros before its first use.  With it, the rows of large

@@ -226,7 +226,7 @@ MAX_GROUP = 1024
 class GemvGroup:
     """A reusable list of independent GEMVs y_i = W_i x_i launched as one
     nf4_gemv_grouped call.  All W_i share K, the block sizes, code2 and the
-    batch (1 or 2).  The descriptor table is built and uploaded once; launch()
+    batch (1..8).  The descriptor table is built and uploaded once; launch()
     only enqueues the kernel (so it can be captured in a HIP graph).
 
     items: list of (w: NF4Tensor, N, x: bf16 [batch][K] tensor, y: bf16 [batch][N] tensor).
@@ -245,8 +245,8 @@ class GemvGroup:
         w0 = items[0][0]
         self.blocksize, self.s2_blocksize, self.code2 = w0.blocksize, w0.s2_blocksize, w0.code2
         self.batch = items[0][2].shape[0] if items[0][2].dim() == 2 else 1
-        if self.batch not in (1, 2):
-            raise ValueError("grouped GEMV supports batch 1 or 2")
+        if not 1 <= self.batch <= 8:
+            raise ValueError("grouped GEMV supports batch 1..8")
         if K % 32 or K <= 0 or K > 16384:
             raise ValueError("grouped GEMV needs K % 32 == 0 and 0 < K <= 16384")
         if self.blocksize < 32:

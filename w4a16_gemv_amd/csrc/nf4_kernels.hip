@@ -512,8 +512,8 @@ __device__ __forceinline__ int next_group(RowCursor& c, int r_end, const int* s_
 // computes the current one.  All loads and the y stores are branch-free
 // buffer operations.
 // ---------------------------------------------------------------------------
-template <int B, int R, int NW>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_stream_kernel(
+template <int B, int R, int NW, int WPE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemv_stream_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
     int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2) {
   constexpr int nw = NW;  // waves per team: one per 2048-column slab of K
@@ -666,16 +666,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if constexpr (R * B == 2) {
       const float tot = wave_sum_pair(val[0], val[1]);
       if ((lane & 31) == 0) s_red[buf][wave][lane >> 5] = tot;
-    } else if constexpr (R * B == 4) {
-      const float tot = wave_sum_quad(val[0], val[1], val[2], val[3]);
-      // row 0 holds value 0, row 1 value 2, row 2 value 1, row 3 value 3
-      const int row16 = lane >> 4;
-      if ((lane & 15) == 0) s_red[buf][wave][((row16 & 1) << 1) | (row16 >> 1)] = tot;
     } else {
+      // four values at a time; 16-lane row r holds value 4 q + 2 (r & 1) + (r >> 1)
+      const int row16 = lane >> 4;
+      const int slot = ((row16 & 1) << 1) | (row16 >> 1);
 #pragma unroll
-      for (int v = 0; v < R * B; ++v) {
-        const float tot = wave_sum_to_lane63(val[v]);
-        if (lane == 63) s_red[buf][wave][v] = tot;
+      for (int q = 0; q < (R * B + 3) / 4; ++q) {
+        const float tot = wave_sum_quad(val[4 * q], 4 * q + 1 < R * B ? val[4 * q + 1] : 0.0f,
+                                        4 * q + 2 < R * B ? val[4 * q + 2] : 0.0f,
+                                        4 * q + 3 < R * B ? val[4 * q + 3] : 0.0f);
+        if ((lane & 15) == 0 && 4 * q + slot < R * B) s_red[buf][wave][4 * q + slot] = tot;
       }
     }
     __syncthreads();
@@ -1345,15 +1345,19 @@ nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const 
 
 // rows per group: 4 at batch 1, 2 at batch 2 (four values per wave
 // reduction; with prefetch depth 2 this stays within the 128 VGPRs of four
-// waves per SIMD)
+// waves per SIMD), 1 above.  Waves per SIMD: the activations take 16 B VGPRs,
+// so batches above 4 run at two waves per SIMD (one workgroup per CU).
 template <int B>
-constexpr int stream_rows() { return B == 1 ? 4 : 2; }
+constexpr int stream_rows() { return B == 1 ? 4 : (B == 2 ? 2 : 1); }
+template <int B>
+constexpr int stream_wpe() { return B <= 4 ? 4 : 2; }
 
 template <int B, int NW>
 void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                       int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                       int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>(), NW>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>(), NW, stream_wpe<B>()>),
+                     dim3(static_cast<uint32_t>(grid)),
                      dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2);
 }
 
@@ -1408,7 +1412,7 @@ template <int B>
 nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                          unsigned* sched, hipStream_t st) {
-  {
+  if constexpr (B <= 2) {
     const nf4_status ws =
         wave_dispatch<B>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
     if (ws != NF4_EUNSUPPORTED) return ws;
@@ -1416,8 +1420,8 @@ nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   const int nw = (K + kSlab - 1) / kSlab;
   const int teams = 8 / nw;
   // persistent: at most two 512-lane workgroups per CU (the decode table takes
-  // 64 KiB of LDS), at least one row per team
-  const int64_t max_wg = static_cast<int64_t>(device_cus()) * 2;
+  // 64 KiB of LDS; one at two waves per SIMD), at least one row per team
+  const int64_t max_wg = static_cast<int64_t>(device_cus()) * (stream_wpe<B>() / 2);
   const int64_t want = (static_cast<int64_t>(total_rows) + teams - 1) / teams;
   const int64_t grid = want < max_wg ? (want > 0 ? want : 1) : max_wg;
   switch (nw) {
@@ -1440,20 +1444,18 @@ nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const u
                          int ls2, const uint16_t* x, uint16_t* y, hipStream_t st) {
   const bool vec = lbs >= 5 && K % 32 == 0 && K <= 8 * kSlab && N <= 0x7FFFFFFF &&
                    aligned(packed, 16) && aligned(x, 16);
-  if constexpr (B <= 2) {
-    if (vec && N * K < (int64_t(1) << 31)) {  // the streaming kernel's offset range
-      nf4_gemv_desc one{};
-      one.packed = packed;
-      one.absmax_q = absmax_q;
-      one.absmax2 = absmax2;
-      one.x = x;
-      one.y = y;
-      one.N = N;
-      one.row_begin = 0;
-      one.offset = offset;
-      return stream_launch<B>(nullptr, one, 1, static_cast<int>(N), static_cast<int>(K), lbs, ls2,
-                              code2, nullptr, st);
-    }
+  if (vec && N * K < (int64_t(1) << 31)) {  // the streaming kernels' offset range
+    nf4_gemv_desc one{};
+    one.packed = packed;
+    one.absmax_q = absmax_q;
+    one.absmax2 = absmax2;
+    one.x = x;
+    one.y = y;
+    one.N = N;
+    one.row_begin = 0;
+    one.offset = offset;
+    return stream_launch<B>(nullptr, one, 1, static_cast<int>(N), static_cast<int>(K), lbs, ls2,
+                            code2, nullptr, st);
   }
   if (vec) {
     constexpr int R = B <= 4 ? 2 : 1;
@@ -1555,16 +1557,22 @@ nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t t
   if (count == 0 || total_rows == 0) return NF4_OK;
   if (!descs || !code2 || (reinterpret_cast<uintptr_t>(descs) & 7)) return NF4_EINVAL;
   if (count > kMaxDescs || total_rows >= 0x7FFFFFFF || K == 0 || K % 32 != 0 ||
-      K > 8 * kSlab || lbs < 5 || batch < 1 || batch > 2)
+      K > 8 * kSlab || lbs < 5 || batch < 1 || batch > 8)
     return NF4_EUNSUPPORTED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const nf4_gemv_desc none{};
   unsigned* sc = static_cast<unsigned*>(sched);
-  if (batch == 1)
-    return stream_launch<1>(descs, none, count, static_cast<int>(total_rows), static_cast<int>(K),
-                            lbs, ls2, code2, sc, st);
-  return stream_launch<2>(descs, none, count, static_cast<int>(total_rows), static_cast<int>(K),
-                          lbs, ls2, code2, sc, st);
+  const int tr = static_cast<int>(total_rows), k = static_cast<int>(K);
+  switch (batch) {
+    case 1: return stream_launch<1>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 2: return stream_launch<2>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 3: return stream_launch<3>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 4: return stream_launch<4>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 5: return stream_launch<5>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 6: return stream_launch<6>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 7: return stream_launch<7>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    default: return stream_launch<8>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+  }
 }
 
 }  // extern "C"

@@ -13,12 +13,21 @@ namespace nf4dev {
 
 // The 16 NF4 code values, as the 8-decimal literals printed in [blog] "naive";
 // each literal is rounded to the nearest fp32 by the compiler.
-__device__ const float kNF4[16] = {
+__device__ constexpr float kNF4[16] = {
     -1.00000000f, -0.69619280f, -0.52507305f, -0.39491749f,
     -0.28444138f, -0.18477343f, -0.09105004f, 0.00000000f,
     0.07958030f,  0.16093020f,  0.24611230f,  0.33791524f,
     0.44070983f,  0.56261700f,  0.72295684f,  1.00000000f,
 };
+
+// NF4[i] for a runtime index without a memory access: a chain of selects over
+// the literals (constant indices fold to immediates).
+__device__ __forceinline__ float nf4_value(uint32_t i) {
+  float v = kNF4[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) v = i == static_cast<uint32_t>(j) ? kNF4[j] : v;
+  return v;
+}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
 
   // 2. tables, then one absmax_real per block
   s_code2[t] = f16_to_f32(c2);
-  if (t < 16) s_nf4[t] = kNF4[t];
+  if (t < 16) s_nf4[t] = nf4_value(static_cast<uint32_t>(t));
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void dequant_any_kernel(
     const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
     int64_t n, int log2bs, int log2s2, uint16_t* __restrict__ out2) {
   __shared__ float s_nf4[16];
-  if (threadIdx.x < 16) s_nf4[threadIdx.x] = kNF4[threadIdx.x];
+  if (threadIdx.x < 16) s_nf4[threadIdx.x] = nf4_value(threadIdx.x);
   __syncthreads();
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
@@ -261,6 +261,29 @@ constexpr int kSlab = 2048;
 constexpr int kPairCopies = 32;
 
 constexpr int kMaxDescs = 1024;  // matrices per grouped launch
+
+// The decode table: entry b = (hi, lo) where hi holds the bf16 pair
+// (NF4[b >> 4], NF4[b & 15]) and lo the bf16 pair of the exact differences
+// v - bf16(v), replicated kPairCopies times (copy c of entry b at uint2 index
+// 32 b + c).  Each of the 256 entries is computed once by two threads, each
+// of which writes 16 of its copies; the copy order is rotated by the entry,
+// so the 64 lanes of a wave write 32 distinct bank pairs at a time.
+__device__ __forceinline__ void build_pair_table(uint2* s_pairs, int tid, int nthreads) {
+  static_assert(kPairCopies == 32, "two threads per entry, 16 copies each");
+  for (int w = tid; w < 512; w += nthreads) {
+    const int b = w & 255, half = w >> 8;
+    const float ve = nf4_value(b >> 4), vo = nf4_value(b & 15);
+    const uint32_t hi = pack_pair<NF4_BF16>(ve, vo);
+    const float he = __builtin_bit_cast(float, hi << 16);
+    const float ho = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+    const uint32_t lo2 = pack_pair<NF4_BF16>(ve - he, vo - ho);  // exact differences
+    const uint2 entry = make_uint2(hi, lo2);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s_pairs[b * kPairCopies + ((b + 16 * half + k) & 31)] = entry;
+  }
+}
+
+
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -451,15 +474,26 @@ __device__ __forceinline__ int uniform_lds(const int* p, int i) {
   return __builtin_amdgcn_readfirstlane(p[i]);
 }
 
+// Row offsets of the matrices (row_begin, with total_rows after the last):
+// read from LDS for a descriptor list; for a single matrix they are just 0 and
+// N, and no LDS read (a round trip on the kernel's critical path) is made.
+struct RowBegins {
+  const int* lds;  // nullptr: a single matrix
+  int total;
+  __device__ __forceinline__ int operator()(int m) const {
+    return lds != nullptr ? uniform_lds(lds, m) : (m <= 0 ? 0 : total);
+  }
+};
+
 // Descriptor m for the kernel: a matrix it cannot use (see desc_usable) is
 // replaced by an empty one, whose loads read zeros and whose stores are
 // dropped.
 __device__ __forceinline__ nf4_gemv_desc open_desc(const nf4_gemv_desc* __restrict__ descs,
                                                    const nf4_gemv_desc& single, int m, int len,
-                                                   const int* s_rowbeg, int K) {
+                                                   const RowBegins& rbeg, int K) {
   nf4_gemv_desc d = fetch_desc(descs, single, m);
   if (len <= 0 || m < 0 ||
-      !desc_usable(d, uniform_lds(s_rowbeg, m + 1) - uniform_lds(s_rowbeg, m), K)) {
+      !desc_usable(d, rbeg(m + 1) - rbeg(m), K)) {
     d.packed = nullptr;
     d.absmax_q = nullptr;
     d.absmax2 = nullptr;
@@ -469,6 +503,18 @@ __device__ __forceinline__ nf4_gemv_desc open_desc(const nf4_gemv_desc* __restri
     d.offset = 0.0f;
   }
   return d;
+}
+
+// Part i of `total` rows split as evenly as possible into `parts` contiguous
+// ranges (the first total % parts ranges hold one row more): [*lo, *hi).  All
+// 32-bit, so that wave-uniform operands stay a few scalar instructions (a
+// 64-bit division is a long emulated sequence on the scalar unit).
+__device__ __forceinline__ void split_rows(uint32_t total, uint32_t parts, uint32_t i, int* lo,
+                                           int* hi) {
+  const uint32_t q = total / parts, rem = total - q * parts;
+  const uint32_t b = i * q + (i < rem ? i : rem);
+  *lo = static_cast<int>(b);
+  *hi = static_cast<int>(b + q + (i < rem ? 1u : 0u));
 }
 
 // Where a team is in the concatenated row space: matrix m, global row r.
@@ -484,12 +530,12 @@ struct RowCursor {
 // range is exhausted).  The row offsets in LDS are read only when the cursor
 // moves to another matrix.
 template <int R>
-__device__ __forceinline__ int next_group(RowCursor& c, int r_end, const int* s_rowbeg, int count,
+__device__ __forceinline__ int next_group(RowCursor& c, int r_end, const RowBegins& rbeg, int count,
                                           int* m_out, int* rl_out) {
   if (c.r >= c.end && c.r < r_end) {  // skip finished / empty matrices
-    while (c.m < count && uniform_lds(s_rowbeg, c.m + 1) <= c.r) ++c.m;
-    c.beg = c.m < count ? uniform_lds(s_rowbeg, c.m) : c.r;
-    c.end = c.m < count ? uniform_lds(s_rowbeg, c.m + 1) : c.r;
+    while (c.m < count && rbeg(c.m + 1) <= c.r) ++c.m;
+    c.beg = c.m < count ? rbeg(c.m) : c.r;
+    c.end = c.m < count ? rbeg(c.m + 1) : c.r;
   }
   if (c.r >= r_end || c.r >= c.end) {
     *m_out = -1;
@@ -518,7 +564,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2) {
   constexpr int nw = NW;  // waves per team: one per 2048-column slab of K
   __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
-  __shared__ float s_nf4[16];
   __shared__ float s_code2[256];
   __shared__ float s_red[2][8][R * B];
   __shared__ int s_rowbeg[kMaxDescs + 1];
@@ -528,6 +573,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // wave-uniform by construction; saying so keeps all per-team bookkeeping
   // in scalar registers and scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // code2 is fetched first and written to LDS only after the row loads are
+  // issued: its wait then overlaps theirs (the launch uses 512 threads)
+  // (a bounds-checked load for all lanes: lanes past the table read 0)
+  const uint16_t code2_bits = __builtin_amdgcn_raw_buffer_load_b16(
+      rsrc(code2, 512), static_cast<uint32_t>(tid) * 2u, 0u, 0);
   constexpr int teams = 8 / NW;         // the workgroup has 8 waves
   const int team = wave / nw;           // == teams for helper waves
   const int slab = wave - team * nw;
@@ -545,34 +595,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     s_rowbeg[count] = total_rows;
     s_iters = 0;
   }
-  for (int i = tid; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
-  if (tid < 16) s_nf4[tid] = kNF4[tid];
   __syncthreads();
+  const RowBegins rbeg{descs != nullptr ? s_rowbeg : nullptr, total_rows};
 
   // the team's row range
-  const int64_t tt = static_cast<int64_t>(gridDim.x) * teams;
-  const int64_t tg = static_cast<int64_t>(blockIdx.x) * teams + team;
-  const int r_begin = in_team ? static_cast<int>(tg * total_rows / tt) : 0;
-  const int r_end = in_team ? static_cast<int>((tg + 1) * total_rows / tt) : 0;
+  int r_begin = 0, r_end = 0;
+  if (in_team)
+    split_rows(static_cast<uint32_t>(total_rows), gridDim.x * static_cast<uint32_t>(teams),
+               blockIdx.x * static_cast<uint32_t>(teams) + static_cast<uint32_t>(team), &r_begin,
+               &r_end);
   RowCursor cur_c;
   {
     int lo = 0, hi = count - 1;  // last matrix whose first row is <= r_begin
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (uniform_lds(s_rowbeg, mid) <= r_begin) lo = mid; else hi = mid - 1;
+      if (rbeg(mid) <= r_begin) lo = mid; else hi = mid - 1;
     }
     cur_c.m = lo;
     cur_c.r = r_begin;
-    cur_c.beg = uniform_lds(s_rowbeg, lo);
-    cur_c.end = uniform_lds(s_rowbeg, lo + 1);
+    cur_c.beg = rbeg(lo);
+    cur_c.end = rbeg(lo + 1);
   }
   // number of groups of this team (per matrix it overlaps), then the
   // workgroup maximum: every wave runs that many iterations
   {
     int ng = 0;
-    for (int mm = cur_c.m; mm < count && uniform_lds(s_rowbeg, mm) < r_end; ++mm) {
-      const int lo = max(r_begin, uniform_lds(s_rowbeg, mm));
-      const int hi = min(r_end, uniform_lds(s_rowbeg, mm + 1));
+    for (int mm = cur_c.m; mm < count && rbeg(mm) < r_end; ++mm) {
+      const int lo = max(r_begin, rbeg(mm));
+      const int hi = min(r_end, rbeg(mm + 1));
       if (hi > lo) ng += (hi - lo + R - 1) / R;
     }
     if (lane == 0 && slab == 0 && in_team) atomicMax(&s_iters, ng);
@@ -583,10 +633,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // of the newest group's matrix (mL), and the output side of the two groups
   // in compute order; descriptors are re-read only when the matrix changes.
   int m0, rl0, m1, rl1;
-  int len0 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m0, &rl0);
+  int len0 = next_group<R>(cur_c, r_end, rbeg, count, &m0, &rl0);
   m0 = __builtin_amdgcn_readfirstlane(m0);
-  const nf4_gemv_desc d0 = open_desc(descs, single, m0, len0, s_rowbeg, K);
-  int len1 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m1, &rl1);
+  const nf4_gemv_desc d0 = open_desc(descs, single, m0, len0, rbeg, K);
+  int len1 = next_group<R>(cur_c, r_end, rbeg, count, &m1, &rl1);
   m1 = __builtin_amdgcn_readfirstlane(m1);
   LoadBufs lb0 = load_bufs(d0, K, log2bs, log2s2);
   OutBufs ob0 = out_bufs<B>(d0);
@@ -602,7 +652,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   LoadBufs lbL = lb0;
   OutBufs ob1 = ob0;
   if (len1 > 0 && m1 != m0) {
-    const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, s_rowbeg, K);
+    const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, rbeg, K);
     lbL = load_bufs(d1, K, log2bs, log2s2);
     ob1 = out_bufs<B>(d1);
     mL = m1;
@@ -610,15 +660,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   load_row_group<R>(g1, lbL, rl1, len1, lo, K, log2bs, log2s2);
 
   // the 256 x 32 pair table: (bf16 hi pair, bf16 lo pair) of each byte
-  for (int e = tid; e < 256 * kPairCopies; e += blockDim.x) {
-    const int b = e / kPairCopies;
-    const float ve = s_nf4[b >> 4], vo = s_nf4[b & 15];
-    const uint32_t hi = pack_pair<NF4_BF16>(ve, vo);
-    const float he = __builtin_bit_cast(float, hi << 16);
-    const float ho = __builtin_bit_cast(float, hi & 0xFFFF0000u);
-    const uint32_t lo2 = pack_pair<NF4_BF16>(ve - he, vo - ho);  // exact differences
-    s_pairs[e] = make_uint2(hi, lo2);
-  }
+  if (tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
+  build_pair_table(s_pairs, tid, blockDim.x);
   const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
   __syncthreads();
   const int iters = __builtin_amdgcn_readfirstlane(s_iters);
@@ -631,11 +674,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   int buf = 0;
   auto step = [&](RowGroup<R>& cur, RowGroup<R>& fut) {
     int m2, rl2;
-    const int len2 = next_group<R>(cur_c, r_end, s_rowbeg, count, &m2, &rl2);
+    const int len2 = next_group<R>(cur_c, r_end, rbeg, count, &m2, &rl2);
     m2 = __builtin_amdgcn_readfirstlane(m2);
     OutBufs ob2 = ob1;
     if (len2 > 0 && m2 != mL) {
-      const nf4_gemv_desc d2 = open_desc(descs, single, m2, len2, s_rowbeg, K);
+      const nf4_gemv_desc d2 = open_desc(descs, single, m2, len2, rbeg, K);
       lbL = load_bufs(d2, K, log2bs, log2s2);
       ob2 = out_bufs<B>(d2);
       mL = m2;
@@ -694,7 +737,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     // the next group starts a new matrix: fetch its activations now that the
     // current ones are no longer needed
     if (len1 > 0 && m1 != m0) {
-      load_x<B>(xr, x_buf<B>(open_desc(descs, single, m1, len1, s_rowbeg, K), K), lo, K);
+      load_x<B>(xr, x_buf<B>(open_desc(descs, single, m1, len1, rbeg, K), K), lo, K);
       // drain here (rare: once per matrix change) so that the loads of this
       // branch are not assumed outstanding on the common path, where they
       // would make every wait for the current group also wait for the next
@@ -885,7 +928,8 @@ __device__ __forceinline__ void claim_chunk(uint32_t& claim, unsigned* claims, i
 // claimed), or the wave's range ends at the region's end.
 template <int R>
 __device__ __forceinline__ int next_group_dyn(RowCursor& c, int& r_end, uint32_t& claim,
-                                              const SchedRegion& sr, int C, const int* s_rowbeg,
+                                              const SchedRegion& sr, int C, int log2C,
+                                              const RowBegins& rbeg,
                                               int count, int lane, int* m_out, int* rl_out) {
   if (c.r >= r_end && r_end < sr.hi) {
     // read at the use, not hoisted next to the atomic: an early read would
@@ -893,17 +937,17 @@ __device__ __forceinline__ int next_group_dyn(RowCursor& c, int& r_end, uint32_t
     uint32_t cl;
     asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(cl) : "v"(claim));
     const uint32_t ch = static_cast<uint32_t>(sr.W) + cl;
-    const uint32_t nch = (static_cast<uint32_t>(sr.hi - sr.lo) + static_cast<uint32_t>(C) - 1u) /
-                         static_cast<uint32_t>(C);
+    const uint32_t nch =
+        (static_cast<uint32_t>(sr.hi - sr.lo) + static_cast<uint32_t>(C) - 1u) >> log2C;
     if (ch >= nch) {
       c.r = r_end = sr.hi;
     } else {
-      c.r = sr.lo + static_cast<int>(ch * static_cast<uint32_t>(C));
+      c.r = sr.lo + static_cast<int>(ch << log2C);
       r_end = min(c.r + C, sr.hi);
       if (r_end < sr.hi) claim_chunk(claim, sr.claims, lane);
     }
   }
-  return next_group<R>(c, r_end, s_rowbeg, count, m_out, rl_out);
+  return next_group<R>(c, r_end, rbeg, count, m_out, rl_out);
 }
 
 template <int B, int R, int P, int WPE, bool DYN>
@@ -911,13 +955,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
     int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2, unsigned* sched, int C) {
   static_assert(R * B <= 4, "one pair or quad reduction per group");
+  const int log2C = C > 0 ? __builtin_ctz(static_cast<unsigned>(C)) : 0;  // C is a power of two
   __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
-  __shared__ float s_nf4[16];
   __shared__ float s_code2[256];
   __shared__ int s_rowbeg[kMaxDescs + 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // code2 is fetched first and written to LDS only after the row loads are
+  // issued: its wait then overlaps theirs (the launch uses 512 threads)
+  // (a bounds-checked load for all lanes: lanes past the table read 0)
+  const uint16_t code2_bits = __builtin_amdgcn_raw_buffer_load_b16(
+      rsrc(code2, 512), static_cast<uint32_t>(tid) * 2u, 0u, 0);
 
   if (descs == nullptr) {
     if (tid == 0) s_rowbeg[0] = 0;
@@ -925,9 +974,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     for (int i = tid; i < count; i += blockDim.x) s_rowbeg[i] = static_cast<int>(descs[i].row_begin);
   }
   if (tid == 0) s_rowbeg[count] = total_rows;
-  for (int i = tid; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
-  if (tid < 16) s_nf4[tid] = kNF4[tid];
   __syncthreads();
+  const RowBegins rbeg{descs != nullptr ? s_rowbeg : nullptr, total_rows};
 
   // the wave's rows: a fixed share, or its first chunk (DYN)
   const int waves = blockDim.x >> 6;
@@ -939,38 +987,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     const int region = static_cast<int>(blockIdx.x) % nreg;
     sr.claims = sched + region * kSchedStride;
     sr.done = sr.claims + 1;
-    sr.lo = static_cast<int>(static_cast<int64_t>(total_rows) * region / nreg);
-    sr.hi = static_cast<int>(static_cast<int64_t>(total_rows) * (region + 1) / nreg);
+    split_rows(static_cast<uint32_t>(total_rows), static_cast<uint32_t>(nreg),
+               static_cast<uint32_t>(region), &sr.lo, &sr.hi);
     sr.W = waves * ((static_cast<int>(gridDim.x) - 1 - region) / nreg + 1);
     const int wr = (static_cast<int>(blockIdx.x) / nreg) * waves + wave;  // index in the region
-    const int64_t first = static_cast<int64_t>(wr) * C;
-    const int rows = sr.hi - sr.lo;
-    r_begin = sr.lo + static_cast<int>(min(first, static_cast<int64_t>(rows)));
-    r_end = sr.lo + static_cast<int>(min(first + C, static_cast<int64_t>(rows)));
+    const uint32_t rows = static_cast<uint32_t>(sr.hi - sr.lo);
+    const uint32_t first = static_cast<uint32_t>(wr) << log2C;  // wr < 2^13, C <= 32
+    r_begin = sr.lo + static_cast<int>(first < rows ? first : rows);
+    r_end = sr.lo + static_cast<int>(first + C < rows ? first + C : rows);
     if (r_end < sr.hi) claim_chunk(claim, sr.claims, lane);
   } else {
-    const int64_t tw = static_cast<int64_t>(gridDim.x) * waves;
-    const int64_t wg = static_cast<int64_t>(blockIdx.x) * waves + wave;
-    r_begin = static_cast<int>(wg * total_rows / tw);
-    r_end = static_cast<int>((wg + 1) * total_rows / tw);
+    split_rows(static_cast<uint32_t>(total_rows), gridDim.x * static_cast<uint32_t>(waves),
+               blockIdx.x * static_cast<uint32_t>(waves) + static_cast<uint32_t>(wave), &r_begin,
+               &r_end);
   }
   RowCursor cur_c;
   {
     int lo = 0, hi = count - 1;  // last matrix whose first row is <= r_begin
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (uniform_lds(s_rowbeg, mid) <= r_begin) lo = mid; else hi = mid - 1;
+      if (rbeg(mid) <= r_begin) lo = mid; else hi = mid - 1;
     }
     cur_c.m = lo;
     cur_c.r = r_begin;
-    cur_c.beg = uniform_lds(s_rowbeg, lo);
-    cur_c.end = uniform_lds(s_rowbeg, lo + 1);
+    cur_c.beg = rbeg(lo);
+    cur_c.end = rbeg(lo + 1);
   }
   // groups of this wave (static split only)
   int iters = 0;
-  for (int mm = cur_c.m; !DYN && mm < count && uniform_lds(s_rowbeg, mm) < r_end; ++mm) {
-    const int lo = max(r_begin, uniform_lds(s_rowbeg, mm));
-    const int hi = min(r_end, uniform_lds(s_rowbeg, mm + 1));
+  for (int mm = cur_c.m; !DYN && mm < count && rbeg(mm) < r_end; ++mm) {
+    const int lo = max(r_begin, rbeg(mm));
+    const int hi = min(r_end, rbeg(mm + 1));
     if (hi > lo) iters += (hi - lo + R - 1) / R;
   }
 
@@ -987,16 +1034,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 
   auto advance = [&](int* m_out, int* rl_out) {
     if constexpr (DYN)
-      return next_group_dyn<R>(cur_c, r_end, claim, sr, C, s_rowbeg, count, lane, m_out, rl_out);
+      return next_group_dyn<R>(cur_c, r_end, claim, sr, C, log2C, rbeg, count, lane, m_out,
+                               rl_out);
     else
-      return next_group<R>(cur_c, r_end, s_rowbeg, count, m_out, rl_out);
+      return next_group<R>(cur_c, r_end, rbeg, count, m_out, rl_out);
   };
 
   // the first two groups
   int m0, rl0, m1, rl1;
   int len0 = advance(&m0, &rl0);
   m0 = __builtin_amdgcn_readfirstlane(m0);
-  const nf4_gemv_desc d0 = open_desc(descs, single, m0, len0, s_rowbeg, K);
+  const nf4_gemv_desc d0 = open_desc(descs, single, m0, len0, rbeg, K);
   int len1 = advance(&m1, &rl1);
   m1 = __builtin_amdgcn_readfirstlane(m1);
   LoadBufs lb0 = load_bufs(d0, K, log2bs, log2s2);
@@ -1010,22 +1058,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   LoadBufs lbL = lb0;
   OutBufs ob1 = ob0;
   if (len1 > 0 && m1 != m0) {
-    const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, s_rowbeg, K);
+    const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, rbeg, K);
     lbL = load_bufs(d1, K, log2bs, log2s2);
     ob1 = out_bufs<B>(d1);
     mL = m1;
   }
   load_wave_group<R, P>(g1, lbL, rl1, len1, wl, K, log2bs, log2s2);
 
-  for (int e = tid; e < 256 * kPairCopies; e += blockDim.x) {
-    const int b = e / kPairCopies;
-    const float ve = s_nf4[b >> 4], vo = s_nf4[b & 15];
-    const uint32_t hi = pack_pair<NF4_BF16>(ve, vo);
-    const float he = __builtin_bit_cast(float, hi << 16);
-    const float ho = __builtin_bit_cast(float, hi & 0xFFFF0000u);
-    const uint32_t lo2 = pack_pair<NF4_BF16>(ve - he, vo - ho);  // exact differences
-    s_pairs[e] = make_uint2(hi, lo2);
-  }
+  if (tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
+  build_pair_table(s_pairs, tid, blockDim.x);
   const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
   __syncthreads();
 
@@ -1035,7 +1076,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     m2 = __builtin_amdgcn_readfirstlane(m2);
     OutBufs ob2 = ob1;
     if (len2 > 0 && m2 != mL) {
-      const nf4_gemv_desc d2 = open_desc(descs, single, m2, len2, s_rowbeg, K);
+      const nf4_gemv_desc d2 = open_desc(descs, single, m2, len2, rbeg, K);
       lbL = load_bufs(d2, K, log2bs, log2s2);
       ob2 = out_bufs<B>(d2);
       mL = m2;
@@ -1071,7 +1112,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     // the next group starts a matrix with other activations: fetch them now
     // that the current ones are no longer needed
     if (len1 > 0 && m1 != m0) {
-      const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, s_rowbeg, K);
+      const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, rbeg, K);
       if (d1.x != x_cur) {
         load_wave_x<B, P>(xr, x_buf<B>(d1, K), wl, K);
         x_cur = d1.x;
@@ -1169,7 +1210,7 @@ __global__ __launch_bounds__(512) void gemv_vec_kernel(
     }
   }
   for (int i = threadIdx.x; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
-  if (threadIdx.x < 16) s_nf4[threadIdx.x] = kNF4[threadIdx.x];
+  if (threadIdx.x < 16) s_nf4[threadIdx.x] = nf4_value(threadIdx.x);
   __syncthreads();
   float a[R];
 #pragma unroll
@@ -1247,7 +1288,7 @@ __global__ __launch_bounds__(256) void gemv_any_kernel(
     int64_t N, int64_t K, int log2bs, int log2s2, const uint16_t* __restrict__ x,
     uint16_t* __restrict__ y) {
   __shared__ float s_nf4[16];
-  if (threadIdx.x < 16) s_nf4[threadIdx.x] = kNF4[threadIdx.x];
+  if (threadIdx.x < 16) s_nf4[threadIdx.x] = nf4_value(threadIdx.x);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -1370,10 +1411,14 @@ template <int B, int R, int P, int WPE>
 nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                        int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                        unsigned* sched, hipStream_t st) {
-  // one 512-lane workgroup per CU at two waves per SIMD, two at four
-  const int64_t max_wg = static_cast<int64_t>(device_cus()) * (WPE / 2);
+  // One row per wave at most one 512-lane workgroup per CU; a second one per
+  // CU (four waves per SIMD) only once every wave gets two rows or more: with
+  // one row per wave the younger workgroup mostly waits behind the older one
+  // (4096 x 4096 takes 9.4 us on two per CU, 7.3 us on one).
+  const int64_t cus = device_cus();
   const int64_t want = (static_cast<int64_t>(total_rows) + 7) / 8;
-  const int64_t grid = want < max_wg ? (want > 0 ? want : 1) : max_wg;
+  int64_t grid = want < cus ? (want > 0 ? want : 1) : cus;
+  if (WPE == 4 && want >= 4 * cus) grid = want < 2 * cus ? want : 2 * cus;
   const int64_t rows_per_wave = (static_cast<int64_t>(total_rows) + grid * 8 - 1) / (grid * 8);
   if (WPE == 4 && sched != nullptr && rows_per_wave >= 64) {
     int C = 4;

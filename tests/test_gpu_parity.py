@@ -73,6 +73,9 @@ EDGE = [
     (100_003, 64, 256), (2048 * 8 * 3 + 5, 64, 256), (4096, 8, 2), (4099, 16, 1),
     (5000, 32, 4), (5000, 128, 256), (3001, 4, 8), (3001, 2, 1), (777, 1, 4),
     (70_000, 1 << 14, 1), (1 << 16, 64, 1 << 12),
+    # tile-size boundaries of the vector path on 256 CUs: 1, 2 and 4 steps
+    # per lane, each with a ragged tail; blocksize 8 fills the scale table
+    (1_048_575, 64, 256), (1_500_001, 64, 256), (2_097_147, 64, 256), (2_100_003, 8, 2),
 ]
 
 

@@ -53,17 +53,22 @@ __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ absmax_
 // computes one absmax_real per first-level block into LDS (a 64-element block
 // is shared by 8 lanes) and decodes with the NF4 table in LDS (lanes index it
 // divergently; 16 distinct words never conflict on LDS banks).
+// The output, four times the bytes of the input, goes out with streaming
+// (non-temporal) stores.  Tiles are small (U = 4, fewer on inputs that would
+// not give every CU a tile) so that several workgroups per CU sit at
+// different phases and one's stores overlap another's loads.
 // Requirements (checked on the host): packed 4-byte aligned, out 16-byte
 // aligned, blocksize >= 8 so that a step never straddles a block.
 // ---------------------------------------------------------------------------
 constexpr int kDqThreads = 256;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int OUT, int U>
 __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
     const uint32_t* __restrict__ packed32, const uint8_t* __restrict__ packed8,
     const uint8_t* __restrict__ absmax_q, const uint16_t* __restrict__ absmax2,
     const uint16_t* __restrict__ code2, float offset, int64_t n, int log2bs, int log2s2,
-    uint4* __restrict__ out16, uint16_t* __restrict__ out2) {
+    u32x4* __restrict__ out16, uint16_t* __restrict__ out2) {
   __shared__ float s_nf4[16];
   __shared__ float s_code2[256];
   __shared__ float s_scale[kDqThreads * U];
@@ -120,12 +125,9 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
         const float vo = s_nf4[(wd >> (8 * j)) & 15u] * a;
         o[j] = pack_pair<OUT>(ve, vo);
       }
-      uint4 v;
-      v.x = o[0];
-      v.y = o[1];
-      v.z = o[2];
-      v.w = o[3];
-      out16[s] = v;
+      // streaming store: the kernel never reads its output back
+      const u32x4 v = {o[0], o[1], o[2], o[3]};
+      __builtin_nontemporal_store(v, out16 + s);
     } else if (s == full_steps) {
       // ragged tail: the last n % 8 elements, one at a time
       for (int64_t e = s * 8; e < n; ++e) {
@@ -359,6 +361,9 @@ struct LaneOffsets {
   uint32_t k0;
 };
 constexpr uint32_t kFar = 0x40000000u;  // added to an in-range offset: still < 2^31, never wraps
+// Cache-policy operand of the packed-weight loads: the nt (streaming) bit.
+// Every weight byte is read once per launch, so there is nothing to keep.
+constexpr int kStreamLoad = 2;
 
 template <int R>
 __device__ __forceinline__ void load_row_group(RowGroup<R>& rg, const LoadBufs& mb, int rl,
@@ -371,7 +376,7 @@ __device__ __forceinline__ void load_row_group(RowGroup<R>& rg, const LoadBufs& 
     const uint32_t srow = rr < len ? row * static_cast<uint32_t>(K >> 1) : kFar;
     const uint32_t sfar = rr < len ? 0u : kFar;
     const uint32_t blk = (row * static_cast<uint32_t>(K) + lo.k0) >> log2bs;
-    rg.pk[rr] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, lo.pk, srow, 0);
+    rg.pk[rr] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, lo.pk, srow, kStreamLoad);
     rg.q[rr] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
     rg.a2[rr] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, (blk >> log2s2) * 2u, sfar, 0);
   }
@@ -813,8 +818,9 @@ __device__ __forceinline__ void load_wave_group(WaveGroup<R, P>& g, const LoadBu
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint32_t blk = (row * static_cast<uint32_t>(K) + wl.c0[p]) >> log2bs;
-      g.pk[rr][p][0] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p], srow, 0);
-      g.pk[rr][p][1] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p] + 16u, srow, 0);
+      g.pk[rr][p][0] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p], srow, kStreamLoad);
+      g.pk[rr][p][1] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p] + 16u, srow,
+                                                              kStreamLoad);
       g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
       g.a2[rr][p] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, (blk >> log2s2) * 2u, sfar, 0);
     }
@@ -1368,12 +1374,15 @@ nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const 
   const bool vec = lbs >= 3 && aligned(packed, 4) && aligned(out, 16);
   if (vec) {
     const int64_t steps = (n >> 3) + ((n & 7) ? 1 : 0);
-    constexpr int U = 8;
+    const int64_t cus = device_cus();
+    const int U = steps >= cus * kDqThreads * 4 ? 4 : (steps >= cus * kDqThreads * 2 ? 2 : 1);
     const int64_t tiles = (steps + kDqThreads * U - 1) / (kDqThreads * U);
     if (tiles > 0x7FFFFFFF) return NF4_EUNSUPPORTED;
-    hipLaunchKernelGGL((dequant_vec_kernel<OUT, U>), dim3(static_cast<uint32_t>(tiles)),
-                       dim3(kDqThreads), 0, st, reinterpret_cast<const uint32_t*>(packed), packed,
-                       absmax_q, absmax2, code2, offset, n, lbs, ls2, reinterpret_cast<uint4*>(out),
+    const auto kernel = U == 4 ? dequant_vec_kernel<OUT, 4>
+                               : (U == 2 ? dequant_vec_kernel<OUT, 2> : dequant_vec_kernel<OUT, 1>);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(tiles)), dim3(kDqThreads), 0, st,
+                       reinterpret_cast<const uint32_t*>(packed), packed, absmax_q, absmax2, code2,
+                       offset, n, lbs, ls2, reinterpret_cast<u32x4*>(out),
                        reinterpret_cast<uint16_t*>(out));
   } else {
     const int64_t blocks = (n + 255) / 256;

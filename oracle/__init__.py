@@ -1,4 +1,5 @@
-"""CPU oracle for the NF4 double-quantization path (ctypes wrapper).
+"""CPU oracle for the NF4 double-quantization path and the single-level
+fp32-absmax format (ctypes wrapper).
 
 TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only tests/, the smoke check in
 __graft_entry__ and the CPU-baseline leg of bench.py may import this package.
@@ -53,6 +54,11 @@ def _load():
         "oracle_dequant": (None, [p, p, p, p, f32, i64, i32, i32, i32, i64, i64, p]),
         "oracle_dequant_at": (None, [p, p, p, p, f32, i32, i32, i32, p, i64, p]),
         "oracle_gemv": (None, [p, p, p, p, f32, i64, i64, i32, i32, p, i32, p, i64, p, p]),
+        "oracle_quantize_sl": (C.c_int, [p, i64, i32, p, p]),
+        "oracle_dequant_sl_f32": (None, [p, p, i64, i32, i64, i64, p]),
+        "oracle_dequant_sl": (None, [p, p, i64, i32, i32, i64, i64, p]),
+        "oracle_dequant_sl_at": (None, [p, p, i32, i32, p, i64, p]),
+        "oracle_gemv_sl": (None, [p, p, i64, i64, i32, p, i32, p, i64, p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -215,4 +221,72 @@ def gemv(q: Quantized, N: int, K: int, x_bf16: np.ndarray, rows: np.ndarray | No
     S = np.empty((B, nr), np.float64)
     _load().oracle_gemv(*_qargs(q), N, K, q.blocksize, q.s2_blocksize, _ptr(x), B, _ptr(rows),
                         nr, _ptr(y), _ptr(S))
+    return y, S
+
+
+@dataclass
+class QuantizedSL:
+    """The single-level NF4 format: one fp32 absmax per block, no second level."""
+    packed: np.ndarray      # uint8 [ceil(n/2)], even element in the high nibble
+    absmax: np.ndarray      # float32 [ceil(n/blocksize)]
+    n: int
+    blocksize: int = 64
+
+    @property
+    def nblocks(self) -> int:
+        return (self.n + self.blocksize - 1) // self.blocksize
+
+
+def quantize_sl(w: np.ndarray, blocksize: int = 64) -> QuantizedSL:
+    w = np.ascontiguousarray(w, np.float32).reshape(-1)
+    n = w.size
+    packed = np.empty((n + 1) // 2, np.uint8)
+    absmax = np.empty((n + blocksize - 1) // blocksize, np.float32)
+    rc = _load().oracle_quantize_sl(_ptr(w), n, blocksize, _ptr(packed), _ptr(absmax))
+    if rc != 0:
+        raise RuntimeError(f"oracle_quantize_sl failed: {rc}")
+    return QuantizedSL(packed, absmax, n, blocksize)
+
+
+def dequant_sl_f32(q: QuantizedSL, e0: int = 0, e1: int | None = None) -> np.ndarray:
+    e1 = q.n if e1 is None else min(e1, q.n)
+    out = np.empty(max(e1 - e0, 0), np.float32)
+    _load().oracle_dequant_sl_f32(_ptr(q.packed), _ptr(q.absmax), q.n, q.blocksize, e0, e1,
+                                  _ptr(out))
+    return out
+
+
+def dequant_sl(q: QuantizedSL, out_dtype: int = BF16, e0: int = 0,
+               e1: int | None = None) -> np.ndarray:
+    """16-bit output bits (uint16) of elements [e0, e1)."""
+    e1 = q.n if e1 is None else min(e1, q.n)
+    out = np.empty(max(e1 - e0, 0), np.uint16)
+    _load().oracle_dequant_sl(_ptr(q.packed), _ptr(q.absmax), q.n, q.blocksize, int(out_dtype),
+                              e0, e1, _ptr(out))
+    return out
+
+
+def dequant_sl_at(q: QuantizedSL, idx: np.ndarray, out_dtype: int = BF16) -> np.ndarray:
+    idx = np.ascontiguousarray(idx, np.int64)
+    out = np.empty(idx.size, np.uint16)
+    _load().oracle_dequant_sl_at(_ptr(q.packed), _ptr(q.absmax), q.blocksize, int(out_dtype),
+                                 _ptr(idx), idx.size, _ptr(out))
+    return out
+
+
+def gemv_sl(q: QuantizedSL, N: int, K: int, x_bf16: np.ndarray,
+            rows: np.ndarray | None = None):
+    """fp64 reference (y, S) for the single-level format; as gemv()."""
+    assert N * K == q.n
+    x = np.ascontiguousarray(x_bf16, np.uint16).reshape(-1, K)
+    B = x.shape[0]
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, np.int64)
+        nr = rows.size
+    else:
+        nr = N
+    y = np.empty((B, nr), np.float64)
+    S = np.empty((B, nr), np.float64)
+    _load().oracle_gemv_sl(_ptr(q.packed), _ptr(q.absmax), N, K, q.blocksize, _ptr(x), B,
+                           _ptr(rows), nr, _ptr(y), _ptr(S))
     return y, S

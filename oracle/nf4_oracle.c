@@ -48,6 +48,11 @@
  *  - code2 (linear variant): fp16 nearest to -1 + 2 i / 255, i = 0..255.
  *  - odd n: the pad (low) nibble of the last byte is written as 0, ignored
  *    when reading.
+ *  - single-level format ([quanttax] "量化的标准预期": one fp32 absmax per
+ *    block of 64; "Kernel 实现": the fused kernel multiplies the fp32 code
+ *    value by the block's fp32 scale): value = f32(NF4[idx] * absmax[block]),
+ *    one rounding; the quantizer is the level-1 step of the double-quantized
+ *    one (true block absmax, nearest NF4 code, ties to the smaller index).
  */
 #include <math.h>
 #include <stdint.h>
@@ -363,6 +368,105 @@ void oracle_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t*
                 const int64_t e = r * K + k;
                 const float a = block_scale(absmax_q, absmax2, code2, offset, e / bs, s2);
                 const float v = NF4_TABLE[nibble_at(packed, e)] * a;
+                const double p = (double)v * xd[(int64_t)b * K + k];
+                acc += p;
+                mag += fabs(p);
+            }
+            if (y) y[(int64_t)b * nrows + j] = acc;
+            if (S) S[(int64_t)b * nrows + j] = mag;
+        }
+    }
+    free(xd);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Single-level format: one fp32 absmax per block, no second level            */
+/* ([quanttax] "量化的标准预期" and "Kernel 实现")                           */
+/* ------------------------------------------------------------------------ */
+
+/* Quantize fp32 weights w[0..n) with one fp32 absmax per block of bs
+ * elements.  packed: ceil(n/2) bytes (even element in the high nibble);
+ * absmax: ceil(n/bs) fp32 values.  Returns 0 on success. */
+int oracle_quantize_sl(const float* w, int64_t n, int32_t bs, uint8_t* packed, float* absmax) {
+    if (n < 0 || bs <= 0) return 1;
+    const int64_t nb = (n + bs - 1) / bs;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nb; ++b) {
+        float m = 0.0f;
+        const int64_t e1 = (b + 1) * bs < n ? (b + 1) * bs : n;
+        for (int64_t e = b * bs; e < e1; ++e) {
+            const float a = fabsf(w[e]);
+            if (a > m) m = a;
+        }
+        absmax[b] = m;
+    }
+    const int64_t nbytes = (n + 1) / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nbytes; ++i) {
+        int idx[2] = {0, 0};
+        for (int h = 0; h < 2; ++h) {
+            const int64_t e = 2 * i + h;
+            if (e >= n) continue; /* pad nibble stays 0 */
+            const float m = absmax[e / bs];
+            idx[h] = (m == 0.0f) ? 7 : nearest_nf4(w[e] / m);
+        }
+        packed[i] = (uint8_t)((idx[0] << 4) | idx[1]);
+    }
+    return 0;
+}
+
+/* Unrounded fp32 values of elements [e0, e1): NF4[idx] * absmax[block]. */
+void oracle_dequant_sl_f32(const uint8_t* packed, const float* absmax, int64_t n, int32_t bs,
+                           int64_t e0, int64_t e1, float* out) {
+    if (e1 > n) e1 = n;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = e0; e < e1; ++e) {
+        const float v = NF4_TABLE[nibble_at(packed, e)] * absmax[e / bs];
+        out[e - e0] = v;
+    }
+}
+
+/* 16-bit output (0 = bf16, 1 = fp16) of elements [e0, e1). */
+void oracle_dequant_sl(const uint8_t* packed, const float* absmax, int64_t n, int32_t bs,
+                       int32_t out_dtype, int64_t e0, int64_t e1, uint16_t* out) {
+    if (e1 > n) e1 = n;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = e0; e < e1; ++e) {
+        const float v = NF4_TABLE[nibble_at(packed, e)] * absmax[e / bs];
+        out[e - e0] = out_dtype == 0 ? oracle_bf16_from_float(v) : oracle_f16_from_float(v);
+    }
+}
+
+/* The same for the elements listed in idx[0..m). */
+void oracle_dequant_sl_at(const uint8_t* packed, const float* absmax, int32_t bs,
+                          int32_t out_dtype, const int64_t* idx, int64_t m, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        const int64_t e = idx[i];
+        const float v = NF4_TABLE[nibble_at(packed, e)] * absmax[e / bs];
+        out[i] = out_dtype == 0 ? oracle_bf16_from_float(v) : oracle_f16_from_float(v);
+    }
+}
+
+/* fp64 reference y[b][r] = sum_k v[r][k] * x[b][k] (k ascending) and
+ * S[b][r] = sum_k |v x| for the single-level format; v is the unrounded fp32
+ * value NF4[idx] * absmax[block].  Layout and arguments as oracle_gemv. */
+void oracle_gemv_sl(const uint8_t* packed, const float* absmax, int64_t N, int64_t K, int32_t bs,
+                    const uint16_t* x, int32_t B, const int64_t* rows, int64_t nrows, double* y,
+                    double* S) {
+    if (!rows) nrows = N;
+    (void)N;
+    double* xd = (double*)malloc((size_t)B * (size_t)K * sizeof(double));
+    if (!xd) return;
+    for (int64_t i = 0; i < (int64_t)B * K; ++i) xd[i] = oracle_bf16_to_double(x[i]);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t j = 0; j < nrows; ++j) {
+        const int64_t r = rows ? rows[j] : j;
+        for (int32_t b = 0; b < B; ++b) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t e = r * K + k;
+                const float v = NF4_TABLE[nibble_at(packed, e)] * absmax[e / bs];
                 const double p = (double)v * xd[(int64_t)b * K + k];
                 acc += p;
                 mag += fabs(p);

@@ -56,7 +56,8 @@ def bf16_bits_torch(a: np.ndarray) -> np.ndarray:
 
 
 def f16_bits_numpy(a: np.ndarray) -> np.ndarray:
-    return np.ascontiguousarray(a, np.float32).astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):   # overflow to +-inf is the expected result
+        return np.ascontiguousarray(a, np.float32).astype(np.float16).view(np.uint16)
 
 
 def make_q(packed, absmax_q, absmax2, code2, offset, n, bs, s2):
@@ -439,4 +440,155 @@ def test_gemv_matches_float64_matmul(N, K, B):
     assert np.allclose(S, np.abs(xf) @ np.abs(W).T, rtol=1e-12)
     rows = np.array([N - 1, 0, N // 2])
     y2, S2 = oracle.gemv(q, N, K, xb, rows)
+    assert np.array_equal(y2, y[:, rows]) and np.array_equal(S2, S[:, rows])
+
+
+# ----------------------------------------------------------------------------
+# Single-level format (one fp32 absmax per block, no second level)
+# ----------------------------------------------------------------------------
+
+
+def make_sl(packed, absmax, n, bs):
+    return oracle.QuantizedSL(np.ascontiguousarray(packed, np.uint8),
+                              np.ascontiguousarray(absmax, np.float32), n, bs)
+
+
+def test_sl_exhaustive_byte_decode(page_table):
+    """absmax = 1 everywhere: every packed byte decodes to (NF4[hi], NF4[lo])
+    of the page table, the even element from the high nibble."""
+    q = make_sl(np.arange(256, dtype=np.uint8), np.ones(8, np.float32), 512, 64)
+    v = oracle.dequant_sl_f32(q)
+    expect = np.empty(512, np.float32)
+    expect[0::2] = page_table[np.arange(256) >> 4]
+    expect[1::2] = page_table[np.arange(256) & 15]
+    assert np.array_equal(v.view(np.uint32), expect.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,bs", [(4096, 64), (1001, 64), (777, 32), (65, 64), (2, 64), (300, 2),
+                                  (513, 128), (5000, 256)])
+def test_sl_block_index_closed_form(n, bs):
+    """Every code 15 (value +1) and absmax[b] = b + 1/4: element e reads exactly
+    e // bs + 1/4; code 0 (-1) gives the negation and code 7 (+0) zeros."""
+    nb = (n + bs - 1) // bs
+    absmax = (np.arange(nb) + 0.25).astype(np.float32)
+    packed = np.full((n + 1) // 2, 0xFF, np.uint8)
+    v = oracle.dequant_sl_f32(make_sl(packed, absmax, n, bs)).astype(np.float64)
+    expect = np.arange(n) // bs + 0.25
+    assert np.array_equal(v, expect)
+    v0 = oracle.dequant_sl_f32(make_sl(np.zeros_like(packed), absmax, n, bs)).astype(np.float64)
+    assert np.array_equal(v0, -expect)
+    v7 = oracle.dequant_sl_f32(make_sl(np.full_like(packed, 0x77), absmax, n, bs))
+    assert np.all(v7.view(np.uint32) == 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_sl_dequant_matches_exact_rational(seed, page_table):
+    """Exact rationals: the product NF4[idx] * absmax rounded once to fp32
+    (subnormal range included); the 16-bit outputs are numpy's (fp16) and
+    torch's (bf16) RNE casts of that value."""
+    rng = np.random.default_rng(300 + seed)
+    n, bs = 1501, 32
+    nb = (n + bs - 1) // bs
+    packed = rng.integers(0, 256, (n + 1) // 2).astype(np.uint8)
+    absmax = (rng.standard_normal(nb) * 2.0 ** rng.integers(-140, 20, nb)).astype(np.float32)
+    q = make_sl(packed, absmax, n, bs)
+    got = oracle.dequant_sl_f32(q)
+    nib = np.empty(2 * packed.size, np.int64)
+    nib[0::2] = packed >> 4
+    nib[1::2] = packed & 15
+    expect = np.array([float(round_fraction(Fraction(float(page_table[nib[e]]))
+                                            * Fraction(float(absmax[e // bs]))))
+                       for e in range(n)], np.float32)
+    # a zero product carries the XOR of the operands' signs (+0 * negative = -0)
+    neg = np.signbit(page_table[nib[:n]]) ^ np.signbit(absmax[np.arange(n) // bs])
+    expect = np.where(expect == 0, np.where(neg, np.float32(-0.0), np.float32(0.0)), expect)
+    assert np.any((expect == 0) & neg)
+    assert np.array_equal(got.view(np.uint32), expect.view(np.uint32))
+    assert np.array_equal(oracle.dequant_sl(q, oracle.BF16), bf16_bits_torch(expect))
+    assert np.array_equal(oracle.dequant_sl(q, oracle.FP16), f16_bits_numpy(expect))
+
+
+def test_sl_reduces_to_double_quant():
+    """With absmax[b] set to the double-quantized tensor's absmax_real (formed
+    here with numpy float32 operations: IEEE product, then IEEE sum), the
+    single-level dequant equals the double-quantized one bit for bit."""
+    q = oracle.quantize(synth.weights(41, 64 * 256 * 2 + 640, outliers=True), 64, 256)
+    c2 = q.code2.view(np.float16).astype(np.float32)
+    a2 = q.absmax2.view(np.float16).astype(np.float32)
+    blk = np.arange(q.nblocks)
+    a_real = (c2[q.absmax_q] * a2[blk // q.s2_blocksize]).astype(np.float32) + np.float32(q.offset)
+    assert a_real.dtype == np.float32
+    sl = make_sl(q.packed, a_real, q.n, q.blocksize)
+    for dt in (oracle.BF16, oracle.FP16):
+        assert np.array_equal(oracle.dequant_sl(sl, dt), oracle.dequant(q, dt))
+    assert np.array_equal(oracle.dequant_sl_f32(sl).view(np.uint32),
+                          oracle.dequant_f32(q).view(np.uint32))
+
+
+def test_sl_sampled_and_ranges_agree():
+    q = oracle.quantize_sl(synth.weights(43, 10_007), 64)
+    full = oracle.dequant_sl(q, oracle.FP16)
+    idx = np.random.default_rng(3).integers(0, q.n, 500)
+    assert np.array_equal(oracle.dequant_sl_at(q, idx, oracle.FP16), full[idx])
+    assert np.array_equal(oracle.dequant_sl(q, oracle.FP16, 1234, 5678), full[1234:5678])
+
+
+@pytest.mark.parametrize("n,bs,seed", [(4096, 64, 1), (3001, 64, 2), (255, 32, 3), (1000, 128, 4)])
+def test_sl_quantizer_brute_force(n, bs, seed, page_table):
+    w = synth.weights(seed, n, outliers=True)
+    q = oracle.quantize_sl(w, bs)
+    nb = (n + bs - 1) // bs
+    wp = np.concatenate([w, np.zeros(nb * bs - n, np.float32)]).reshape(nb, bs)
+    absmax = np.abs(wp).max(axis=1)
+    assert np.array_equal(q.absmax, absmax)
+    r = w / np.repeat(absmax, bs)[:n]
+    d = np.abs(r[:, None] - page_table[None, :])
+    assert np.array_equal(_nibbles(q), np.argmin(d, axis=1))
+    if n % 2:
+        assert q.packed[-1] & 15 == 0
+
+
+def test_sl_quantizer_roundtrip_and_gridpoints():
+    """|w - value| <= half the largest NF4 gap times absmax (plus the fp32
+    rounding of the product); weights on the grid NF4[j] * A come back as j."""
+    w = synth.weights(22, 1 << 15, outliers=True)
+    q = oracle.quantize_sl(w)
+    t = oracle.nf4_table().astype(np.float64)
+    half_gap = np.diff(t).max() / 2
+    absmax = np.repeat(q.absmax, 64)[: q.n].astype(np.float64)
+    v = oracle.dequant_sl_f32(q).astype(np.float64)
+    assert np.all(np.abs(w - v) <= half_gap * absmax * (1 + 2 ** -20) + np.abs(v) * 2 ** -24)
+    rng = np.random.default_rng(10)
+    A = np.float32(0.01) + rng.random(100, dtype=np.float32)
+    j = rng.integers(0, 16, (100, 64))
+    j[:, 0] = 0                       # -A in every block: absmax is A
+    wg = (oracle.nf4_table()[j] * A[:, None]).astype(np.float32).reshape(-1)
+    assert np.array_equal(_nibbles(oracle.quantize_sl(wg)), j.reshape(-1))
+    z = oracle.quantize_sl(np.zeros(999, np.float32))
+    assert np.all(z.packed[:-1] == 0x77) and z.packed[-1] == 0x70 and np.all(z.absmax == 0)
+
+
+def test_sl_gemv_one_hot_reproduces_columns():
+    N, K = 40, 256
+    q = oracle.quantize_sl(synth.weights(5, N * K), 64)
+    W = oracle.dequant_sl_f32(q).reshape(N, K)
+    for k in (0, 1, 64, 255):
+        x = np.zeros((1, K), np.float32)
+        x[0, k] = 1.0
+        y, S = oracle.gemv_sl(q, N, K, synth.to_bf16_bits(x))
+        assert np.array_equal(y[0], W[:, k].astype(np.float64))
+        assert np.array_equal(S[0], np.abs(W[:, k]).astype(np.float64))
+
+
+@pytest.mark.parametrize("N,K,B,bs", [(64, 512, 1, 64), (33, 1536, 4, 128), (7, 128, 8, 32)])
+def test_sl_gemv_matches_float64_matmul(N, K, B, bs):
+    q = oracle.quantize_sl(synth.weights(N + K + 1, N * K), bs)
+    W = oracle.dequant_sl_f32(q).reshape(N, K).astype(np.float64)
+    xb = synth.activations(8, B, K)
+    xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    y, S = oracle.gemv_sl(q, N, K, xb)
+    assert np.allclose(y, xf @ W.T, rtol=1e-12, atol=1e-12 * np.abs(xf) @ np.abs(W).T)
+    assert np.allclose(S, np.abs(xf) @ np.abs(W).T, rtol=1e-12)
+    rows = np.array([N - 1, 0])
+    y2, S2 = oracle.gemv_sl(q, N, K, xb, rows)
     assert np.array_equal(y2, y[:, rows]) and np.array_equal(S2, S[:, rows])

@@ -112,8 +112,10 @@ nf4_status nf4_dequant(const uint8_t* packed, const uint8_t* absmax_q, const uin
  *  y             : device bf16 bits [batch][N], row-major; each output is
  *                  the fp32 sum rounded to nearest even.
  *  stream        : hipStream_t.
- * Weights are used at full fp32 precision (never rounded to 16 bits) and the
- * sum is accumulated in fp32: each output is the bf16 rounding (nearest even)
+ * Weights are never rounded to 16 bits: each NF4 value enters the products
+ * as the sum of two bf16 values (within 2^-16 of its fp32 value), the block
+ * scale is applied in fp32, and the sum is accumulated in fp32: each output
+ * is the bf16 rounding (nearest even)
  * of a value within 2^-14 * sum_k |w x| of the exact sum, so
  * |y - exact| <= 2^-8 |exact| + (1 + 2^-8) 2^-14 sum_k |w x|.  Deterministic:
  * the summation order depends only on N, K and batch.
@@ -124,6 +126,50 @@ nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16
                     const uint16_t* code2, float offset, int64_t N, int64_t K,
                     int32_t blocksize, int32_t s2_blocksize, const uint16_t* x, int32_t batch,
                     uint16_t* y, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Single-level format: one fp32 absmax per block, no second level
+ * ---------------------------------------------------------------------------
+ * The same packed codes with a plain fp32 scale per block instead of the
+ * double-quantized (absmax_q, absmax2, code2, offset):
+ *
+ *  absmax    fp32[ceil(n/blocksize)]   scale of each block of `blocksize`
+ *                                      consecutive elements (4-byte aligned)
+ *  value     = fp32(NF4[index(e)] * absmax[e / blocksize])   (one rounding)
+ *
+ * This is the format of [quanttax] "量化的标准预期" (one fp32 absmax per
+ * block of 64) and of the fused kernel in its "Kernel 实现", which multiplies
+ * the fp32 code value by the block's fp32 scale.  The kernels, tolerances and
+ * conventions are those of the double-quantized entry points.
+ */
+
+/*
+ * nf4_dequant_absmax32 -- standalone dequant of the single-level format.
+ *
+ *  packed        : device, ceil(n/2) bytes (nibble order as above).
+ *  absmax        : device fp32 [ceil(n/blocksize)], 4-byte aligned.
+ *  n, blocksize, out, out_dtype, stream : as for nf4_dequant.
+ * Returns NF4_EINVAL for a NULL pointer with n > 0, a misaligned absmax,
+ * n < 0, a block size that is not a power of two in [1, 2^30], or an unknown
+ * dtype; NF4_EUNSUPPORTED for n >= 2^40.
+ */
+nf4_status nf4_dequant_absmax32(const uint8_t* packed, const float* absmax, int64_t n,
+                                int32_t blocksize, void* out, int32_t out_dtype, void* stream);
+
+/*
+ * nf4_gemv_absmax32 -- fused dequant + matrix-vector product (batch 1..8) for
+ * the single-level format: y[b][r] = sum_k value(r*K + k) * x[b][k].
+ *
+ *  packed, absmax : the single-level format of W [N][K] flattened row-major
+ *                  (blocks follow the flat index r*K + k).
+ *  N, K, blocksize, x, batch, y, stream : as for nf4_gemv.
+ * Same accumulation and tolerance as nf4_gemv.  Returns NF4_EINVAL as
+ * nf4_gemv does, and for a misaligned absmax.
+ */
+nf4_status nf4_gemv_absmax32(const uint8_t* packed, const float* absmax, int64_t N, int64_t K,
+                             int32_t blocksize, const uint16_t* x, int32_t batch, uint16_t* y,
+                             void* stream);
 
 /*
  * One matrix of a grouped GEMV (64 bytes; all pointers are device pointers).

@@ -81,3 +81,21 @@ def gemv_within_tolerance(y_gpu: np.ndarray, y_ref: np.ndarray, S: np.ndarray):
     worst = float(np.max(np.where(bound > 0, err / np.where(bound > 0, bound, 1), 0))) \
         if err.size else 0.0
     return ok, worst
+
+
+ONE_HOT_REL = 2.0 ** -15
+
+
+def one_hot_ok(y: np.ndarray, w_col: np.ndarray) -> bool:
+    """For x = e_k the GEMV output of row r is a single product: the kernels
+    that decode through the bf16 pair table feed each NF4 value as the sum of
+    two bf16 values (within 2^-16 of its fp32 value), times the block scale
+    in fp32.  So y[r] must be the bf16 rounding (nearest even) of a real
+    within 2^-15 |W[r][k]| of the fp32 weight W[r][k] -- far tighter than one
+    bf16 step, so a wrong row, column or batch index still fails."""
+    import oracle
+    w = w_col.astype(np.float64)
+    d = ONE_HOT_REL * np.abs(w)
+    lo = bf16_to_f64(oracle.bf16_from_f64(w - d))
+    hi = bf16_to_f64(oracle.bf16_from_f64(w + d))
+    return bool(np.all((y >= lo) & (y <= hi)))

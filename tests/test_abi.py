@@ -133,3 +133,32 @@ def test_gemv_grouped_rejects_bad_arguments(lib, kw):
 
 def test_gemv_grouped_empty_is_a_no_op(lib):
     assert lib.nf4_gemv_grouped(None, 0, 0, 64, 64, 256, None, 1, None, 0, None) == 0
+
+
+def _dq32(lib, n=16, bs=64, dtype=0, packed=FAKE, absmax=FAKE, out=FAKE):
+    return lib.nf4_dequant_absmax32(packed, absmax, n, bs, out, dtype, None)
+
+
+def _gv32(lib, N=4, K=64, bs=64, batch=1, x=FAKE, y=FAKE, packed=FAKE, absmax=FAKE):
+    return lib.nf4_gemv_absmax32(packed, absmax, N, K, bs, x, batch, y, None)
+
+
+@pytest.mark.parametrize("kw", [dict(n=-1), dict(bs=0), dict(bs=48), dict(bs=2 ** 31 - 1),
+                                dict(dtype=2), dict(packed=None), dict(absmax=None),
+                                dict(out=None), dict(absmax=C.c_void_p(0x1002))])
+def test_dequant_absmax32_rejects_bad_arguments(lib, kw):
+    assert _dq32(lib, **kw) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(N=-1), dict(K=-2), dict(K=63), dict(batch=0), dict(batch=9),
+                                dict(bs=24), dict(x=None), dict(y=None), dict(packed=None),
+                                dict(absmax=None), dict(absmax=C.c_void_p(0x1001))])
+def test_gemv_absmax32_rejects_bad_arguments(lib, kw):
+    assert _gv32(lib, **kw) == 1
+
+
+def test_absmax32_empty_and_oversized(lib):
+    assert lib.nf4_dequant_absmax32(None, None, 0, 64, None, 0, None) == 0
+    assert lib.nf4_gemv_absmax32(None, None, 0, 64, 64, None, 1, None, None) == 0
+    assert _dq32(lib, n=1 << 41) == 2
+    assert _gv32(lib, N=1 << 30, K=1 << 12) == 2

@@ -2,7 +2,8 @@
 AMD Instinct MI355X (gfx950).
 
 The compute lives in libnf4.so (HIP, C ABI in include/nf4.h); this package is
-its Python binding.  See nf4_dequant / nf4_gemv.
+its Python binding.  See nf4_dequant / nf4_gemv (double-quantized format) and
+nf4_dequant_absmax32 / nf4_gemv_absmax32 (one fp32 absmax per block).
 """
 from ._binding import (  # noqa: F401
     EXPORTED,
@@ -20,7 +21,9 @@ from ._binding import (  # noqa: F401
     load,
     nf4_code2_linear,
     nf4_dequant,
+    nf4_dequant_absmax32,
     nf4_gemv,
+    nf4_gemv_absmax32,
     nf4_quantize,
     status_string,
 )

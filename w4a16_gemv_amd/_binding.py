@@ -19,7 +19,8 @@ NF4_OK, NF4_EINVAL, NF4_EUNSUPPORTED, NF4_EHIP = 0, 1, 2, 3
 NF4_BF16, NF4_FP16 = 0, 1
 
 EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv",
-            "nf4_gemv_grouped", "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
+            "nf4_dequant_absmax32", "nf4_gemv_absmax32", "nf4_gemv_grouped",
+            "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
             "nf4_quantize")
 
 _lib = None
@@ -49,6 +50,10 @@ def load() -> C.CDLL:
     lib.nf4_dequant.argtypes = [p, p, p, p, f32, i64, i32, i32, p, i32, p]
     lib.nf4_gemv.restype = C.c_int
     lib.nf4_gemv.argtypes = [p, p, p, p, f32, i64, i64, i32, i32, p, i32, p, p]
+    lib.nf4_dequant_absmax32.restype = C.c_int
+    lib.nf4_dequant_absmax32.argtypes = [p, p, i64, i32, p, i32, p]
+    lib.nf4_gemv_absmax32.restype = C.c_int
+    lib.nf4_gemv_absmax32.argtypes = [p, p, i64, i64, i32, p, i32, p, p]
     lib.nf4_gemv_grouped.restype = C.c_int
     lib.nf4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, i32, p, C.c_size_t, p]
     lib.nf4_gemv_sched_size.restype = C.c_size_t
@@ -127,6 +132,24 @@ def nf4_gemv(packed, absmax_q, absmax2, code2, offset: float, N: int, K: int, x:
     """y[b][r] = sum_k W[r][k] x[b][k] with W the NF4 tensor viewed as [N][K].
 
     x: bf16 [batch][K] (or [K]); returns y bf16 [batch][N] (or [N])."""
+    xb, batch, y, squeeze = _gemv_io(x, N, K, y)
+    nbytes, nb, ng = format_sizes(int(N) * int(K), int(blocksize), int(s2_blocksize))
+    args = (_dev(packed, "packed", _U8, nbytes), _dev(absmax_q, "absmax_q", _U8, nb),
+            _dev(absmax2, "absmax2", _HALF_BITS, ng), _dev(code2, "code2", _HALF_BITS, 256))
+    px = _dev(xb, "x", _BF16_BITS, batch * int(K))
+    py = _dev(y, "y", _BF16_BITS, batch * int(N))
+    st = load().nf4_gemv(*args, C.c_float(offset), int(N), int(K), int(blocksize),
+                         int(s2_blocksize), px, int(batch), py, _stream(y))
+    _check("nf4_gemv", st)
+    return y.view(int(N)) if squeeze and y.dim() == 2 else y
+
+
+_F32 = (torch.float32,)
+
+
+def _gemv_io(x: torch.Tensor, N: int, K: int, y: torch.Tensor | None):
+    """Shape checks shared by the GEMV wrappers: (x as [batch][K], batch, y,
+    whether to return y as 1-D)."""
     if x.dim() not in (1, 2):
         raise ValueError(f"x must be 1-D or 2-D, got shape {tuple(x.shape)}")
     squeeze = x.dim() == 1
@@ -136,16 +159,46 @@ def nf4_gemv(packed, absmax_q, absmax2, code2, offset: float, N: int, K: int, x:
         raise ValueError(f"x width {xb.shape[1]} does not match K={K}")
     if not 1 <= batch <= 8:
         raise ValueError(f"batch must be 1..8, got {batch}")
-    nbytes, nb, ng = format_sizes(int(N) * int(K), int(blocksize), int(s2_blocksize))
     if y is None:
         y = torch.empty(batch, int(N), dtype=torch.bfloat16, device=x.device)
-    args = (_dev(packed, "packed", _U8, nbytes), _dev(absmax_q, "absmax_q", _U8, nb),
-            _dev(absmax2, "absmax2", _HALF_BITS, ng), _dev(code2, "code2", _HALF_BITS, 256))
+    return xb, batch, y, squeeze
+
+
+def nf4_dequant_absmax32(packed, absmax, n: int, blocksize: int = 64,
+                         out: torch.Tensor | None = None,
+                         out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Dequantize n elements of the single-level format (fp32 absmax per
+    block) to bf16 / fp16 (returns `out`, shape [n])."""
+    nbytes = (int(n) + 1) // 2
+    nb = -(-int(n) // int(blocksize))
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float16")
+    if out is None:
+        out = torch.empty(int(n), dtype=out_dtype, device=packed.device)
+    if out.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("out must be bfloat16 or float16")
+    code = NF4_BF16 if out.dtype == torch.bfloat16 else NF4_FP16
+    pp = _dev(packed, "packed", _U8, nbytes)
+    pa = _dev(absmax, "absmax", _F32, nb)
+    po = _dev(out, "out", (out.dtype,), int(n))
+    st = load().nf4_dequant_absmax32(pp, pa, int(n), int(blocksize), po, code, _stream(out))
+    _check("nf4_dequant_absmax32", st)
+    return out
+
+
+def nf4_gemv_absmax32(packed, absmax, N: int, K: int, x: torch.Tensor, blocksize: int = 64,
+                      y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[b][r] = sum_k W[r][k] x[b][k] for W in the single-level format viewed
+    as [N][K].  x: bf16 [batch][K] (or [K]); returns y bf16 [batch][N] (or [N])."""
+    xb, batch, y, squeeze = _gemv_io(x, N, K, y)
+    n = int(N) * int(K)
+    pp = _dev(packed, "packed", _U8, (n + 1) // 2)
+    pa = _dev(absmax, "absmax", _F32, -(-n // int(blocksize)))
     px = _dev(xb, "x", _BF16_BITS, batch * int(K))
     py = _dev(y, "y", _BF16_BITS, batch * int(N))
-    st = load().nf4_gemv(*args, C.c_float(offset), int(N), int(K), int(blocksize),
-                         int(s2_blocksize), px, int(batch), py, _stream(y))
-    _check("nf4_gemv", st)
+    st = load().nf4_gemv_absmax32(pp, pa, int(N), int(K), int(blocksize), px, int(batch), py,
+                                  _stream(y))
+    _check("nf4_gemv_absmax32", st)
     return y.view(int(N)) if squeeze and y.dim() == 2 else y
 
 

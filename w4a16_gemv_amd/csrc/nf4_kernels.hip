@@ -27,15 +27,36 @@ namespace {
 
 using namespace nf4dev;
 
-// absmax_real of one first-level block: fp32 product, then fp32 sum.
+// Where a block's scale comes from (a template parameter of every kernel).
+// kFmtDouble: the double-quantized format, absmax_real = fp32(code2[absmax_q
+// [block]] * absmax2[group]) + offset.  kFmtAbsmax32: one fp32 absmax per
+// block and no second level; the absmax_q argument then carries that fp32
+// array and absmax2, code2 and offset are not used.
+constexpr int kFmtDouble = 0;
+constexpr int kFmtAbsmax32 = 1;
+
+// Register type of a block's scale bits as loaded: the absmax_q byte, or the
+// fp32 absmax.
+template <int FMT>
+struct ScaleBits { using type = uint8_t; };
+template <>
+struct ScaleBits<kFmtAbsmax32> { using type = uint32_t; };
+
+// absmax_real of one first-level block: fp32 product, then fp32 sum (or the
+// stored fp32 absmax).
+template <int FMT>
 __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ absmax_q,
                                              const uint16_t* __restrict__ absmax2,
                                              const uint16_t* __restrict__ code2, float offset,
                                              int64_t blk, int log2s2) {
-  const float c = f16_to_f32(code2[absmax_q[blk]]);
-  const float g = f16_to_f32(absmax2[blk >> log2s2]);
-  const float s = c * g;
-  return s + offset;
+  if constexpr (FMT == kFmtAbsmax32) {
+    return reinterpret_cast<const float*>(absmax_q)[blk];
+  } else {
+    const float c = f16_to_f32(code2[absmax_q[blk]]);
+    const float g = f16_to_f32(absmax2[blk >> log2s2]);
+    const float s = c * g;
+    return s + offset;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -63,7 +84,7 @@ __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ absmax_
 constexpr int kDqThreads = 256;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int OUT, int U>
+template <int OUT, int U, int FMT = kFmtDouble>
 __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
     const uint32_t* __restrict__ packed32, const uint8_t* __restrict__ packed8,
     const uint8_t* __restrict__ absmax_q, const uint16_t* __restrict__ absmax2,
@@ -83,7 +104,7 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
     const int64_t s = step0 + u * kDqThreads + t;
     w[u] = s < full_steps ? packed32[s] : 0u;
   }
-  const uint16_t c2 = code2[t];
+  const uint16_t c2 = FMT == kFmtDouble ? code2[t] : uint16_t(0);
   const int64_t e_begin = step0 * 8;
   const int64_t e_end = (step0 + kDqThreads * U) * 8 < n ? (step0 + kDqThreads * U) * 8 : n;
   const int64_t blk0 = e_begin >> log2bs;
@@ -93,20 +114,28 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int i = t + u * kDqThreads;
-    qv[u] = i < nblk ? absmax_q[blk0 + i] : 0u;
-    gv[u] = i < nblk ? absmax2[(blk0 + i) >> log2s2] : uint16_t(0);
+    if constexpr (FMT == kFmtAbsmax32) {
+      qv[u] = i < nblk ? reinterpret_cast<const uint32_t*>(absmax_q)[blk0 + i] : 0u;
+    } else {
+      qv[u] = i < nblk ? absmax_q[blk0 + i] : 0u;
+      gv[u] = i < nblk ? absmax2[(blk0 + i) >> log2s2] : uint16_t(0);
+    }
   }
 
   // 2. tables, then one absmax_real per block
-  s_code2[t] = f16_to_f32(c2);
+  if constexpr (FMT == kFmtDouble) s_code2[t] = f16_to_f32(c2);
   if (t < 16) s_nf4[t] = nf4_value(static_cast<uint32_t>(t));
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int i = t + u * kDqThreads;
     if (i < nblk) {
-      const float prod = s_code2[qv[u]] * f16_to_f32(gv[u]);
-      s_scale[i] = prod + offset;
+      if constexpr (FMT == kFmtAbsmax32) {
+        s_scale[i] = __builtin_bit_cast(float, qv[u]);
+      } else {
+        const float prod = s_code2[qv[u]] * f16_to_f32(gv[u]);
+        s_scale[i] = prod + offset;
+      }
     }
   }
   __syncthreads();
@@ -145,7 +174,7 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
 // Used for unaligned buffers and block sizes below 8.  Same arithmetic, same
 // bits.
 // ---------------------------------------------------------------------------
-template <int OUT>
+template <int OUT, int FMT = kFmtDouble>
 __global__ __launch_bounds__(256) void dequant_any_kernel(
     const uint8_t* __restrict__ packed8, const uint8_t* __restrict__ absmax_q,
     const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
@@ -158,7 +187,7 @@ __global__ __launch_bounds__(256) void dequant_any_kernel(
        e += stride) {
     const uint8_t byte = packed8[e >> 1];
     const uint32_t nib = (e & 1) ? (byte & 15u) : (byte >> 4);
-    const float a = block_scale(absmax_q, absmax2, code2, offset, e >> log2bs, log2s2);
+    const float a = block_scale<FMT>(absmax_q, absmax2, code2, offset, e >> log2bs, log2s2);
     out2[e] = to_half_bits<OUT>(s_nf4[nib] * a);
   }
 }
@@ -314,6 +343,7 @@ struct OutBufs {
   float offset;
 };
 
+template <int FMT>
 __device__ __forceinline__ LoadBufs load_bufs(const nf4_gemv_desc& d, int K, int log2bs,
                                               int log2s2) {
   LoadBufs lb;
@@ -321,8 +351,13 @@ __device__ __forceinline__ LoadBufs load_bufs(const nf4_gemv_desc& d, int K, int
   const uint64_t nb = n ? ((n - 1) >> log2bs) + 1 : 0;
   const uint64_t ng = nb ? ((nb - 1) >> log2s2) + 1 : 0;
   lb.packed = rsrc(d.packed, static_cast<uint32_t>(n >> 1));
-  lb.absmax_q = rsrc(d.absmax_q, static_cast<uint32_t>(nb));
-  lb.absmax2 = rsrc(d.absmax2, static_cast<uint32_t>(ng * 2));
+  if constexpr (FMT == kFmtAbsmax32) {
+    lb.absmax_q = rsrc(d.absmax_q, static_cast<uint32_t>(nb * 4));  // the fp32 absmax
+    lb.absmax2 = rsrc(nullptr, 0);
+  } else {
+    lb.absmax_q = rsrc(d.absmax_q, static_cast<uint32_t>(nb));
+    lb.absmax2 = rsrc(d.absmax2, static_cast<uint32_t>(ng * 2));
+  }
   return lb;
 }
 
@@ -342,13 +377,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t x_buf(const nf4_gemv_desc& d, 
 
 // Loads of one row group for one lane: the 16-byte packed chunk, absmax_q
 // and absmax2 of rows [rl, rl + len) (rows past len read as zeros).
-template <int R>
+template <int R, int FMT>
 struct RowGroup {
   u32x4 pk[R];
   // at the loaded width: widened where they are used, so that the widening
   // is not hoisted to the loop latch, where it would wait for the loads
-  uint8_t q[R];
-  uint16_t a2[R];
+  typename ScaleBits<FMT>::type q[R];
+  uint16_t a2[R];  // double-quantized format only
 };
 
 // Per-lane parts of the buffer offsets (constant for the whole kernel): the
@@ -365,8 +400,8 @@ constexpr uint32_t kFar = 0x40000000u;  // added to an in-range offset: still < 
 // Every weight byte is read once per launch, so there is nothing to keep.
 constexpr int kStreamLoad = 2;
 
-template <int R>
-__device__ __forceinline__ void load_row_group(RowGroup<R>& rg, const LoadBufs& mb, int rl,
+template <int R, int FMT>
+__device__ __forceinline__ void load_row_group(RowGroup<R, FMT>& rg, const LoadBufs& mb, int rl,
                                                int len, const LaneOffsets& lo, int K, int log2bs,
                                                int log2s2) {
 #pragma unroll
@@ -377,8 +412,12 @@ __device__ __forceinline__ void load_row_group(RowGroup<R>& rg, const LoadBufs& 
     const uint32_t sfar = rr < len ? 0u : kFar;
     const uint32_t blk = (row * static_cast<uint32_t>(K) + lo.k0) >> log2bs;
     rg.pk[rr] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, lo.pk, srow, kStreamLoad);
-    rg.q[rr] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
-    rg.a2[rr] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, (blk >> log2s2) * 2u, sfar, 0);
+    if constexpr (FMT == kFmtAbsmax32) {
+      rg.q[rr] = __builtin_amdgcn_raw_buffer_load_b32(mb.absmax_q, blk * 4u, sfar, 0);
+    } else {
+      rg.q[rr] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
+      rg.a2[rr] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, (blk >> log2s2) * 2u, sfar, 0);
+    }
   }
 }
 
@@ -402,8 +441,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // hi) (hi + lo is within 2^-16 |v| of v); an activation dword is already the
 // matching bf16 pair (even column low), so two v_dot2c_f32_bf16 per byte do
 // the four products with fp32 accumulation and no conversion.
-template <int B, int R>
-__device__ __forceinline__ void dot_columns(const RowGroup<R>& rg, const u32x4 (&xr)[B][4], int j,
+template <int B, int R, int FMT>
+__device__ __forceinline__ void dot_columns(const RowGroup<R, FMT>& rg, const u32x4 (&xr)[B][4], int j,
                                             uint32_t copy_off, const uint2* s_pairs,
                                             float (&part)[R][B]) {
 #pragma unroll
@@ -433,13 +472,14 @@ __device__ __forceinline__ void dot_columns(const RowGroup<R>& rg, const u32x4 (
 // A descriptor the streaming kernel can read: 16-byte aligned packed weights
 // and activations, non-NULL arrays, a row count that matches the row offsets
 // and N * K < 2^31.  Matrices that fail this are skipped (y is not written).
+template <int FMT>
 __device__ __forceinline__ bool desc_usable(const nf4_gemv_desc& d, int rows, int K) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(d.packed) | reinterpret_cast<uintptr_t>(d.x);
   // every offset the kernel forms must stay below 2^30 (see kFar)
   const bool small = d.N >= 0 && static_cast<uint64_t>(d.N) * static_cast<uint64_t>(K) <
                                      (uint64_t(1) << 31);
-  return (a & 15) == 0 && d.N == rows && small && d.packed && d.absmax_q && d.absmax2 && d.x &&
-         d.y;
+  return (a & 15) == 0 && d.N == rows && small && d.packed && d.absmax_q &&
+         (FMT == kFmtAbsmax32 || d.absmax2) && d.x && d.y;
 }
 
 // Field-wise copy of descriptor m (or of the by-value descriptor when the
@@ -493,12 +533,13 @@ struct RowBegins {
 // Descriptor m for the kernel: a matrix it cannot use (see desc_usable) is
 // replaced by an empty one, whose loads read zeros and whose stores are
 // dropped.
+template <int FMT>
 __device__ __forceinline__ nf4_gemv_desc open_desc(const nf4_gemv_desc* __restrict__ descs,
                                                    const nf4_gemv_desc& single, int m, int len,
                                                    const RowBegins& rbeg, int K) {
   nf4_gemv_desc d = fetch_desc(descs, single, m);
   if (len <= 0 || m < 0 ||
-      !desc_usable(d, rbeg(m + 1) - rbeg(m), K)) {
+      !desc_usable<FMT>(d, rbeg(m + 1) - rbeg(m), K)) {
     d.packed = nullptr;
     d.absmax_q = nullptr;
     d.absmax2 = nullptr;
@@ -563,7 +604,7 @@ __device__ __forceinline__ int next_group(RowCursor& c, int r_end, const RowBegi
 // computes the current one.  All loads and the y stores are branch-free
 // buffer operations.
 // ---------------------------------------------------------------------------
-template <int B, int R, int NW, int WPE>
+template <int B, int R, int NW, int WPE, int FMT = kFmtDouble>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemv_stream_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
     int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2) {
@@ -582,7 +623,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // issued: its wait then overlaps theirs (the launch uses 512 threads)
   // (a bounds-checked load for all lanes: lanes past the table read 0)
   const uint16_t code2_bits = __builtin_amdgcn_raw_buffer_load_b16(
-      rsrc(code2, 512), static_cast<uint32_t>(tid) * 2u, 0u, 0);
+      rsrc(FMT == kFmtDouble ? code2 : nullptr, 512), static_cast<uint32_t>(tid) * 2u, 0u, 0);
   constexpr int teams = 8 / NW;         // the workgroup has 8 waves
   const int team = wave / nw;           // == teams for helper waves
   const int slab = wave - team * nw;
@@ -640,32 +681,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   int m0, rl0, m1, rl1;
   int len0 = next_group<R>(cur_c, r_end, rbeg, count, &m0, &rl0);
   m0 = __builtin_amdgcn_readfirstlane(m0);
-  const nf4_gemv_desc d0 = open_desc(descs, single, m0, len0, rbeg, K);
+  const nf4_gemv_desc d0 = open_desc<FMT>(descs, single, m0, len0, rbeg, K);
   int len1 = next_group<R>(cur_c, r_end, rbeg, count, &m1, &rl1);
   m1 = __builtin_amdgcn_readfirstlane(m1);
-  LoadBufs lb0 = load_bufs(d0, K, log2bs, log2s2);
+  LoadBufs lb0 = load_bufs<FMT>(d0, K, log2bs, log2s2);
   OutBufs ob0 = out_bufs<B>(d0);
   LaneOffsets lo;
   lo.pk = active ? static_cast<uint32_t>(k0 >> 1) : kFar;
   lo.x = active ? static_cast<uint32_t>(k0 * 2) : kFar;
   lo.k0 = static_cast<uint32_t>(k0);
-  RowGroup<R> g0, g1;
-  load_row_group<R>(g0, lb0, rl0, len0, lo, K, log2bs, log2s2);
+  RowGroup<R, FMT> g0, g1;
+  load_row_group<R, FMT>(g0, lb0, rl0, len0, lo, K, log2bs, log2s2);
   u32x4 xr[B][4];
   load_x<B>(xr, x_buf<B>(d0, K), lo, K);
   int mL = m0;            // matrix of lbL
   LoadBufs lbL = lb0;
   OutBufs ob1 = ob0;
   if (len1 > 0 && m1 != m0) {
-    const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, rbeg, K);
-    lbL = load_bufs(d1, K, log2bs, log2s2);
+    const nf4_gemv_desc d1 = open_desc<FMT>(descs, single, m1, len1, rbeg, K);
+    lbL = load_bufs<FMT>(d1, K, log2bs, log2s2);
     ob1 = out_bufs<B>(d1);
     mL = m1;
   }
-  load_row_group<R>(g1, lbL, rl1, len1, lo, K, log2bs, log2s2);
+  load_row_group<R, FMT>(g1, lbL, rl1, len1, lo, K, log2bs, log2s2);
 
   // the 256 x 32 pair table: (bf16 hi pair, bf16 lo pair) of each byte
-  if (tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
+  if (FMT == kFmtDouble && tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
   build_pair_table(s_pairs, tid, blockDim.x);
   const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
   __syncthreads();
@@ -677,37 +718,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // register copies: a copy out of a buffer whose loads are in flight would
   // wait for them, and the prefetch would be lost.
   int buf = 0;
-  auto step = [&](RowGroup<R>& cur, RowGroup<R>& fut) {
+  auto step = [&](RowGroup<R, FMT>& cur, RowGroup<R, FMT>& fut) {
     int m2, rl2;
     const int len2 = next_group<R>(cur_c, r_end, rbeg, count, &m2, &rl2);
     m2 = __builtin_amdgcn_readfirstlane(m2);
     OutBufs ob2 = ob1;
     if (len2 > 0 && m2 != mL) {
-      const nf4_gemv_desc d2 = open_desc(descs, single, m2, len2, rbeg, K);
-      lbL = load_bufs(d2, K, log2bs, log2s2);
+      const nf4_gemv_desc d2 = open_desc<FMT>(descs, single, m2, len2, rbeg, K);
+      lbL = load_bufs<FMT>(d2, K, log2bs, log2s2);
       ob2 = out_bufs<B>(d2);
       mL = m2;
     }
-    load_row_group<R>(fut, lbL, rl2, len2, lo, K, log2bs, log2s2);
+    load_row_group<R, FMT>(fut, lbL, rl2, len2, lo, K, log2bs, log2s2);
     // issue these loads here: sunk below the first wait for the current group
     // they would turn that wait into a wait for the group after it as well
     __builtin_amdgcn_sched_barrier(0);
 
     float c2[R];
+    if constexpr (FMT == kFmtDouble) {
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) c2[rr] = s_code2[cur.q[rr]];
+      for (int rr = 0; rr < R; ++rr) c2[rr] = s_code2[cur.q[rr]];
+    }
     float part[R][B];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr)
 #pragma unroll
       for (int b = 0; b < B; ++b) part[rr][b] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dot_columns<B, R>(cur, xr, j, copy_off, s_pairs, part);
+    for (int j = 0; j < 4; ++j) dot_columns<B, R, FMT>(cur, xr, j, copy_off, s_pairs, part);
     float val[R * B];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      const float prod = c2[rr] * f16_to_f32(cur.a2[rr]);
-      const float a = prod + ob0.offset;
+      float a;
+      if constexpr (FMT == kFmtAbsmax32) {
+        a = __builtin_bit_cast(float, cur.q[rr]);
+      } else {
+        const float prod = c2[rr] * f16_to_f32(cur.a2[rr]);
+        a = prod + ob0.offset;
+      }
 #pragma unroll
       for (int b = 0; b < B; ++b) val[rr * B + b] = a * part[rr][b];
     }
@@ -742,7 +790,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     // the next group starts a new matrix: fetch its activations now that the
     // current ones are no longer needed
     if (len1 > 0 && m1 != m0) {
-      load_x<B>(xr, x_buf<B>(open_desc(descs, single, m1, len1, rbeg, K), K), lo, K);
+      load_x<B>(xr, x_buf<B>(open_desc<FMT>(descs, single, m1, len1, rbeg, K), K), lo, K);
       // drain here (rare: once per matrix change) so that the loads of this
       // branch are not assumed outstanding on the common path, where they
       // would make every wait for the current group also wait for the next
@@ -761,7 +809,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // exit from the middle of a round would give the compiler a path from that
   // step back to the loop header, and loads still counted on it would make
   // the first step wait for the loads it has just issued.
-  RowGroup<R> g2;
+  RowGroup<R, FMT> g2;
   const int rounds = iters / 3;
   for (int it = 0; it < rounds; ++it) {
     step(g0, g2);
@@ -789,11 +837,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 // ---------------------------------------------------------------------------
 constexpr int kWaveCols = 4096;  // columns per pass of a wave (64 lanes x 64)
 
-template <int R, int P>
+template <int R, int P, int FMT>
 struct WaveGroup {
   u32x4 pk[R][P][2];
-  uint8_t q[R][P];
-  uint16_t a2[R][P];
+  typename ScaleBits<FMT>::type q[R][P];
+  uint16_t a2[R][P];  // double-quantized format only
 };
 
 // Per-lane offsets of pass p: packed byte offset inside a row and activation
@@ -806,8 +854,8 @@ struct WaveLane {
   uint32_t c0[P];
 };
 
-template <int R, int P>
-__device__ __forceinline__ void load_wave_group(WaveGroup<R, P>& g, const LoadBufs& mb, int rl,
+template <int R, int P, int FMT>
+__device__ __forceinline__ void load_wave_group(WaveGroup<R, P, FMT>& g, const LoadBufs& mb, int rl,
                                                 int len, const WaveLane<P>& wl, int K, int log2bs,
                                                 int log2s2) {
 #pragma unroll
@@ -821,8 +869,13 @@ __device__ __forceinline__ void load_wave_group(WaveGroup<R, P>& g, const LoadBu
       g.pk[rr][p][0] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p], srow, kStreamLoad);
       g.pk[rr][p][1] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p] + 16u, srow,
                                                               kStreamLoad);
-      g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
-      g.a2[rr][p] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, (blk >> log2s2) * 2u, sfar, 0);
+      if constexpr (FMT == kFmtAbsmax32) {
+        g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b32(mb.absmax_q, blk * 4u, sfar, 0);
+      } else {
+        g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
+        g.a2[rr][p] =
+            __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, (blk >> log2s2) * 2u, sfar, 0);
+      }
     }
   }
 }
@@ -848,8 +901,8 @@ __device__ __forceinline__ void load_wave_x(u32x4 (&xr)[B][P][8], __amdgpu_buffe
 // compiler from hoisting more reads, whose results would not fit in
 // registers.  Each (row, pass) piece is one 64-column block piece: its sum is
 // scaled by the block's absmax_real and added to the row's value.
-template <int B, int R, int P>
-__device__ __forceinline__ void wave_rows(const WaveGroup<R, P>& g, const u32x4 (&xr)[B][P][8],
+template <int B, int R, int P, int FMT>
+__device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u32x4 (&xr)[B][P][8],
                                           uint32_t copy_off, const uint2* s_pairs,
                                           const float* s_code2, float offset,
                                           const bool (&lane_in)[P], float (&val)[R * B]) {
@@ -894,8 +947,13 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P>& g, const u32x4 
       }
     }
     if (hj == 7) {
-      const float prod = s_code2[g.q[rr][p]] * f16_to_f32(g.a2[rr][p]);
-      const float a = prod + offset;
+      float a;
+      if constexpr (FMT == kFmtAbsmax32) {
+        a = __builtin_bit_cast(float, g.q[rr][p]);
+      } else {
+        const float prod = s_code2[g.q[rr][p]] * f16_to_f32(g.a2[rr][p]);
+        a = prod + offset;
+      }
 #pragma unroll
       for (int b = 0; b < B; ++b) val[rr * B + b] += lane_in[p] ? a * part[b] : 0.0f;
     }
@@ -956,7 +1014,7 @@ __device__ __forceinline__ int next_group_dyn(RowCursor& c, int& r_end, uint32_t
   return next_group<R>(c, r_end, rbeg, count, m_out, rl_out);
 }
 
-template <int B, int R, int P, int WPE, bool DYN>
+template <int B, int R, int P, int WPE, bool DYN, int FMT = kFmtDouble>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemv_wave_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
     int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2, unsigned* sched, int C) {
@@ -972,7 +1030,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // issued: its wait then overlaps theirs (the launch uses 512 threads)
   // (a bounds-checked load for all lanes: lanes past the table read 0)
   const uint16_t code2_bits = __builtin_amdgcn_raw_buffer_load_b16(
-      rsrc(code2, 512), static_cast<uint32_t>(tid) * 2u, 0u, 0);
+      rsrc(FMT == kFmtDouble ? code2 : nullptr, 512), static_cast<uint32_t>(tid) * 2u, 0u, 0);
 
   if (descs == nullptr) {
     if (tid == 0) s_rowbeg[0] = 0;
@@ -1050,13 +1108,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   int m0, rl0, m1, rl1;
   int len0 = advance(&m0, &rl0);
   m0 = __builtin_amdgcn_readfirstlane(m0);
-  const nf4_gemv_desc d0 = open_desc(descs, single, m0, len0, rbeg, K);
+  const nf4_gemv_desc d0 = open_desc<FMT>(descs, single, m0, len0, rbeg, K);
   int len1 = advance(&m1, &rl1);
   m1 = __builtin_amdgcn_readfirstlane(m1);
-  LoadBufs lb0 = load_bufs(d0, K, log2bs, log2s2);
+  LoadBufs lb0 = load_bufs<FMT>(d0, K, log2bs, log2s2);
   OutBufs ob0 = out_bufs<B>(d0);
-  WaveGroup<R, P> g0, g1, g2;
-  load_wave_group<R, P>(g0, lb0, rl0, len0, wl, K, log2bs, log2s2);
+  WaveGroup<R, P, FMT> g0, g1, g2;
+  load_wave_group<R, P, FMT>(g0, lb0, rl0, len0, wl, K, log2bs, log2s2);
   u32x4 xr[B][P][8];
   load_wave_x<B, P>(xr, x_buf<B>(d0, K), wl, K);
   const void* x_cur = d0.x;  // activations held in xr
@@ -1064,36 +1122,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   LoadBufs lbL = lb0;
   OutBufs ob1 = ob0;
   if (len1 > 0 && m1 != m0) {
-    const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, rbeg, K);
-    lbL = load_bufs(d1, K, log2bs, log2s2);
+    const nf4_gemv_desc d1 = open_desc<FMT>(descs, single, m1, len1, rbeg, K);
+    lbL = load_bufs<FMT>(d1, K, log2bs, log2s2);
     ob1 = out_bufs<B>(d1);
     mL = m1;
   }
-  load_wave_group<R, P>(g1, lbL, rl1, len1, wl, K, log2bs, log2s2);
+  load_wave_group<R, P, FMT>(g1, lbL, rl1, len1, wl, K, log2bs, log2s2);
 
-  if (tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
+  if (FMT == kFmtDouble && tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
   build_pair_table(s_pairs, tid, blockDim.x);
   const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
   __syncthreads();
 
-  auto step = [&](WaveGroup<R, P>& cur, WaveGroup<R, P>& fut) {
+  auto step = [&](WaveGroup<R, P, FMT>& cur, WaveGroup<R, P, FMT>& fut) {
     int m2, rl2;
     const int len2 = advance(&m2, &rl2);
     m2 = __builtin_amdgcn_readfirstlane(m2);
     OutBufs ob2 = ob1;
     if (len2 > 0 && m2 != mL) {
-      const nf4_gemv_desc d2 = open_desc(descs, single, m2, len2, rbeg, K);
-      lbL = load_bufs(d2, K, log2bs, log2s2);
+      const nf4_gemv_desc d2 = open_desc<FMT>(descs, single, m2, len2, rbeg, K);
+      lbL = load_bufs<FMT>(d2, K, log2bs, log2s2);
       ob2 = out_bufs<B>(d2);
       mL = m2;
     }
-    load_wave_group<R, P>(fut, lbL, rl2, len2, wl, K, log2bs, log2s2);
+    load_wave_group<R, P, FMT>(fut, lbL, rl2, len2, wl, K, log2bs, log2s2);
     __builtin_amdgcn_sched_barrier(0);
 
     // (a chunked range may end inside a round: empty groups skip the work)
     if (len0 > 0) {
       float val[R * B];
-      wave_rows<B, R, P>(cur, xr, copy_off, s_pairs, s_code2, ob0.offset, lane_in, val);
+      wave_rows<B, R, P, FMT>(cur, xr, copy_off, s_pairs, s_code2, ob0.offset, lane_in, val);
       // value v of the group ends up in lane 32 v (pair) or in row 16-lane
       // row r with v = 2 (r & 1) + (r >> 1) (quad)
       float tot;
@@ -1118,7 +1176,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     // the next group starts a matrix with other activations: fetch them now
     // that the current ones are no longer needed
     if (len1 > 0 && m1 != m0) {
-      const nf4_gemv_desc d1 = open_desc(descs, single, m1, len1, rbeg, K);
+      const nf4_gemv_desc d1 = open_desc<FMT>(descs, single, m1, len1, rbeg, K);
       if (d1.x != x_cur) {
         load_wave_x<B, P>(xr, x_buf<B>(d1, K), wl, K);
         x_cur = d1.x;
@@ -1181,7 +1239,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 // Requirements (checked on the host): K % 32 == 0, K <= 16384, blocksize >=
 // 32, packed 16-byte aligned, x 16-byte aligned.
 // ---------------------------------------------------------------------------
-template <int B, int R>
+template <int B, int R, int FMT = kFmtDouble>
 __global__ __launch_bounds__(512) void gemv_vec_kernel(
     const uint4* __restrict__ packed16, const uint8_t* __restrict__ absmax_q,
     const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
@@ -1207,22 +1265,32 @@ __global__ __launch_bounds__(512) void gemv_vec_kernel(
       const int64_t e = static_cast<int64_t>(r) * K + k0;
       const int64_t blk = e >> log2bs;
       pk[rr] = packed16[e >> 5];
-      qv[rr] = absmax_q[blk];
-      a2v[rr] = f16_to_f32(absmax2[blk >> log2s2]);
+      if constexpr (FMT == kFmtAbsmax32) {
+        qv[rr] = reinterpret_cast<const uint32_t*>(absmax_q)[blk];
+        a2v[rr] = 0.0f;
+      } else {
+        qv[rr] = absmax_q[blk];
+        a2v[rr] = f16_to_f32(absmax2[blk >> log2s2]);
+      }
     } else {
       pk[rr] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
       qv[rr] = 0;
       a2v[rr] = 0.0f;
     }
   }
-  for (int i = threadIdx.x; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
+  if constexpr (FMT == kFmtDouble)
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
   if (threadIdx.x < 16) s_nf4[threadIdx.x] = nf4_value(threadIdx.x);
   __syncthreads();
   float a[R];
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
-    const float prod = s_code2[qv[rr]] * a2v[rr];
-    a[rr] = prod + offset;
+    if constexpr (FMT == kFmtAbsmax32) {
+      a[rr] = __builtin_bit_cast(float, qv[rr]);
+    } else {
+      const float prod = s_code2[qv[rr]] * a2v[rr];
+      a[rr] = prod + offset;
+    }
   }
 
   float part[R][B];
@@ -1287,7 +1355,7 @@ __global__ __launch_bounds__(512) void gemv_vec_kernel(
 // row two elements (one byte) at a time, per-element scales.  Any even K,
 // any power-of-two block sizes, any alignment.
 // ---------------------------------------------------------------------------
-template <int B>
+template <int B, int FMT = kFmtDouble>
 __global__ __launch_bounds__(256) void gemv_any_kernel(
     const uint8_t* __restrict__ packed8, const uint8_t* __restrict__ absmax_q,
     const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
@@ -1306,9 +1374,9 @@ __global__ __launch_bounds__(256) void gemv_any_kernel(
     const int64_t e = r * K + k;
     const uint8_t byte = packed8[e >> 1];
     const float ve = s_nf4[byte >> 4] *
-                     block_scale(absmax_q, absmax2, code2, offset, e >> log2bs, log2s2);
+                     block_scale<FMT>(absmax_q, absmax2, code2, offset, e >> log2bs, log2s2);
     const float vo = s_nf4[byte & 15u] *
-                     block_scale(absmax_q, absmax2, code2, offset, (e + 1) >> log2bs, log2s2);
+                     block_scale<FMT>(absmax_q, absmax2, code2, offset, (e + 1) >> log2bs, log2s2);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const float x0 = __builtin_bit_cast(float, static_cast<uint32_t>(x[b * K + k]) << 16);
@@ -1367,7 +1435,7 @@ nf4_status launch_status() {
   return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 
-template <int OUT>
+template <int OUT, int FMT>
 nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
                           const uint16_t* code2, float offset, int64_t n, int lbs, int ls2,
                           void* out, hipStream_t st) {
@@ -1378,8 +1446,9 @@ nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const 
     const int U = steps >= cus * kDqThreads * 4 ? 4 : (steps >= cus * kDqThreads * 2 ? 2 : 1);
     const int64_t tiles = (steps + kDqThreads * U - 1) / (kDqThreads * U);
     if (tiles > 0x7FFFFFFF) return NF4_EUNSUPPORTED;
-    const auto kernel = U == 4 ? dequant_vec_kernel<OUT, 4>
-                               : (U == 2 ? dequant_vec_kernel<OUT, 2> : dequant_vec_kernel<OUT, 1>);
+    const auto kernel = U == 4   ? dequant_vec_kernel<OUT, 4, FMT>
+                        : U == 2 ? dequant_vec_kernel<OUT, 2, FMT>
+                                 : dequant_vec_kernel<OUT, 1, FMT>;
     hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(tiles)), dim3(kDqThreads), 0, st,
                        reinterpret_cast<const uint32_t*>(packed), packed, absmax_q, absmax2, code2,
                        offset, n, lbs, ls2, reinterpret_cast<u32x4*>(out),
@@ -1387,7 +1456,7 @@ nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const 
   } else {
     const int64_t blocks = (n + 255) / 256;
     const uint32_t grid = static_cast<uint32_t>(blocks < 65536 ? blocks : 65536);
-    hipLaunchKernelGGL((dequant_any_kernel<OUT>), dim3(grid), dim3(256), 0, st, packed, absmax_q,
+    hipLaunchKernelGGL((dequant_any_kernel<OUT, FMT>), dim3(grid), dim3(256), 0, st, packed, absmax_q,
                        absmax2, code2, offset, n, lbs, ls2, reinterpret_cast<uint16_t*>(out));
   }
   return launch_status();
@@ -1402,11 +1471,11 @@ constexpr int stream_rows() { return B == 1 ? 4 : (B == 2 ? 2 : 1); }
 template <int B>
 constexpr int stream_wpe() { return B <= 4 ? 4 : 2; }
 
-template <int B, int NW>
+template <int B, int NW, int FMT>
 void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                       int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                       int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>(), NW, stream_wpe<B>()>),
+  hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>(), NW, stream_wpe<B>(), FMT>),
                      dim3(static_cast<uint32_t>(grid)),
                      dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2);
 }
@@ -1416,7 +1485,7 @@ void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, i
 // and three groups are in flight.  With a scheduling workspace, four waves per
 // SIMD and at least 64 rows per wave, rows are handed out in chunks (see
 // SchedRegion): about 16 chunks per wave, 4 to 32 rows each.
-template <int B, int R, int P, int WPE>
+template <int B, int R, int P, int WPE, int FMT>
 nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                        int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                        unsigned* sched, hipStream_t st) {
@@ -1432,11 +1501,11 @@ nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, 
   if (WPE == 4 && sched != nullptr && rows_per_wave >= 64) {
     int C = 4;
     while (C < 32 && C * 2 * 16 <= rows_per_wave) C *= 2;
-    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, true>), dim3(static_cast<uint32_t>(grid)),
+    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, true, FMT>), dim3(static_cast<uint32_t>(grid)),
                        dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2, sched,
                        C);
   } else {
-    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, false>), dim3(static_cast<uint32_t>(grid)),
+    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, false, FMT>), dim3(static_cast<uint32_t>(grid)),
                        dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2,
                        nullptr, 0);
   }
@@ -1445,30 +1514,30 @@ nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, 
 
 // Returns NF4_EUNSUPPORTED (without launching) when no wave-per-row
 // configuration covers (B, K, blocksize).
-template <int B>
+template <int B, int FMT>
 nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                          unsigned* sched, hipStream_t st) {
   if (K % 64 != 0 || lbs < 6) return NF4_EUNSUPPORTED;
   const int P = (K + kWaveCols - 1) / kWaveCols;
   if constexpr (B == 1) {
-    if (P == 1) return wave_launch<1, 2, 1, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
-    if (P == 2) return wave_launch<1, 1, 2, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
-    if (P == 3) return wave_launch<1, 1, 3, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 1) return wave_launch<1, 2, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 2) return wave_launch<1, 1, 2, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 3) return wave_launch<1, 1, 3, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
   } else {
-    if (P == 1) return wave_launch<2, 1, 1, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
-    if (P == 2) return wave_launch<2, 1, 2, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 1) return wave_launch<2, 1, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 2) return wave_launch<2, 1, 2, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
   }
   return NF4_EUNSUPPORTED;
 }
 
-template <int B>
+template <int B, int FMT>
 nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                          unsigned* sched, hipStream_t st) {
   if constexpr (B <= 2) {
     const nf4_status ws =
-        wave_dispatch<B>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+        wave_dispatch<B, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
     if (ws != NF4_EUNSUPPORTED) return ws;
   }
   const int nw = (K + kSlab - 1) / kSlab;
@@ -1479,20 +1548,20 @@ nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   const int64_t want = (static_cast<int64_t>(total_rows) + teams - 1) / teams;
   const int64_t grid = want < max_wg ? (want > 0 ? want : 1) : max_wg;
   switch (nw) {
-    case 1: stream_launch_nw<B, 1>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
-    case 2: stream_launch_nw<B, 2>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
-    case 3: stream_launch_nw<B, 3>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
-    case 4: stream_launch_nw<B, 4>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
-    case 5: stream_launch_nw<B, 5>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
-    case 6: stream_launch_nw<B, 6>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
-    case 7: stream_launch_nw<B, 7>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
-    case 8: stream_launch_nw<B, 8>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 1: stream_launch_nw<B, 1, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 2: stream_launch_nw<B, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 3: stream_launch_nw<B, 3, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 4: stream_launch_nw<B, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 5: stream_launch_nw<B, 5, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 6: stream_launch_nw<B, 6, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 7: stream_launch_nw<B, 7, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
+    case 8: stream_launch_nw<B, 8, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, grid, st); break;
     default: return NF4_EUNSUPPORTED;
   }
   return launch_status();
 }
 
-template <int B>
+template <int B, int FMT>
 nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
                          const uint16_t* code2, float offset, int64_t N, int64_t K, int lbs,
                          int ls2, const uint16_t* x, uint16_t* y, hipStream_t st) {
@@ -1508,22 +1577,32 @@ nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const u
     one.N = N;
     one.row_begin = 0;
     one.offset = offset;
-    return stream_launch<B>(nullptr, one, 1, static_cast<int>(N), static_cast<int>(K), lbs, ls2,
-                            code2, nullptr, st);
+    return stream_launch<B, FMT>(nullptr, one, 1, static_cast<int>(N), static_cast<int>(K), lbs,
+                                 ls2, code2, nullptr, st);
   }
   if (vec) {
     constexpr int R = B <= 4 ? 2 : 1;
     const int nw = static_cast<int>((K + kSlab - 1) / kSlab);
     const int64_t grid = (N + R - 1) / R;
-    hipLaunchKernelGGL((gemv_vec_kernel<B, R>), dim3(static_cast<uint32_t>(grid)), dim3(64 * nw),
+    hipLaunchKernelGGL((gemv_vec_kernel<B, R, FMT>), dim3(static_cast<uint32_t>(grid)), dim3(64 * nw),
                        0, st, reinterpret_cast<const uint4*>(packed), absmax_q, absmax2, code2,
                        offset, static_cast<int>(N), static_cast<int>(K), lbs, ls2, x, y);
   } else {
     const int64_t grid = (N + 3) / 4;
     if (grid > 0x7FFFFFFF) return NF4_EUNSUPPORTED;
-    hipLaunchKernelGGL((gemv_any_kernel<B>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st,
+    hipLaunchKernelGGL((gemv_any_kernel<B, FMT>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st,
                        packed, absmax_q, absmax2, code2, offset, N, K, lbs, ls2, x, y);
   }
+  return launch_status();
+}
+
+// y = +0 for N x batch outputs (empty sums, K == 0).
+nf4_status gemv_fill_zero(uint16_t* y, int64_t N, int32_t batch, hipStream_t st) {
+  if (N > kMaxElems) return NF4_EUNSUPPORTED;
+  const int64_t count = N * batch;
+  const int64_t blocks = (count + 255) / 256;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>(blocks < 4096 ? blocks : 4096)),
+                     dim3(256), 0, st, y, count);
   return launch_status();
 }
 
@@ -1554,8 +1633,10 @@ nf4_status nf4_dequant(const uint8_t* packed, const uint8_t* absmax_q, const uin
   if (n >= kMaxElems) return NF4_EUNSUPPORTED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (out_dtype == NF4_BF16)
-    return dequant_launch<NF4_BF16>(packed, absmax_q, absmax2, code2, offset, n, lbs, ls2, out, st);
-  return dequant_launch<NF4_FP16>(packed, absmax_q, absmax2, code2, offset, n, lbs, ls2, out, st);
+    return dequant_launch<NF4_BF16, kFmtDouble>(packed, absmax_q, absmax2, code2, offset, n, lbs,
+                                                ls2, out, st);
+  return dequant_launch<NF4_FP16, kFmtDouble>(packed, absmax_q, absmax2, code2, offset, n, lbs, ls2,
+                                              out, st);
 }
 
 nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
@@ -1567,21 +1648,15 @@ nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16
   if (!pow2_log2(blocksize, &lbs) || !pow2_log2(s2_blocksize, &ls2)) return NF4_EINVAL;
   if (N == 0) return NF4_OK;
   if (!y) return NF4_EINVAL;
-  if (K == 0) {  // empty sums: y = +0
-    if (N > kMaxElems) return NF4_EUNSUPPORTED;
-    const int64_t count = N * batch;
-    const int64_t blocks = (count + 255) / 256;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>(blocks < 4096 ? blocks : 4096)), dim3(256),
-                       0, reinterpret_cast<hipStream_t>(stream), y, count);
-    return launch_status();
-  }
+  if (K == 0) return gemv_fill_zero(y, N, batch, reinterpret_cast<hipStream_t>(stream));
   if (!packed || !absmax_q || !absmax2 || !code2 || !x) return NF4_EINVAL;
   if (N > kMaxElems / K) return NF4_EUNSUPPORTED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   switch (batch) {
 #define NF4_GEMV_CASE(BB) \
   case BB:                \
-    return gemv_launch_b<BB>(packed, absmax_q, absmax2, code2, offset, N, K, lbs, ls2, x, y, st);
+    return gemv_launch_b<BB, kFmtDouble>(packed, absmax_q, absmax2, code2, offset, N, K, lbs, ls2, \
+                                         x, y, st);
     NF4_GEMV_CASE(1)
     NF4_GEMV_CASE(2)
     NF4_GEMV_CASE(3)
@@ -1591,6 +1666,54 @@ nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16
     NF4_GEMV_CASE(7)
     NF4_GEMV_CASE(8)
 #undef NF4_GEMV_CASE
+  }
+  return NF4_EINVAL;
+}
+
+nf4_status nf4_dequant_absmax32(const uint8_t* packed, const float* absmax, int64_t n,
+                                int32_t blocksize, void* out, int32_t out_dtype, void* stream) {
+  int lbs = 0;
+  if (n < 0 || !pow2_log2(blocksize, &lbs)) return NF4_EINVAL;
+  if (out_dtype != NF4_BF16 && out_dtype != NF4_FP16) return NF4_EINVAL;
+  if (n == 0) return NF4_OK;
+  if (!packed || !absmax || !out || !aligned(absmax, 4)) return NF4_EINVAL;
+  if (n >= kMaxElems) return NF4_EUNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* am = reinterpret_cast<const uint8_t*>(absmax);
+  if (out_dtype == NF4_BF16)
+    return dequant_launch<NF4_BF16, kFmtAbsmax32>(packed, am, nullptr, nullptr, 0.0f, n, lbs, 0,
+                                                  out, st);
+  return dequant_launch<NF4_FP16, kFmtAbsmax32>(packed, am, nullptr, nullptr, 0.0f, n, lbs, 0, out,
+                                                st);
+}
+
+nf4_status nf4_gemv_absmax32(const uint8_t* packed, const float* absmax, int64_t N, int64_t K,
+                             int32_t blocksize, const uint16_t* x, int32_t batch, uint16_t* y,
+                             void* stream) {
+  int lbs = 0;
+  if (N < 0 || K < 0 || (K & 1) || batch < 1 || batch > 8) return NF4_EINVAL;
+  if (!pow2_log2(blocksize, &lbs)) return NF4_EINVAL;
+  if (N == 0) return NF4_OK;
+  if (!y) return NF4_EINVAL;
+  if (K == 0) return gemv_fill_zero(y, N, batch, reinterpret_cast<hipStream_t>(stream));
+  if (!packed || !absmax || !x || !aligned(absmax, 4)) return NF4_EINVAL;
+  if (N > kMaxElems / K) return NF4_EUNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* am = reinterpret_cast<const uint8_t*>(absmax);
+  switch (batch) {
+#define NF4_GEMV_SL_CASE(BB)                                                                  \
+  case BB:                                                                                    \
+    return gemv_launch_b<BB, kFmtAbsmax32>(packed, am, nullptr, nullptr, 0.0f, N, K, lbs, 0, x, \
+                                           y, st);
+    NF4_GEMV_SL_CASE(1)
+    NF4_GEMV_SL_CASE(2)
+    NF4_GEMV_SL_CASE(3)
+    NF4_GEMV_SL_CASE(4)
+    NF4_GEMV_SL_CASE(5)
+    NF4_GEMV_SL_CASE(6)
+    NF4_GEMV_SL_CASE(7)
+    NF4_GEMV_SL_CASE(8)
+#undef NF4_GEMV_SL_CASE
   }
   return NF4_EINVAL;
 }
@@ -1618,14 +1741,14 @@ nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t t
   unsigned* sc = static_cast<unsigned*>(sched);
   const int tr = static_cast<int>(total_rows), k = static_cast<int>(K);
   switch (batch) {
-    case 1: return stream_launch<1>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 2: return stream_launch<2>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 3: return stream_launch<3>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 4: return stream_launch<4>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 5: return stream_launch<5>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 6: return stream_launch<6>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 7: return stream_launch<7>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    default: return stream_launch<8>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 1: return stream_launch<1, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 2: return stream_launch<2, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 3: return stream_launch<3, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 4: return stream_launch<4, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 5: return stream_launch<5, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 6: return stream_launch<6, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    case 7: return stream_launch<7, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
+    default: return stream_launch<8, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
   }
 }
 

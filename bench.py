@@ -27,7 +27,10 @@ milliseconds of load while its clocks settle.
 --workload picks another configuration as a context measurement (the default
 `sweep` is the headline): dequant_1k / dequant_4k (1024^2 and 4096^2 bf16
 dequant), qwen_b1 (the 7 Qwen2.5-1.5B-shaped GEMVs), llama_b1 / llama_b4 /
-llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8).  These run one
+llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8), and each of these
+with the suffix _absmax32 for the single-level format (one fp32 absmax per
+block: nf4_dequant_absmax32 / nf4_gemv_absmax32, encoded by
+nf4_quantize_absmax32).  These run one
 nf4_dequant / nf4_gemv call per matrix over copies of the encoded data rotated
 so that every step reads past the 256 MB MALL (cold HBM), timed from HIP
 graphs, and report the kernel of their largest matrix as the dominant one.
@@ -39,7 +42,8 @@ rocprofv3 counter summary (profiles/), given only when that summary was taken
 on the current kernel source; the CPU oracle timed on a bounded sample of the
 same workload.
 Algorithmic bytes: dequant ceil(n/2) + ceil(n/64) + 2 ceil(n/16384) + 516 + 2n;
-GEMV ceil(NK/2) + ceil(NK/64) + 2 ceil(NK/16384) + 516 + 2KB + 2NB.
+GEMV ceil(NK/2) + ceil(NK/64) + 2 ceil(NK/16384) + 516 + 2KB + 2NB; in the
+single-level format 4 ceil(n/64) bytes of scales replace the second-level terms.
 """
 import argparse
 import hashlib
@@ -53,6 +57,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CONTEXT_WORKLOADS = ("dequant_1k", "dequant_4k", "qwen_b1", "llama_b1", "llama_b4", "llama_b8")
 METRIC = "NF4 dequant & fused GEMV: achieved HBM GB/s and % of MI355X peak (1 GPU)"
 
 
@@ -67,6 +72,17 @@ def dequant_bytes(n: int) -> int:
 def gemv_bytes(N: int, K: int, B: int = 1) -> int:
     n = N * K
     return (n + 1) // 2 + -(-n // 64) + 2 * -(-n // 16384) + 516 + 2 * K * B + 2 * N * B
+
+
+# the single-level format: 4 bytes of fp32 absmax per 64-element block, no
+# second level
+def dequant_bytes_sl(n: int) -> int:
+    return (n + 1) // 2 + 4 * -(-n // 64) + 2 * n
+
+
+def gemv_bytes_sl(N: int, K: int, B: int = 1) -> int:
+    n = N * K
+    return (n + 1) // 2 + 4 * -(-n // 64) + 2 * K * B + 2 * N * B
 
 
 def build_workload(dev):
@@ -202,22 +218,33 @@ def build_context(dev, name):
     import synth
     import w4a16_gemv_amd as nf4
     code2 = nf4.nf4_code2_linear().to(dev)
+    single = name.endswith("_absmax32")        # the single-level format
+    base_name = name[: -len("_absmax32")] if single else name
+    dq_bytes = dequant_bytes_sl if single else dequant_bytes
+    gv_bytes = gemv_bytes_sl if single else gemv_bytes
 
     def encode(seed, n, outliers=False):
         w = synth.weights_device(seed, n, dev, outliers=outliers)
-        ws = torch.empty(nf4.load().nf4_quantize_workspace_size(n, 64), dtype=torch.uint8, device=dev)
-        t = nf4.nf4_quantize(w, 64, 256, code2=code2, workspace=ws)
-        del w, ws
+        if single:
+            t = nf4.nf4_quantize_absmax32(w, 64)
+        else:
+            ws = torch.empty(nf4.load().nf4_quantize_workspace_size(n, 64), dtype=torch.uint8,
+                             device=dev)
+            t = nf4.nf4_quantize(w, 64, 256, code2=code2, workspace=ws)
+            del ws
+        del w
         return t
 
     def clone(t):
+        if single:
+            return nf4.NF4Absmax32Tensor(t.packed.clone(), t.absmax.clone(), t.n, t.blocksize)
         return nf4.NF4Tensor(t.packed.clone(), t.absmax_q.clone(), t.absmax2.clone(), t.code2,
                              t.offset, t.n, t.blocksize, t.s2_blocksize)
 
-    if name.startswith("dequant"):
-        cfg = synth.DEQUANT_1K if name == "dequant_1k" else synth.DEQUANT_4K
+    if base_name.startswith("dequant"):
+        cfg = synth.DEQUANT_1K if base_name == "dequant_1k" else synth.DEQUANT_4K
         base = encode(cfg.seed, cfg.n, cfg.outliers)
-        set_bytes = dequant_bytes(cfg.n)
+        set_bytes = dq_bytes(cfg.n)
         nsets = max(2, -(-2 * MALL_BYTES // set_bytes))
         sets = []
         for _ in range(nsets):
@@ -227,17 +254,18 @@ def build_context(dev, name):
             t, out = st
             t.dequant(out=out)
         return dict(sets=sets, step_bytes=set_bytes, flops=0, launches=1, run=run,
-                    dominant=f"dequant_vec_kernel<bf16,8> ({cfg.rows}x{cfg.cols})",
+                    dominant=f"dequant_vec_kernel ({cfg.rows}x{cfg.cols}"
+                             f"{', fp32 absmax' if single else ''})",
                     dominant_bytes=set_bytes, dominant_flops=0)
 
-    if name == "qwen_b1":
+    if base_name == "qwen_b1":
         gemvs, batch, xseed = synth.QWEN_GEMVS, 1, synth.QWEN_X_SEED
     else:
-        batch = int(name.split("_b")[1])
+        batch = int(base_name.split("_b")[1])
         gemvs, xseed = synth.LLAMA_GEMVS, synth.llama_x_seed(batch)
     xs = {K: synth.activations_device(xseed, batch, K, dev) for K in {g.K for g in gemvs}}
     base = [(g, encode(g.seed, g.N * g.K)) for g in gemvs]
-    set_bytes = sum(gemv_bytes(g.N, g.K, batch) for g in gemvs)
+    set_bytes = sum(gv_bytes(g.N, g.K, batch) for g in gemvs)
     nsets = max(2, -(-2 * MALL_BYTES // set_bytes))
     sets = []
     for _ in range(nsets):
@@ -252,8 +280,9 @@ def build_context(dev, name):
                 t.gemv(g.N, g.K, xs[g.K], y)
     return dict(sets=sets, step_bytes=set_bytes, flops=sum(2 * g.N * g.K * batch for g in gemvs),
                 launches=len(gemvs), run=run, batch=batch,
-                dominant=f"nf4_gemv {gd.N}x{gd.K} batch {batch}",
-                dominant_bytes=gemv_bytes(gd.N, gd.K, batch), dominant_flops=2 * gd.N * gd.K * batch)
+                dominant=f"{'nf4_gemv_absmax32' if single else 'nf4_gemv'} {gd.N}x{gd.K} "
+                         f"batch {batch}",
+                dominant_bytes=gv_bytes(gd.N, gd.K, batch), dominant_flops=2 * gd.N * gd.K * batch)
 
 
 def bench_context(args, dev):
@@ -347,8 +376,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--schedule", choices=("stream", "layered"), default="stream")
     ap.add_argument("--workload", default="sweep",
-                    choices=("sweep", "dequant_1k", "dequant_4k", "qwen_b1", "llama_b1",
-                             "llama_b4", "llama_b8"))
+                    choices=("sweep",) + CONTEXT_WORKLOADS
+                    + tuple(w + "_absmax32" for w in CONTEXT_WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--prewarm", type=float, default=1.0,
                     help="seconds of untimed steps before the W warm-up steps")
@@ -378,7 +407,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic",
             "config": {"workload": args.workload, "batch": r["batch"], "blocksize": 64,
-                       "s2_blocksize": 256, "launches_per_step": r["launches"],
+                       "s2_blocksize": None if args.workload.endswith("_absmax32") else 256,
+                       "launches_per_step": r["launches"],
                        "bytes_per_step": r["step_bytes"], "rotating_sets": r["sets"],
                        "prewarm_s": args.prewarm},
             "pct_of_peak": round(100 * r["value"] / HBM_PEAK_GBS, 2),

@@ -272,6 +272,24 @@ nf4_status nf4_quantize(const float* w, int64_t n, int32_t blocksize, int32_t s2
                         uint16_t* absmax2, float* offset, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * nf4_quantize_absmax32 -- encode n fp32 weights into the single-level format
+ * on the GPU: the level-1 step of nf4_quantize alone ([quanttax]
+ * "量化的标准预期": one fp32 absmax per block).  absmax[b] = the largest |w|
+ * of block b; each code is the nearest NF4 value of w / absmax[b] (ties to the
+ * smaller index; code 7, the exact zero, for an all-zero block); two codes per
+ * byte, even element high.  Bit-identical to the level-1 output of
+ * nf4_quantize.
+ *
+ *  w             : device fp32[n].
+ *  packed        : device output, ceil(n/2) bytes.
+ *  absmax        : device output fp32[ceil(n/blocksize)], 4-byte aligned.
+ * Returns NF4_EINVAL for NULL pointers (n > 0), a misaligned absmax or a bad
+ * block size; NF4_EUNSUPPORTED for n >= 2^40.
+ */
+nf4_status nf4_quantize_absmax32(const float* w, int64_t n, int32_t blocksize, uint8_t* packed,
+                                 float* absmax, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,3 +162,12 @@ def test_absmax32_empty_and_oversized(lib):
     assert lib.nf4_gemv_absmax32(None, None, 0, 64, 64, None, 1, None, None) == 0
     assert _dq32(lib, n=1 << 41) == 2
     assert _gv32(lib, N=1 << 30, K=1 << 12) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(n=-1), dict(bs=3), dict(w=None), dict(packed=None),
+                                dict(absmax=None), dict(absmax=C.c_void_p(0x1002))])
+def test_quantize_absmax32_rejects_bad_arguments(lib, kw):
+    rc = lib.nf4_quantize_absmax32(kw.get("w", FAKE), kw.get("n", 4096), kw.get("bs", 64),
+                                   kw.get("packed", FAKE), kw.get("absmax", FAKE), None)
+    assert rc == 1
+    assert lib.nf4_quantize_absmax32(None, 0, 64, None, None, None) == 0

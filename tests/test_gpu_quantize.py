@@ -74,3 +74,39 @@ def test_quantize_is_deterministic():
     b = quantize_on_gpu(w, 64, 256)
     assert a.offset == b.offset
     assert torch.equal(a.packed, b.packed) and torch.equal(a.absmax_q, b.absmax_q)
+
+
+# ---------------------------------------------------------------------------
+# single-level format
+# ---------------------------------------------------------------------------
+
+SL_CASES = [(1 << 20, 64, False), (4096 * 4096, 64, True), (1, 64, False), (63, 64, True),
+            (100_001, 32, True), (70_000, 128, False), (5000, 8, True), (3001, 1, False)]
+
+
+@pytest.mark.parametrize("n,bs,outliers", SL_CASES)
+def test_quantize_absmax32_matches_oracle(n, bs, outliers):
+    w = synth.weights(n + 5 * bs, n, outliers=outliers)
+    ref = oracle.quantize_sl(w, bs)
+    print(f"[quantize_absmax32] n={n} bs={bs}", flush=True)
+    got = nf4.nf4_quantize_absmax32(torch.from_numpy(w).to(G.dev()), bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.absmax.cpu().numpy().view(np.uint32), ref.absmax.view(np.uint32))
+    assert np.array_equal(got.packed.cpu().numpy(), ref.packed)
+
+
+def test_quantize_absmax32_round_trip_on_gpu():
+    """GPU single-level encode, then GPU dequant and GEMV, against the oracle
+    on its own encoding of the same weights."""
+    N, K = 512, 4096
+    w = synth.weights(46, N * K, outliers=True)
+    got = nf4.nf4_quantize_absmax32(torch.from_numpy(w).to(G.dev()), 64)
+    out = got.dequant()
+    xb = synth.activations(47, 2, K)
+    y = got.gemv(N, K, G.x_to_device(xb))
+    torch.cuda.synchronize()
+    ref = oracle.quantize_sl(w, 64)
+    assert np.array_equal(G.bits16(out), oracle.dequant_sl(ref))
+    yr, S = oracle.gemv_sl(ref, N, K, xb)
+    ok, worst = G.gemv_within_tolerance(G.bf16_to_f64(G.bits16(y)), yr, S)
+    assert ok, worst

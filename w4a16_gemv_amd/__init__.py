@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     EXPORTED,
     GemvGroup,
     LIB_PATH,
+    NF4Absmax32Tensor,
     NF4_BF16,
     NF4_EHIP,
     NF4_EINVAL,
@@ -25,5 +26,6 @@ from ._binding import (  # noqa: F401
     nf4_gemv,
     nf4_gemv_absmax32,
     nf4_quantize,
+    nf4_quantize_absmax32,
     status_string,
 )

@@ -21,7 +21,7 @@ NF4_BF16, NF4_FP16 = 0, 1
 EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv",
             "nf4_dequant_absmax32", "nf4_gemv_absmax32", "nf4_gemv_grouped",
             "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
-            "nf4_quantize")
+            "nf4_quantize", "nf4_quantize_absmax32")
 
 _lib = None
 
@@ -64,6 +64,8 @@ def load() -> C.CDLL:
     lib.nf4_quantize_workspace_size.argtypes = [i64, i32]
     lib.nf4_quantize.restype = C.c_int
     lib.nf4_quantize.argtypes = [p, i64, i32, i32, p, p, p, p, p, p, C.c_size_t, p]
+    lib.nf4_quantize_absmax32.restype = C.c_int
+    lib.nf4_quantize_absmax32.argtypes = [p, i64, i32, p, p, p]
     _lib = lib
     return lib
 
@@ -267,6 +269,43 @@ def nf4_quantize(w: torch.Tensor, blocksize: int = 64, s2_blocksize: int = 256,
         return NF4Tensor(packed, absmax_q, absmax2, code2, off.item(), n, blocksize, s2_blocksize)
     return NF4Tensor(packed, absmax_q, absmax2, code2, float("nan"), n, blocksize,
                      s2_blocksize), off
+
+
+class NF4Absmax32Tensor:
+    """A flattened tensor in the single-level NF4 format (one fp32 absmax per
+    block), on the GPU."""
+
+    def __init__(self, packed, absmax, n: int, blocksize: int = 64):
+        self.packed, self.absmax = packed, absmax
+        self.n, self.blocksize = int(n), int(blocksize)
+
+    @property
+    def nbytes(self) -> int:
+        return self.packed.numel() + 4 * self.absmax.numel()
+
+    def dequant(self, out=None, out_dtype=torch.bfloat16):
+        return nf4_dequant_absmax32(self.packed, self.absmax, self.n, self.blocksize, out=out,
+                                    out_dtype=out_dtype)
+
+    def gemv(self, N: int, K: int, x, y=None):
+        if N * K != self.n:
+            raise ValueError(f"N*K = {N * K} does not match the tensor's {self.n} elements")
+        return nf4_gemv_absmax32(self.packed, self.absmax, N, K, x, self.blocksize, y=y)
+
+
+def nf4_quantize_absmax32(w: torch.Tensor, blocksize: int = 64) -> NF4Absmax32Tensor:
+    """Encode fp32 weights (any shape, flattened) into the single-level format
+    on w's GPU."""
+    if w.dtype != torch.float32:
+        raise ValueError("w must be float32")
+    n = w.numel()
+    wc = w.contiguous().view(-1)
+    packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(-(-n // int(blocksize)), dtype=torch.float32, device=w.device)
+    st = load().nf4_quantize_absmax32(_dev(wc, "w", (torch.float32,), n), n, int(blocksize),
+                                      packed.data_ptr(), absmax.data_ptr(), _stream(wc))
+    _check("nf4_quantize_absmax32", st)
+    return NF4Absmax32Tensor(packed, absmax, n, blocksize)
 
 
 # layout of nf4_gemv_desc (include/nf4.h), 64 bytes

@@ -1,4 +1,5 @@
-// nf4_quantize.hip -- the NF4 double-quantization encoder on the GPU.
+// nf4_quantize.hip -- the NF4 encoders on the GPU: double-quantized, and the
+// single-level format (one fp32 absmax per block, its level-1 step alone).
 //
 // Produces the format that nf4_dequant / nf4_gemv read, from fp32 weights,
 // following the two levels described on the pages: [blog] "NF4反量化算子优化",
@@ -216,6 +217,23 @@ nf4_status nf4_quantize(const float* w, int64_t n, int32_t blocksize, int32_t s2
                      ls2, offset, absmax2);
   hipLaunchKernelGGL(block_code_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, st, absmax, nb,
                      ls2, offset, absmax2, code2, absmax_q);
+  hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for((n + 1) / 2)), dim3(kThreads), 0, st, w, n,
+                     lbs, absmax, packed);
+  return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+nf4_status nf4_quantize_absmax32(const float* w, int64_t n, int32_t blocksize, uint8_t* packed,
+                                 float* absmax, void* stream) {
+  int lbs = 0;
+  if (n < 0 || !pow2_log2(blocksize, &lbs)) return NF4_EINVAL;
+  if (n == 0) return NF4_OK;
+  if (!w || !packed || !absmax || (reinterpret_cast<uintptr_t>(absmax) & 3) != 0)
+    return NF4_EINVAL;
+  if (n >= (int64_t(1) << 40)) return NF4_EUNSUPPORTED;
+  const int64_t nb = (n + blocksize - 1) / blocksize;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(block_absmax_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, st, w, n, lbs,
+                     absmax);
   hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for((n + 1) / 2)), dim3(kThreads), 0, st, w, n,
                      lbs, absmax, packed);
   return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EHIP;

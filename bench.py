@@ -74,16 +74,6 @@ def gemv_bytes(N: int, K: int, B: int = 1) -> int:
     return (n + 1) // 2 + -(-n // 64) + 2 * -(-n // 16384) + 516 + 2 * K * B + 2 * N * B
 
 
-# the single-level format: 4 bytes of fp32 absmax per 64-element block, no
-# second level
-def dequant_bytes_sl(n: int) -> int:
-    return (n + 1) // 2 + 4 * -(-n // 64) + 2 * n
-
-
-def gemv_bytes_sl(N: int, K: int, B: int = 1) -> int:
-    n = N * K
-    return (n + 1) // 2 + 4 * -(-n // 64) + 2 * K * B + 2 * N * B
-
 
 def build_workload(dev):
     import torch
@@ -209,7 +199,7 @@ MALL_BYTES = 256 << 20
 VALU_PEAK_TFLOPS = 157.3
 
 
-def build_context(dev, name):
+def build_context(dev, name, bs=64):
     """One of the smaller configurations, encoded once and copied into enough
     sets that one pass over all sets reads more than twice the MALL.
     Returns dict(sets, step_bytes, flops, launches, dominant, run)."""
@@ -220,17 +210,28 @@ def build_context(dev, name):
     code2 = nf4.nf4_code2_linear().to(dev)
     single = name.endswith("_absmax32")        # the single-level format
     base_name = name[: -len("_absmax32")] if single else name
-    dq_bytes = dequant_bytes_sl if single else dequant_bytes
-    gv_bytes = gemv_bytes_sl if single else gemv_bytes
+    if single:
+        def dq_bytes(n):
+            return (n + 1) // 2 + 4 * -(-n // bs) + 2 * n
+
+        def gv_bytes(N, K, B):
+            return (N * K + 1) // 2 + 4 * -(-N * K // bs) + 2 * K * B + 2 * N * B
+    else:
+        def dq_bytes(n):
+            return (n + 1) // 2 + -(-n // bs) + 2 * -(-n // (bs * 256)) + 516 + 2 * n
+
+        def gv_bytes(N, K, B):
+            n = N * K
+            return (n + 1) // 2 + -(-n // bs) + 2 * -(-n // (bs * 256)) + 516 + 2 * K * B + 2 * N * B
 
     def encode(seed, n, outliers=False):
         w = synth.weights_device(seed, n, dev, outliers=outliers)
         if single:
-            t = nf4.nf4_quantize_absmax32(w, 64)
+            t = nf4.nf4_quantize_absmax32(w, bs)
         else:
-            ws = torch.empty(nf4.load().nf4_quantize_workspace_size(n, 64), dtype=torch.uint8,
+            ws = torch.empty(nf4.load().nf4_quantize_workspace_size(n, bs), dtype=torch.uint8,
                              device=dev)
-            t = nf4.nf4_quantize(w, 64, 256, code2=code2, workspace=ws)
+            t = nf4.nf4_quantize(w, bs, 256, code2=code2, workspace=ws)
             del ws
         del w
         return t
@@ -291,7 +292,7 @@ def bench_context(args, dev):
     over every rotating set, a second one only the dominant kernel's launches
     over every set.  Per step / per launch = graph time / number of sets."""
     import torch
-    wl = build_context(dev, args.workload)
+    wl = build_context(dev, args.workload, args.blocksize)
     sets = wl["sets"]
     stream = torch.cuda.Stream(dev)
 
@@ -378,6 +379,8 @@ def main():
     ap.add_argument("--workload", default="sweep",
                     choices=("sweep",) + CONTEXT_WORKLOADS
                     + tuple(w + "_absmax32" for w in CONTEXT_WORKLOADS))
+    ap.add_argument("--blocksize", type=int, default=64,
+                    help="first-level block size of the context workloads (the sweep uses 64)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--prewarm", type=float, default=1.0,
                     help="seconds of untimed steps before the W warm-up steps")
@@ -406,7 +409,7 @@ def main():
             "steps": r["steps"], "warmup": args.warmup, "ms_per_step": round(r["ms"], 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic",
-            "config": {"workload": args.workload, "batch": r["batch"], "blocksize": 64,
+            "config": {"workload": args.workload, "batch": r["batch"], "blocksize": args.blocksize,
                        "s2_blocksize": None if args.workload.endswith("_absmax32") else 256,
                        "launches_per_step": r["launches"],
                        "bytes_per_step": r["step_bytes"], "rotating_sets": r["sets"],

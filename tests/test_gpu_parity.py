@@ -283,6 +283,11 @@ def _group_case(shapes_seeds, K, batch, x_seed):
     (4096, [(4096, 600), (4096, 601), (11008, 602), (256, 603), (1, 604), (37, 605)]),
     (1536, [(1536, 610), (256, 611), (256, 612), (8960, 613)]),
     (11008, [(4096, 620), (3, 621)]),
+    # two 4096-column passes per wave; three at their upper end; one column
+    # block past it (no wave configuration: the team kernel)
+    (8192, [(300, 640), (7, 641)]),
+    (12288, [(40, 650), (9, 651)]),
+    (12352, [(33, 655)]),
     (96, [(5, 630)]),
 ])
 def test_gemv_grouped_matches_oracle(K, shapes, batch):

@@ -1522,9 +1522,13 @@ nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   const int P = (K + kWaveCols - 1) / kWaveCols;
   if constexpr (B == 1) {
     if (P == 1) return wave_launch<1, 2, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+  }
+  // the other configurations serve grouped launches only, which take the
+  // double-quantized format
+  if constexpr (B == 1 && FMT == kFmtDouble) {
     if (P == 2) return wave_launch<1, 1, 2, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
     if (P == 3) return wave_launch<1, 1, 3, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
-  } else {
+  } else if constexpr (B == 2 && FMT == kFmtDouble) {
     if (P == 1) return wave_launch<2, 1, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
     if (P == 2) return wave_launch<2, 1, 2, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
   }
@@ -1535,10 +1539,24 @@ template <int B, int FMT>
 nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                          unsigned* sched, hipStream_t st) {
+  // Grouped launches (descs != NULL) at batch 1-2 take the wave kernel.  A
+  // single matrix takes it only at batch 1, one pass and up to 2^24 weights:
+  // there every wave has one or two rows and the wave kernel's lighter
+  // prologue wins (4096 x 4096: 6.8 us against 7.8).  Past that, and at batch
+  // 2, a single launch has all its loads in flight almost at once and ends
+  // with each wave's serial decode of its rows; the team kernel splits every
+  // row over several waves and finishes sooner (11008 x 4096: 11.0 us against
+  // 12.0; 4096 x 11008: 11.2 against 14.5; 4096 x 4096 at batch 2: 7.2
+  // against 8.7).  In a long grouped launch the wave kernel's rows pipeline
+  // and it streams faster than the team kernel.
   if constexpr (B <= 2) {
-    const nf4_status ws =
-        wave_dispatch<B, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
-    if (ws != NF4_EUNSUPPORTED) return ws;
+    const bool single_ok =
+        B == 1 && K <= kWaveCols && static_cast<int64_t>(total_rows) * K <= (int64_t(1) << 24);
+    if (descs != nullptr || single_ok) {
+      const nf4_status ws =
+          wave_dispatch<B, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+      if (ws != NF4_EUNSUPPORTED) return ws;
+    }
   }
   const int nw = (K + kSlab - 1) / kSlab;
   const int teams = 8 / nw;

@@ -111,7 +111,8 @@ def build_workload(dev):
 
 
 DOMINANT_K = 4096
-DOMINANT_KERNEL = "gemv_wave_kernel<1, 2, 1, 4, true> (nf4_gemv_grouped, K=4096, 192 matrices)"
+DOMINANT_KERNEL = ("gemv_wave_kernel<1, 2, 1, 4, true, 0> (nf4_gemv_grouped, K=4096, "
+                   "192 matrices)")
 KERNEL_SOURCE = os.path.join(ROOT, "w4a16_gemv_amd", "csrc", "nf4_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_wave_k4096_sweep_traffic.txt")
 
@@ -542,7 +543,7 @@ def main():
         "all_gemvs": None if args.no_context else {"gbs": round(gemv_gbs, 1), "ms": round(gemv_ms, 4),
                                                    "launches": launches},
         "dequant": None if args.no_context else {
-            "kernel": "dequant_vec_kernel<bf16,8>", "gbs": round(dq_gbs, 1),
+            "kernel": "dequant_vec_kernel<0, 4, 0> (bf16, 4 steps per lane)", "gbs": round(dq_gbs, 1),
             "us": round(dq_ms * 1e3, 2), "frac": round(dq_gbs / HBM_PEAK_GBS, 4)},
         f"{other}_schedule": None if args.no_context else {
             "ms_per_step": round(other_ms, 4),

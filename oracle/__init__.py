@@ -1,5 +1,5 @@
-"""CPU oracle for the NF4 double-quantization path and the single-level
-fp32-absmax format (ctypes wrapper).
+"""CPU oracle for the NF4 double-quantization path, the single-level
+fp32-absmax format and the INT4 asymmetric group format (ctypes wrapper).
 
 TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only tests/, the smoke check in
 __graft_entry__ and the CPU-baseline leg of bench.py may import this package.
@@ -59,6 +59,10 @@ def _load():
         "oracle_dequant_sl": (None, [p, p, i64, i32, i32, i64, i64, p]),
         "oracle_dequant_sl_at": (None, [p, p, i32, i32, p, i64, p]),
         "oracle_gemv_sl": (None, [p, p, i64, i64, i32, p, i32, p, i64, p, p]),
+        "oracle_int4_quantize": (C.c_int, [p, i64, i32, p, p, p]),
+        "oracle_int4_dequant_f32": (None, [p, p, p, i64, i32, i64, i64, p]),
+        "oracle_int4_dequant": (None, [p, p, p, i64, i32, i32, i64, i64, p]),
+        "oracle_int4_gemv": (None, [p, p, p, i64, i64, i32, p, i32, p, i64, p, p, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -290,3 +294,68 @@ def gemv_sl(q: QuantizedSL, N: int, K: int, x_bf16: np.ndarray,
     _load().oracle_gemv_sl(_ptr(q.packed), _ptr(q.absmax), N, K, q.blocksize, _ptr(x), B,
                            _ptr(rows), nr, _ptr(y), _ptr(S))
     return y, S
+
+
+@dataclass
+class QuantizedInt4:
+    """The INT4 asymmetric group format: codes 0..15 (first element of each
+    byte in the LOW nibble), one fp16 scale and one fp16 zero point per group
+    of G consecutive elements."""
+    packed: np.ndarray      # uint8 [ceil(n/2)]
+    scales: np.ndarray      # uint16 fp16 bits [ceil(n/G)]
+    zeros: np.ndarray       # uint16 fp16 bits [ceil(n/G)]
+    n: int
+    group: int = 128
+
+
+def int4_quantize(w: np.ndarray, group: int = 128) -> QuantizedInt4:
+    w = np.ascontiguousarray(w, np.float32).reshape(-1)
+    n = w.size
+    ng = -(-n // group)
+    packed = np.empty((n + 1) // 2, np.uint8)
+    scales = np.empty(ng, np.uint16)
+    zeros = np.empty(ng, np.uint16)
+    rc = _load().oracle_int4_quantize(_ptr(w), n, group, _ptr(packed), _ptr(scales), _ptr(zeros))
+    if rc != 0:
+        raise RuntimeError(f"oracle_int4_quantize failed: {rc}")
+    return QuantizedInt4(packed, scales, zeros, n, group)
+
+
+def _i4args(q: QuantizedInt4):
+    return (_ptr(q.packed), _ptr(q.scales), _ptr(q.zeros))
+
+
+def int4_dequant_f32(q: QuantizedInt4, e0: int = 0, e1: int | None = None) -> np.ndarray:
+    e1 = q.n if e1 is None else min(e1, q.n)
+    out = np.empty(max(e1 - e0, 0), np.float32)
+    _load().oracle_int4_dequant_f32(*_i4args(q), q.n, q.group, e0, e1, _ptr(out))
+    return out
+
+
+def int4_dequant(q: QuantizedInt4, out_dtype: int = BF16, e0: int = 0,
+                 e1: int | None = None) -> np.ndarray:
+    e1 = q.n if e1 is None else min(e1, q.n)
+    out = np.empty(max(e1 - e0, 0), np.uint16)
+    _load().oracle_int4_dequant(*_i4args(q), q.n, q.group, int(out_dtype), e0, e1, _ptr(out))
+    return out
+
+
+def int4_gemv(q: QuantizedInt4, N: int, K: int, x_bf16: np.ndarray,
+              rows: np.ndarray | None = None):
+    """fp64 reference (y, S, M) for W = q viewed as [N][K]: S = sum |w x| and
+    M = sum (|q| + |z|) |s| |x| (the magnitude of the terms when the zero point
+    is applied once per group)."""
+    assert N * K == q.n
+    x = np.ascontiguousarray(x_bf16, np.uint16).reshape(-1, K)
+    B = x.shape[0]
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, np.int64)
+        nr = rows.size
+    else:
+        nr = N
+    y = np.empty((B, nr), np.float64)
+    S = np.empty((B, nr), np.float64)
+    M = np.empty((B, nr), np.float64)
+    _load().oracle_int4_gemv(*_i4args(q), N, K, q.group, _ptr(x), B, _ptr(rows), nr, _ptr(y),
+                             _ptr(S), _ptr(M))
+    return y, S, M

@@ -48,6 +48,8 @@
  *  - code2 (linear variant): fp16 nearest to -1 + 2 i / 255, i = 0..255.
  *  - odd n: the pad (low) nibble of the last byte is written as 0, ignored
  *    when reading.
+ *  [handbook] also defines the INT4 asymmetric group format (sections
+ *  "量化公式" and "W4A16：在寄存器里反量化"): see the INT4 part at the end.
  *  - single-level format ([quanttax] "量化的标准预期": one fp32 absmax per
  *    block of 64; "Kernel 实现": the fused kernel multiplies the fp32 code
  *    value by the block's fp32 scale): value = f32(NF4[idx] * absmax[block]),
@@ -473,6 +475,120 @@ void oracle_gemv_sl(const uint8_t* packed, const float* absmax, int64_t N, int64
             }
             if (y) y[(int64_t)b * nrows + j] = acc;
             if (S) S[(int64_t)b * nrows + j] = mag;
+        }
+    }
+    free(xd);
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT4 asymmetric group format ([handbook] "量化公式", "W4A16：在寄存器里  */
+/* 反量化"): groups of G consecutive elements share an fp16 scale s and an   */
+/* fp16 zero point z; value = (q - z) * s with q in 0..15; two codes per     */
+/* byte with the FIRST (even) element in the LOW nibble.                     */
+/* Readings: s = fp16(fp32(max - min) / 15), replaced by 1 when it is 0;     */
+/* z = round(-min / s) and q = clamp(round(w / s) + z, 0, 15), with round    */
+/* half away from zero (the page's listing rounds with std::round) in fp32,  */
+/* using the stored fp16 s; z is stored as fp16; value = fp32(fp32(q - z) *  */
+/* s) (the difference is exact).                                             */
+/* ------------------------------------------------------------------------ */
+
+static int int4_nibble(const uint8_t* packed, int64_t e) {
+    const uint8_t byte = packed[e / 2];
+    return (e % 2 == 0) ? (byte & 15) : (byte >> 4);
+}
+
+int oracle_int4_quantize(const float* w, int64_t n, int32_t G, uint8_t* packed,
+                         uint16_t* scales, uint16_t* zeros) {
+    if (n < 0 || G <= 0 || G % 2 != 0) return 1;  /* even G: no byte spans two groups */
+    const int64_t ng = (n + G - 1) / G;
+    memset(packed, 0, (size_t)((n + 1) / 2));
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < ng; ++g) {
+        const int64_t e0 = g * G, e1 = (g + 1) * G < n ? (g + 1) * G : n;
+        float mn = w[e0], mx = w[e0];
+        for (int64_t e = e0 + 1; e < e1; ++e) {
+            if (w[e] < mn) mn = w[e];
+            if (w[e] > mx) mx = w[e];
+        }
+        const float range = mx - mn;
+        uint16_t s16 = oracle_f16_from_float(range / 15.0f);
+        float s = (float)oracle_f16_to_double(s16);
+        if (s == 0.0f) { s16 = oracle_f16_from_double(1.0); s = 1.0f; }
+        const float zr = roundf(-mn / s);
+        const uint16_t z16 = oracle_f16_from_float(zr);
+        const float z = (float)oracle_f16_to_double(z16);
+        scales[g] = s16;
+        zeros[g] = z16;
+        for (int64_t e = e0; e < e1; ++e) {
+            float q = roundf(w[e] / s) + z;
+            if (q < 0.0f) q = 0.0f;
+            if (q > 15.0f) q = 15.0f;
+            const int qi = (int)q;
+            /* bytes are owned by one group: G is even, so group starts are even */
+            packed[e / 2] |= (uint8_t)((e % 2 == 0) ? qi : (qi << 4));
+        }
+    }
+    return 0;
+}
+
+static float int4_value(const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                        int32_t G, int64_t e) {
+    const float q = (float)int4_nibble(packed, e);
+    const float z = (float)oracle_f16_to_double(zeros[e / G]);
+    const float s = (float)oracle_f16_to_double(scales[e / G]);
+    const float d = q - z;
+    const float v = d * s;
+    return v;
+}
+
+void oracle_int4_dequant_f32(const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                             int64_t n, int32_t G, int64_t e0, int64_t e1, float* out) {
+    if (e1 > n) e1 = n;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = e0; e < e1; ++e) out[e - e0] = int4_value(packed, scales, zeros, G, e);
+}
+
+void oracle_int4_dequant(const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                         int64_t n, int32_t G, int32_t out_dtype, int64_t e0, int64_t e1,
+                         uint16_t* out) {
+    if (e1 > n) e1 = n;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = e0; e < e1; ++e) {
+        const float v = int4_value(packed, scales, zeros, G, e);
+        out[e - e0] = out_dtype == 0 ? oracle_bf16_from_float(v) : oracle_f16_from_float(v);
+    }
+}
+
+/* fp64 reference y[b][r] = sum_k v[r][k] x[b][k] (k ascending) with v the fp32
+ * value above; S[b][r] = sum_k |v x|; M[b][r] = sum_k (|q| + |z|) |s| |x|,
+ * the magnitude of the terms when the zero point is applied once per group
+ * (sum q x minus z sum x).  Layout as oracle_gemv; y, S or M may be NULL. */
+void oracle_int4_gemv(const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                      int64_t N, int64_t K, int32_t G, const uint16_t* x, int32_t B,
+                      const int64_t* rows, int64_t nrows, double* y, double* S, double* M) {
+    if (!rows) nrows = N;
+    (void)N;
+    double* xd = (double*)malloc((size_t)B * (size_t)K * sizeof(double));
+    if (!xd) return;
+    for (int64_t i = 0; i < (int64_t)B * K; ++i) xd[i] = oracle_bf16_to_double(x[i]);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t j = 0; j < nrows; ++j) {
+        const int64_t r = rows ? rows[j] : j;
+        for (int32_t b = 0; b < B; ++b) {
+            double acc = 0.0, mag = 0.0, mz = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t e = r * K + k;
+                const double xv = xd[(int64_t)b * K + k];
+                const double p = (double)int4_value(packed, scales, zeros, G, e) * xv;
+                acc += p;
+                mag += fabs(p);
+                const double s = oracle_f16_to_double(scales[e / G]);
+                const double z = oracle_f16_to_double(zeros[e / G]);
+                mz += ((double)int4_nibble(packed, e) + fabs(z)) * fabs(s) * fabs(xv);
+            }
+            if (y) y[(int64_t)b * nrows + j] = acc;
+            if (S) S[(int64_t)b * nrows + j] = mag;
+            if (M) M[(int64_t)b * nrows + j] = mz;
         }
     }
     free(xd);

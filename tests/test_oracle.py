@@ -592,3 +592,156 @@ def test_sl_gemv_matches_float64_matmul(N, K, B, bs):
     rows = np.array([N - 1, 0])
     y2, S2 = oracle.gemv_sl(q, N, K, xb, rows)
     assert np.array_equal(y2, y[:, rows]) and np.array_equal(S2, S[:, rows])
+
+
+# ----------------------------------------------------------------------------
+# INT4 asymmetric group format (handbook page: "量化公式", "W4A16：在寄存器里反量化")
+# ----------------------------------------------------------------------------
+
+F16 = np.float16
+
+
+def make_i4(packed, scales, zeros, n, G):
+    return oracle.QuantizedInt4(np.ascontiguousarray(packed, np.uint8),
+                                np.ascontiguousarray(np.asarray(scales, F16).view(np.uint16)),
+                                np.ascontiguousarray(np.asarray(zeros, F16).view(np.uint16)), n, G)
+
+
+def test_int4_word_layout_is_low_nibble_first():
+    """The page stores 8 consecutive weights per 32-bit word with the first
+    one in the low 4 bits: element 8 i + j is (word_i >> 4 j) & 15."""
+    rng = np.random.default_rng(50)
+    words = rng.integers(0, 2 ** 32, 64, dtype=np.uint64).astype(np.uint32)
+    packed = words.view(np.uint8)             # little-endian bytes of the words
+    n = 8 * words.size
+    q = make_i4(packed, np.ones(n // 128), np.zeros(n // 128), n, 128)
+    v = oracle.int4_dequant_f32(q)
+    expect = ((words[:, None] >> (4 * np.arange(8, dtype=np.uint32))[None, :]) & 15).reshape(-1)
+    assert np.array_equal(v, expect.astype(np.float32))
+
+
+def test_int4_exhaustive_byte_decode():
+    q = make_i4(np.arange(256, dtype=np.uint8), [1.0] * 4, [0.0] * 4, 512, 128)
+    v = oracle.int4_dequant_f32(q)
+    assert np.array_equal(v[0::2], (np.arange(256) & 15).astype(np.float32))
+    assert np.array_equal(v[1::2], (np.arange(256) >> 4).astype(np.float32))
+
+
+@pytest.mark.parametrize("n,G", [(4096, 128), (1000, 128), (777 * 2, 32), (64, 64), (300, 2)])
+def test_int4_dequant_closed_form(n, G):
+    """Power-of-two scales and integer zero points: every value is the exact
+    (q - z) * s."""
+    ng = -(-n // G)
+    rng = np.random.default_rng(n + G)
+    s = 2.0 ** (np.arange(ng) % 12 - 6)
+    z = np.arange(ng) % 17 - 1                    # includes -1 and 15
+    packed = rng.integers(0, 256, (n + 1) // 2).astype(np.uint8)
+    v = oracle.int4_dequant_f32(make_i4(packed, s, z, n, G)).astype(np.float64)
+    e = np.arange(n)
+    qv = np.where(e % 2 == 0, packed[e // 2] & 15, packed[e // 2] >> 4).astype(np.float64)
+    assert np.array_equal(v, (qv - z[e // G]) * s[e // G])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_int4_dequant_matches_exact_rational(seed):
+    """Exact rationals with arbitrary fp16 scales (subnormals included) and
+    non-integer fp16 zero points: q - z is exact in fp32, the product is
+    rounded once; the 16-bit outputs are numpy / torch RNE casts of it."""
+    rng = np.random.default_rng(400 + seed)
+    n, G = 1024, 32
+    ng = n // G
+    packed = rng.integers(0, 256, n // 2).astype(np.uint8)
+    s = (rng.standard_normal(ng) * 2.0 ** rng.integers(-26, 4, ng)).astype(F16)
+    z = (rng.standard_normal(ng) * 8).astype(F16)
+    q = make_i4(packed, s, z, n, G)
+    got = oracle.int4_dequant_f32(q)
+    e = np.arange(n)
+    qv = np.where(e % 2 == 0, packed[e // 2] & 15, packed[e // 2] >> 4)
+    expect = np.array([float(round_fraction((Fraction(int(qv[i])) - Fraction(float(z[i // G])))
+                                            * Fraction(float(s[i // G])))) for i in range(n)],
+                      np.float32)
+    neg = np.signbit(s[e // G].astype(np.float32)) ^ ((qv - z[e // G].astype(np.float64)) < 0)
+    expect = np.where(expect == 0, np.where(neg, np.float32(-0.0), np.float32(0.0)), expect)
+    assert np.array_equal(got.view(np.uint32), expect.view(np.uint32))
+    assert np.array_equal(oracle.int4_dequant(q, oracle.BF16), bf16_bits_torch(expect))
+    assert np.array_equal(oracle.int4_dequant(q, oracle.FP16), f16_bits_numpy(expect))
+
+
+def test_int4_quantizer_grid_round_trip():
+    """Groups built on the grid (q - z) s with s a power of two, z an integer
+    in 0..15 and both q = 0 and q = 15 present: min = -z s and max = (15 - z) s,
+    so the quantizer recovers s, z and every code exactly."""
+    rng = np.random.default_rng(11)
+    G, ng = 128, 64
+    s = 2.0 ** rng.integers(-12, -2, ng)
+    z = rng.integers(0, 16, ng)
+    q = rng.integers(0, 16, (ng, G))
+    q[:, 0], q[:, 1] = 0, 15
+    w = ((q - z[:, None]) * s[:, None]).astype(np.float32).reshape(-1)
+    got = oracle.int4_quantize(w, G)
+    assert np.array_equal(got.scales.view(F16).astype(np.float64), s)
+    assert np.array_equal(got.zeros.view(F16).astype(np.float64), z.astype(np.float64))
+    codes = np.empty(w.size, np.int64)
+    codes[0::2] = got.packed & 15
+    codes[1::2] = got.packed >> 4
+    assert np.array_equal(codes, q.reshape(-1))
+
+
+def test_int4_quantizer_bounds():
+    """Random weights: s is the fp16 rounding of (max - min) / 15, z is within
+    1/2 of -min / s, codes are in range, and each weight is within one step s
+    of its value (half a step plus the fp16 rounding of s times 15 at most)."""
+    G = 128
+    w = synth.weights(12, 64 * G, outliers=True)
+    q = oracle.int4_quantize(w, G)
+    wg = w.reshape(-1, G).astype(np.float64)
+    s = q.scales.view(F16).astype(np.float64)
+    z = q.zeros.view(F16).astype(np.float64)
+    span = wg.max(axis=1) - wg.min(axis=1)
+    assert np.all(np.abs(s - span / 15) <= 2.0 ** -11 * span / 15 + 1e-12)
+    assert np.all(np.abs(-wg.min(axis=1) / s - z) <= 0.5 + 1e-6)
+    v = oracle.int4_dequant_f32(q).astype(np.float64).reshape(-1, G)
+    assert np.all(np.abs(wg - v) <= s[:, None] * (0.5 + 15 * 2.0 ** -11) + 1e-9)
+
+
+def test_int4_quantizer_constant_and_zero_groups():
+    w = np.concatenate([np.zeros(128), np.full(128, 0.3), np.full(128, -2.7)]).astype(np.float32)
+    q = oracle.int4_quantize(w, 128)
+    assert np.all(q.scales.view(F16) == 1.0)          # a zero span takes scale 1
+    v = oracle.int4_dequant_f32(q).reshape(3, 128)
+    assert np.all(v[0] == 0.0)
+    assert np.all(np.abs(v[1:] - w.reshape(3, 128)[1:]) <= 0.5)
+
+
+def test_int4_gemv_one_hot_and_magnitudes():
+    N, K, G = 24, 512, 128
+    q = oracle.int4_quantize(synth.weights(13, N * K), G)
+    W = oracle.int4_dequant_f32(q).reshape(N, K)
+    for k in (0, 1, 127, 128, 511):
+        x = np.zeros((1, K), np.float32)
+        x[0, k] = 1.0
+        y, S, M = oracle.int4_gemv(q, N, K, synth.to_bf16_bits(x))
+        assert np.array_equal(y[0], W[:, k].astype(np.float64))
+        assert np.array_equal(S[0], np.abs(W[:, k]).astype(np.float64))
+        codes = np.empty(N * K, np.int64)
+        codes[0::2] = q.packed & 15
+        codes[1::2] = q.packed >> 4
+        grp = (np.arange(N) * K + k) // G
+        s = q.scales.view(F16).astype(np.float64)[grp]
+        z = q.zeros.view(F16).astype(np.float64)[grp]
+        assert np.allclose(M[0], (codes.reshape(N, K)[:, k] + np.abs(z)) * np.abs(s), rtol=1e-15)
+
+
+@pytest.mark.parametrize("N,K,B,G", [(64, 512, 1, 128), (33, 1536, 4, 128), (7, 256, 8, 32)])
+def test_int4_gemv_matches_float64_matmul(N, K, B, G):
+    q = oracle.int4_quantize(synth.weights(N + K + 2, N * K), G)
+    W = oracle.int4_dequant_f32(q).reshape(N, K).astype(np.float64)
+    xb = synth.activations(9, B, K)
+    xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    y, S, M = oracle.int4_gemv(q, N, K, xb)
+    assert np.allclose(y, xf @ W.T, rtol=1e-12, atol=1e-12 * np.abs(xf) @ np.abs(W).T)
+    assert np.allclose(S, np.abs(xf) @ np.abs(W).T, rtol=1e-12)
+    assert np.all(M >= S * (1 - 1e-12))
+    rows = np.array([N - 1, 0])
+    y2, S2, M2 = oracle.int4_gemv(q, N, K, xb, rows)
+    assert np.array_equal(y2, y[:, rows]) and np.array_equal(M2, M[:, rows])

@@ -25,13 +25,15 @@ def declared_functions():
         if fn.endswith(".h"):
             src = open(os.path.join(ROOT, "include", fn), encoding="utf-8").read()
             src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-            names += re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(nf4_\w+)\s*\(", src, flags=re.M)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**((?:nf4|int4)_\w+)\s*\(", src,
+                                flags=re.M)
     return sorted(set(names))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("nf4_dequant", "nf4_gemv", "nf4_abi_version", "nf4_status_string"):
+    for required in ("nf4_dequant", "nf4_gemv", "nf4_abi_version", "nf4_status_string",
+                     "int4_dequant", "int4_gemv", "int4_quantize"):
         assert required in names
 
 
@@ -171,3 +173,32 @@ def test_quantize_absmax32_rejects_bad_arguments(lib, kw):
                                    kw.get("packed", FAKE), kw.get("absmax", FAKE), None)
     assert rc == 1
     assert lib.nf4_quantize_absmax32(None, 0, 64, None, None, None) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(n=-1), dict(G=1), dict(G=48), dict(G=0), dict(dtype=2),
+                                dict(packed=None), dict(scales=None), dict(zeros=None),
+                                dict(out=None)])
+def test_int4_dequant_rejects_bad_arguments(lib, kw):
+    rc = lib.int4_dequant(kw.get("packed", FAKE), kw.get("scales", FAKE), kw.get("zeros", FAKE),
+                          kw.get("n", 4096), kw.get("G", 128), kw.get("out", FAKE),
+                          kw.get("dtype", 0), None)
+    assert rc == 1
+
+
+@pytest.mark.parametrize("kw", [dict(N=-1), dict(K=63), dict(batch=0), dict(batch=9), dict(G=3),
+                                dict(x=None), dict(y=None), dict(packed=None), dict(zeros=None)])
+def test_int4_gemv_rejects_bad_arguments(lib, kw):
+    rc = lib.int4_gemv(kw.get("packed", FAKE), FAKE, kw.get("zeros", FAKE), kw.get("N", 4),
+                       kw.get("K", 256), kw.get("G", 128), kw.get("x", FAKE), kw.get("batch", 1),
+                       kw.get("y", FAKE), None)
+    assert rc == 1
+
+
+def test_int4_empty_oversized_and_quantize_validation(lib):
+    assert lib.int4_dequant(None, None, None, 0, 128, None, 0, None) == 0
+    assert lib.int4_gemv(None, None, None, 0, 256, 128, None, 1, None, None) == 0
+    assert lib.int4_dequant(FAKE, FAKE, FAKE, 1 << 41, 128, FAKE, 0, None) == 2
+    assert lib.int4_gemv(FAKE, FAKE, FAKE, 1 << 30, 1 << 12, 128, FAKE, 1, FAKE, None) == 2
+    assert lib.int4_quantize(FAKE, 4096, 1, FAKE, FAKE, FAKE, None) == 1
+    assert lib.int4_quantize(None, 4096, 128, FAKE, FAKE, FAKE, None) == 1
+    assert lib.int4_quantize(None, 0, 128, None, None, None, None) == 0

@@ -3,11 +3,13 @@ AMD Instinct MI355X (gfx950).
 
 The compute lives in libnf4.so (HIP, C ABI in include/nf4.h); this package is
 its Python binding.  See nf4_dequant / nf4_gemv (double-quantized format) and
-nf4_dequant_absmax32 / nf4_gemv_absmax32 (one fp32 absmax per block).
+nf4_dequant_absmax32 / nf4_gemv_absmax32 (one fp32 absmax per block), and
+int4_dequant / int4_gemv (INT4 asymmetric groups, include/int4.h).
 """
 from ._binding import (  # noqa: F401
     EXPORTED,
     GemvGroup,
+    Int4Tensor,
     LIB_PATH,
     NF4Absmax32Tensor,
     NF4_BF16,
@@ -19,6 +21,9 @@ from ._binding import (  # noqa: F401
     NF4Error,
     NF4Tensor,
     format_sizes,
+    int4_dequant,
+    int4_gemv,
+    int4_quantize,
     load,
     nf4_code2_linear,
     nf4_dequant,

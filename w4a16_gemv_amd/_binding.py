@@ -1,4 +1,4 @@
-"""ctypes binding of libnf4 (include/nf4.h).
+"""ctypes binding of libnf4 (include/nf4.h, include/int4.h).
 
 Argument marshalling only: every step of the dequant and GEMV runs in the HIP
 kernels of libnf4.so.  Tensors must live on an AMD GPU; there is no CPU
@@ -21,7 +21,8 @@ NF4_BF16, NF4_FP16 = 0, 1
 EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv",
             "nf4_dequant_absmax32", "nf4_gemv_absmax32", "nf4_gemv_grouped",
             "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
-            "nf4_quantize", "nf4_quantize_absmax32")
+            "nf4_quantize", "nf4_quantize_absmax32", "int4_dequant", "int4_gemv",
+            "int4_quantize")
 
 _lib = None
 
@@ -66,6 +67,12 @@ def load() -> C.CDLL:
     lib.nf4_quantize.argtypes = [p, i64, i32, i32, p, p, p, p, p, p, C.c_size_t, p]
     lib.nf4_quantize_absmax32.restype = C.c_int
     lib.nf4_quantize_absmax32.argtypes = [p, i64, i32, p, p, p]
+    lib.int4_dequant.restype = C.c_int
+    lib.int4_dequant.argtypes = [p, p, p, i64, i32, p, i32, p]
+    lib.int4_gemv.restype = C.c_int
+    lib.int4_gemv.argtypes = [p, p, p, i64, i64, i32, p, i32, p, p]
+    lib.int4_quantize.restype = C.c_int
+    lib.int4_quantize.argtypes = [p, i64, i32, p, p, p, p]
     _lib = lib
     return lib
 
@@ -306,6 +313,84 @@ def nf4_quantize_absmax32(w: torch.Tensor, blocksize: int = 64) -> NF4Absmax32Te
                                       packed.data_ptr(), absmax.data_ptr(), _stream(wc))
     _check("nf4_quantize_absmax32", st)
     return NF4Absmax32Tensor(packed, absmax, n, blocksize)
+
+
+def int4_dequant(packed, scales, zeros, n: int, group_size: int = 128,
+                 out: torch.Tensor | None = None,
+                 out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Dequantize n elements of the INT4 asymmetric group format (include/int4.h)
+    to bf16 / fp16 (returns `out`, shape [n])."""
+    ng = -(-int(n) // int(group_size))
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float16")
+    if out is None:
+        out = torch.empty(int(n), dtype=out_dtype, device=packed.device)
+    if out.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("out must be bfloat16 or float16")
+    code = NF4_BF16 if out.dtype == torch.bfloat16 else NF4_FP16
+    pp = _dev(packed, "packed", _U8, (int(n) + 1) // 2)
+    ps = _dev(scales, "scales", _HALF_BITS, ng)
+    pz = _dev(zeros, "zeros", _HALF_BITS, ng)
+    po = _dev(out, "out", (out.dtype,), int(n))
+    st = load().int4_dequant(pp, ps, pz, int(n), int(group_size), po, code, _stream(out))
+    _check("int4_dequant", st)
+    return out
+
+
+def int4_gemv(packed, scales, zeros, N: int, K: int, x: torch.Tensor, group_size: int = 128,
+              y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[b][r] = sum_k W[r][k] x[b][k] for W in the INT4 asymmetric group format
+    viewed as [N][K].  x: bf16 [batch][K] (or [K]); returns y bf16 [batch][N]."""
+    xb, batch, y, squeeze = _gemv_io(x, N, K, y)
+    n = int(N) * int(K)
+    ng = -(-n // int(group_size))
+    pp = _dev(packed, "packed", _U8, (n + 1) // 2)
+    ps = _dev(scales, "scales", _HALF_BITS, ng)
+    pz = _dev(zeros, "zeros", _HALF_BITS, ng)
+    px = _dev(xb, "x", _BF16_BITS, batch * int(K))
+    py = _dev(y, "y", _BF16_BITS, batch * int(N))
+    st = load().int4_gemv(pp, ps, pz, int(N), int(K), int(group_size), px, int(batch), py,
+                          _stream(y))
+    _check("int4_gemv", st)
+    return y.view(int(N)) if squeeze and y.dim() == 2 else y
+
+
+class Int4Tensor:
+    """A flattened tensor in the INT4 asymmetric group format, on the GPU."""
+
+    def __init__(self, packed, scales, zeros, n: int, group_size: int = 128):
+        self.packed, self.scales, self.zeros = packed, scales, zeros
+        self.n, self.group_size = int(n), int(group_size)
+
+    @property
+    def nbytes(self) -> int:
+        return self.packed.numel() + 2 * self.scales.numel() + 2 * self.zeros.numel()
+
+    def dequant(self, out=None, out_dtype=torch.bfloat16):
+        return int4_dequant(self.packed, self.scales, self.zeros, self.n, self.group_size,
+                            out=out, out_dtype=out_dtype)
+
+    def gemv(self, N: int, K: int, x, y=None):
+        if N * K != self.n:
+            raise ValueError(f"N*K = {N * K} does not match the tensor's {self.n} elements")
+        return int4_gemv(self.packed, self.scales, self.zeros, N, K, x, self.group_size, y=y)
+
+
+def int4_quantize(w: torch.Tensor, group_size: int = 128) -> Int4Tensor:
+    """Encode fp32 weights (any shape, flattened) into the INT4 asymmetric group
+    format on w's GPU."""
+    if w.dtype != torch.float32:
+        raise ValueError("w must be float32")
+    n = w.numel()
+    wc = w.contiguous().view(-1)
+    ng = -(-n // int(group_size))
+    packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(ng, dtype=torch.int16, device=w.device)
+    zeros = torch.empty(ng, dtype=torch.int16, device=w.device)
+    st = load().int4_quantize(_dev(wc, "w", (torch.float32,), n), n, int(group_size),
+                              packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), _stream(wc))
+    _check("int4_quantize", st)
+    return Int4Tensor(packed, scales, zeros, n, group_size)
 
 
 # layout of nf4_gemv_desc (include/nf4.h), 64 bytes

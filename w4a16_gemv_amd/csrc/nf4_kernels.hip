@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "int4.h"
 #include "nf4.h"
 #include "nf4_device.h"
 
@@ -32,15 +33,33 @@ using namespace nf4dev;
 // [block]] * absmax2[group]) + offset.  kFmtAbsmax32: one fp32 absmax per
 // block and no second level; the absmax_q argument then carries that fp32
 // array and absmax2, code2 and offset are not used.
+// kFmtInt4: the INT4 asymmetric group format ([handbook] "量化公式", "W4A16：
+// 在寄存器里反量化"): codes q in 0..15 with the FIRST element of each byte in
+// the LOW nibble, and per group of 2^log2bs consecutive elements an fp16
+// scale s (passed as absmax_q) and an fp16 zero point z (passed as absmax2):
+// value = fp32(fp32(q - z) * s).
 constexpr int kFmtDouble = 0;
 constexpr int kFmtAbsmax32 = 1;
+constexpr int kFmtInt4 = 2;
 
-// Register type of a block's scale bits as loaded: the absmax_q byte, or the
-// fp32 absmax.
+// Register type of a block's scale bits as loaded: the absmax_q byte, the
+// fp32 absmax, or the fp16 group scale.
 template <int FMT>
 struct ScaleBits { using type = uint8_t; };
 template <>
 struct ScaleBits<kFmtAbsmax32> { using type = uint32_t; };
+template <>
+struct ScaleBits<kFmtInt4> { using type = uint16_t; };
+
+// The code of element 2 i + odd in packed byte i: the high nibble holds the
+// even element in the NF4 formats, the low nibble in the INT4 format.
+template <int FMT>
+__device__ __forceinline__ uint32_t nibble_of(uint32_t byte, uint32_t odd) {
+  if constexpr (FMT == kFmtInt4)
+    return odd ? (byte >> 4) & 15u : byte & 15u;
+  else
+    return odd ? byte & 15u : (byte >> 4) & 15u;
+}
 
 // absmax_real of one first-level block: fp32 product, then fp32 sum (or the
 // stored fp32 absmax).
@@ -57,6 +76,33 @@ __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ absmax_
     const float s = c * g;
     return s + offset;
   }
+}
+
+// The value of one element with code `nib` in block (group) blk; tab holds
+// the 16 NF4 values (the 16 integers 0..15 in the INT4 format).
+template <int FMT>
+__device__ __forceinline__ float element_value(const float* tab, uint32_t nib,
+                                               const uint8_t* __restrict__ absmax_q,
+                                               const uint16_t* __restrict__ absmax2,
+                                               const uint16_t* __restrict__ code2, float offset,
+                                               int64_t blk, int log2s2) {
+  if constexpr (FMT == kFmtInt4) {
+    const float s = f16_to_f32(reinterpret_cast<const uint16_t*>(absmax_q)[blk]);
+    const float z = f16_to_f32(absmax2[blk]);
+    const float d = tab[nib] - z;  // exact
+    return d * s;
+  } else {
+    return tab[nib] * block_scale<FMT>(absmax_q, absmax2, code2, offset, blk, log2s2);
+  }
+}
+
+// The table of the 16 code values: NF4, or the integers 0..15.
+template <int FMT>
+__device__ __forceinline__ float code_value(uint32_t i) {
+  if constexpr (FMT == kFmtInt4)
+    return static_cast<float>(i);
+  else
+    return nf4_value(i);
 }
 
 // ---------------------------------------------------------------------------
@@ -93,6 +139,7 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
   __shared__ float s_nf4[16];
   __shared__ float s_code2[256];
   __shared__ float s_scale[kDqThreads * U];
+  __shared__ float s_zero[FMT == kFmtInt4 ? kDqThreads * U : 1];
   const int t = threadIdx.x;
   const int64_t full_steps = n >> 3;
   const int64_t step0 = static_cast<int64_t>(blockIdx.x) * (kDqThreads * U);
@@ -116,6 +163,9 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
     const int i = t + u * kDqThreads;
     if constexpr (FMT == kFmtAbsmax32) {
       qv[u] = i < nblk ? reinterpret_cast<const uint32_t*>(absmax_q)[blk0 + i] : 0u;
+    } else if constexpr (FMT == kFmtInt4) {
+      qv[u] = i < nblk ? reinterpret_cast<const uint16_t*>(absmax_q)[blk0 + i] : 0u;
+      gv[u] = i < nblk ? absmax2[blk0 + i] : uint16_t(0);
     } else {
       qv[u] = i < nblk ? absmax_q[blk0 + i] : 0u;
       gv[u] = i < nblk ? absmax2[(blk0 + i) >> log2s2] : uint16_t(0);
@@ -124,7 +174,7 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
 
   // 2. tables, then one absmax_real per block
   if constexpr (FMT == kFmtDouble) s_code2[t] = f16_to_f32(c2);
-  if (t < 16) s_nf4[t] = nf4_value(static_cast<uint32_t>(t));
+  if (t < 16) s_nf4[t] = code_value<FMT>(static_cast<uint32_t>(t));
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -132,6 +182,9 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
     if (i < nblk) {
       if constexpr (FMT == kFmtAbsmax32) {
         s_scale[i] = __builtin_bit_cast(float, qv[u]);
+      } else if constexpr (FMT == kFmtInt4) {
+        s_scale[i] = f16_to_f32(static_cast<uint16_t>(qv[u]));
+        s_zero[i] = f16_to_f32(gv[u]);
       } else {
         const float prod = s_code2[qv[u]] * f16_to_f32(gv[u]);
         s_scale[i] = prod + offset;
@@ -145,14 +198,25 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
   for (int u = 0; u < U; ++u) {
     const int64_t s = step0 + u * kDqThreads + t;
     if (s < full_steps) {
-      const float a = s_scale[((s * 8) >> log2bs) - blk0];
+      const int bi = static_cast<int>(((s * 8) >> log2bs) - blk0);
+      const float a = s_scale[bi];
       const uint32_t wd = w[u];
       uint32_t o[4];
+      if constexpr (FMT == kFmtInt4) {
+        const float z = s_zero[bi];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float ve = s_nf4[(wd >> (8 * j + 4)) & 15u] * a;
-        const float vo = s_nf4[(wd >> (8 * j)) & 15u] * a;
-        o[j] = pack_pair<OUT>(ve, vo);
+        for (int j = 0; j < 4; ++j) {
+          const float de = s_nf4[(wd >> (8 * j)) & 15u] - z;  // exact
+          const float dd = s_nf4[(wd >> (8 * j + 4)) & 15u] - z;
+          o[j] = pack_pair<OUT>(de * a, dd * a);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float ve = s_nf4[(wd >> (8 * j + 4)) & 15u] * a;
+          const float vo = s_nf4[(wd >> (8 * j)) & 15u] * a;
+          o[j] = pack_pair<OUT>(ve, vo);
+        }
       }
       // streaming store: the kernel never reads its output back
       const u32x4 v = {o[0], o[1], o[2], o[3]};
@@ -160,10 +224,15 @@ __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
     } else if (s == full_steps) {
       // ragged tail: the last n % 8 elements, one at a time
       for (int64_t e = s * 8; e < n; ++e) {
-        const uint8_t byte = packed8[e >> 1];
-        const uint32_t nib = (e & 1) ? (byte & 15u) : (byte >> 4);
-        const float a = s_scale[(e >> log2bs) - blk0];
-        out2[e] = to_half_bits<OUT>(s_nf4[nib] * a);
+        const uint32_t nib = nibble_of<FMT>(packed8[e >> 1], static_cast<uint32_t>(e & 1));
+        const int bi = static_cast<int>((e >> log2bs) - blk0);
+        const float a = s_scale[bi];
+        if constexpr (FMT == kFmtInt4) {
+          const float d = s_nf4[nib] - s_zero[bi];
+          out2[e] = to_half_bits<OUT>(d * a);
+        } else {
+          out2[e] = to_half_bits<OUT>(s_nf4[nib] * a);
+        }
       }
     }
   }
@@ -180,15 +249,14 @@ __global__ __launch_bounds__(256) void dequant_any_kernel(
     const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset,
     int64_t n, int log2bs, int log2s2, uint16_t* __restrict__ out2) {
   __shared__ float s_nf4[16];
-  if (threadIdx.x < 16) s_nf4[threadIdx.x] = nf4_value(threadIdx.x);
+  if (threadIdx.x < 16) s_nf4[threadIdx.x] = code_value<FMT>(threadIdx.x);
   __syncthreads();
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
        e += stride) {
-    const uint8_t byte = packed8[e >> 1];
-    const uint32_t nib = (e & 1) ? (byte & 15u) : (byte >> 4);
-    const float a = block_scale<FMT>(absmax_q, absmax2, code2, offset, e >> log2bs, log2s2);
-    out2[e] = to_half_bits<OUT>(s_nf4[nib] * a);
+    const uint32_t nib = nibble_of<FMT>(packed8[e >> 1], static_cast<uint32_t>(e & 1));
+    out2[e] = to_half_bits<OUT>(
+        element_value<FMT>(s_nf4, nib, absmax_q, absmax2, code2, offset, e >> log2bs, log2s2));
   }
 }
 
@@ -315,6 +383,43 @@ __device__ __forceinline__ void build_pair_table(uint2* s_pairs, int tid, int nt
 }
 
 
+// The INT4 decode table (same 64 KiB of LDS): entry b is the exact bf16 pair
+// (b & 15, b >> 4) -- the even element, in the low nibble, in the low half --
+// replicated 64 times, copy c of entry b at uint32 index 64 b + c, so lane l
+// reads copy l and the 64 lanes of a wave never share a bank.
+constexpr int kInt4Copies = 64;
+__device__ __forceinline__ void build_int4_table(uint32_t* tab, int tid, int nthreads) {
+  for (int w = tid; w < 256 * kInt4Copies; w += nthreads) {
+    const uint32_t b = static_cast<uint32_t>(w) / kInt4Copies;
+    tab[w] = pack_pair<NF4_BF16>(static_cast<float>(b & 15u), static_cast<float>(b >> 4));
+  }
+}
+
+// Decode table and lane copy offset of the format (LDS byte offset of the
+// lane's copy within an entry row of 256 bytes).
+template <int FMT>
+__device__ __forceinline__ uint32_t build_decode_table(uint2* s_pairs, int tid, int nthreads,
+                                                       int lane) {
+  if constexpr (FMT == kFmtInt4) {
+    build_int4_table(reinterpret_cast<uint32_t*>(s_pairs), tid, nthreads);
+    return static_cast<uint32_t>(lane % kInt4Copies) * 4u;
+  } else {
+    build_pair_table(s_pairs, tid, nthreads);
+    return static_cast<uint32_t>(lane % kPairCopies) * 8u;
+  }
+}
+
+// Sum of the lane's activations of one batch row (raw bf16 pairs in x): the
+// zero-point term of the INT4 format is z times this sum.
+template <int N>
+__device__ __forceinline__ float pair_sum(const uint32_t (&x)[N]) {
+  typedef __bf16 bf16x2_ __attribute__((ext_vector_type(2)));
+  const bf16x2_ one = __builtin_bit_cast(bf16x2_, 0x3F803F80u);
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_, x[i]), one, acc, false);
+  return acc;
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -354,6 +459,9 @@ __device__ __forceinline__ LoadBufs load_bufs(const nf4_gemv_desc& d, int K, int
   if constexpr (FMT == kFmtAbsmax32) {
     lb.absmax_q = rsrc(d.absmax_q, static_cast<uint32_t>(nb * 4));  // the fp32 absmax
     lb.absmax2 = rsrc(nullptr, 0);
+  } else if constexpr (FMT == kFmtInt4) {
+    lb.absmax_q = rsrc(d.absmax_q, static_cast<uint32_t>(nb * 2));  // fp16 group scales
+    lb.absmax2 = rsrc(d.absmax2, static_cast<uint32_t>(nb * 2));    // fp16 zero points
   } else {
     lb.absmax_q = rsrc(d.absmax_q, static_cast<uint32_t>(nb));
     lb.absmax2 = rsrc(d.absmax2, static_cast<uint32_t>(ng * 2));
@@ -414,6 +522,9 @@ __device__ __forceinline__ void load_row_group(RowGroup<R, FMT>& rg, const LoadB
     rg.pk[rr] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, lo.pk, srow, kStreamLoad);
     if constexpr (FMT == kFmtAbsmax32) {
       rg.q[rr] = __builtin_amdgcn_raw_buffer_load_b32(mb.absmax_q, blk * 4u, sfar, 0);
+    } else if constexpr (FMT == kFmtInt4) {
+      rg.q[rr] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax_q, blk * 2u, sfar, 0);
+      rg.a2[rr] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, blk * 2u, sfar, 0);
     } else {
       rg.q[rr] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
       rg.a2[rr] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, (blk >> log2s2) * 2u, sfar, 0);
@@ -453,17 +564,30 @@ __device__ __forceinline__ void dot_columns(const RowGroup<R, FMT>& rg, const u3
       // address bits 15..8 = byte i of d, bits 7..0 = copy offset (selector
       // 0x0C = zero byte, 4 = byte 0 of the first operand, i = byte i of d)
       const uint32_t addr = __builtin_amdgcn_perm(copy_off, d, 0x0C0C0004u | (uint32_t(i) << 8));
-      const uint2 t = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_pairs) + addr);
+      if constexpr (FMT == kFmtInt4) {
+        // one exact bf16 code pair: q x summed here, z sum(x) applied per piece
+        const uint32_t t =
+            *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(s_pairs) + addr);
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        // copy the element out first: __builtin_bit_cast applied directly to a
-        // vector-element lvalue reads element 0 whatever the index
-        const uint32_t xw = xr[b][j][i];
-        const bf16x2 xp = __builtin_bit_cast(bf16x2, xw);
-        part[rr][b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, t.x), xp,
-                                                      part[rr][b], false);
-        part[rr][b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, t.y), xp,
-                                                      part[rr][b], false);
+        for (int b = 0; b < B; ++b) {
+          const uint32_t xw = xr[b][j][i];
+          part[rr][b] = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2, t), __builtin_bit_cast(bf16x2, xw), part[rr][b], false);
+        }
+      } else {
+        const uint2 t =
+            *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_pairs) + addr);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          // copy the element out first: __builtin_bit_cast applied directly to
+          // a vector-element lvalue reads element 0 whatever the index
+          const uint32_t xw = xr[b][j][i];
+          const bf16x2 xp = __builtin_bit_cast(bf16x2, xw);
+          part[rr][b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, t.x), xp,
+                                                        part[rr][b], false);
+          part[rr][b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, t.y), xp,
+                                                        part[rr][b], false);
+        }
       }
     }
   }
@@ -694,6 +818,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   load_row_group<R, FMT>(g0, lb0, rl0, len0, lo, K, log2bs, log2s2);
   u32x4 xr[B][4];
   load_x<B>(xr, x_buf<B>(d0, K), lo, K);
+  float xs[B];  // INT4: the lane's activation sums (computed before the loop)
   int mL = m0;            // matrix of lbL
   LoadBufs lbL = lb0;
   OutBufs ob1 = ob0;
@@ -707,8 +832,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 
   // the 256 x 32 pair table: (bf16 hi pair, bf16 lo pair) of each byte
   if (FMT == kFmtDouble && tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
-  build_pair_table(s_pairs, tid, blockDim.x);
-  const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
+  const uint32_t copy_off = build_decode_table<FMT>(s_pairs, tid, blockDim.x, lane);
+  auto sum_x = [&]() {
+    if constexpr (FMT == kFmtInt4) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        uint32_t w[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[4 * j + i] = xr[b][j][i];
+        xs[b] = pair_sum(w);
+      }
+    }
+  };
+  sum_x();
   __syncthreads();
   const int iters = __builtin_amdgcn_readfirstlane(s_iters);
 
@@ -749,15 +887,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     float val[R * B];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      float a;
-      if constexpr (FMT == kFmtAbsmax32) {
-        a = __builtin_bit_cast(float, cur.q[rr]);
-      } else {
-        const float prod = c2[rr] * f16_to_f32(cur.a2[rr]);
-        a = prod + ob0.offset;
-      }
+      if constexpr (FMT == kFmtInt4) {
+        const float sc = f16_to_f32(cur.q[rr]);
+        const float z = f16_to_f32(cur.a2[rr]);
 #pragma unroll
-      for (int b = 0; b < B; ++b) val[rr * B + b] = a * part[rr][b];
+        for (int b = 0; b < B; ++b) {
+          const float zt = z * xs[b];
+          val[rr * B + b] = sc * (part[rr][b] - zt);
+        }
+      } else {
+        float a;
+        if constexpr (FMT == kFmtAbsmax32) {
+          a = __builtin_bit_cast(float, cur.q[rr]);
+        } else {
+          const float prod = c2[rr] * f16_to_f32(cur.a2[rr]);
+          a = prod + ob0.offset;
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) val[rr * B + b] = a * part[rr][b];
+      }
     }
     if constexpr (R * B == 2) {
       const float tot = wave_sum_pair(val[0], val[1]);
@@ -795,6 +943,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
       // branch are not assumed outstanding on the common path, where they
       // would make every wait for the current group also wait for the next
       __builtin_amdgcn_s_waitcnt(0);
+      sum_x();
     }
     ob0 = ob1;
     ob1 = ob2;
@@ -871,6 +1020,9 @@ __device__ __forceinline__ void load_wave_group(WaveGroup<R, P, FMT>& g, const L
                                                               kStreamLoad);
       if constexpr (FMT == kFmtAbsmax32) {
         g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b32(mb.absmax_q, blk * 4u, sfar, 0);
+      } else if constexpr (FMT == kFmtInt4) {
+        g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax_q, blk * 2u, sfar, 0);
+        g.a2[rr][p] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, blk * 2u, sfar, 0);
       } else {
         g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, blk, sfar, 0);
         g.a2[rr][p] =
@@ -905,7 +1057,8 @@ template <int B, int R, int P, int FMT>
 __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u32x4 (&xr)[B][P][8],
                                           uint32_t copy_off, const uint2* s_pairs,
                                           const float* s_code2, float offset,
-                                          const bool (&lane_in)[P], float (&val)[R * B]) {
+                                          const bool (&lane_in)[P], const float (&xs)[B][P],
+                                          float (&val)[R * B]) {
   constexpr int U = R * P * 8;
   const char* tab = reinterpret_cast<const char*>(s_pairs);
   uint2 t[2][4];
@@ -915,7 +1068,10 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t addr = __builtin_amdgcn_perm(copy_off, d, 0x0C0C0004u | (uint32_t(i) << 8));
-      tt[i] = *reinterpret_cast<const uint2*>(tab + addr);
+      if constexpr (FMT == kFmtInt4)
+        tt[i].x = *reinterpret_cast<const uint32_t*>(tab + addr);  // one exact code pair
+      else
+        tt[i] = *reinterpret_cast<const uint2*>(tab + addr);
     }
   };
 #pragma unroll
@@ -942,20 +1098,32 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
         const bf16x2 xp = __builtin_bit_cast(bf16x2, xw);
         part[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.x), xp, part[b],
                                                   false);
-        part[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.y), xp, part[b],
-                                                  false);
+        if constexpr (FMT != kFmtInt4)
+          part[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.y), xp,
+                                                    part[b], false);
       }
     }
     if (hj == 7) {
-      float a;
-      if constexpr (FMT == kFmtAbsmax32) {
-        a = __builtin_bit_cast(float, g.q[rr][p]);
-      } else {
-        const float prod = s_code2[g.q[rr][p]] * f16_to_f32(g.a2[rr][p]);
-        a = prod + offset;
-      }
+      if constexpr (FMT == kFmtInt4) {
+        // s (sum q x - z sum x) over the lane's 64 columns of one group
+        const float sc = f16_to_f32(g.q[rr][p]);
+        const float z = f16_to_f32(g.a2[rr][p]);
 #pragma unroll
-      for (int b = 0; b < B; ++b) val[rr * B + b] += lane_in[p] ? a * part[b] : 0.0f;
+        for (int b = 0; b < B; ++b) {
+          const float zt = z * xs[b][p];
+          val[rr * B + b] += lane_in[p] ? sc * (part[b] - zt) : 0.0f;
+        }
+      } else {
+        float a;
+        if constexpr (FMT == kFmtAbsmax32) {
+          a = __builtin_bit_cast(float, g.q[rr][p]);
+        } else {
+          const float prod = s_code2[g.q[rr][p]] * f16_to_f32(g.a2[rr][p]);
+          a = prod + offset;
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) val[rr * B + b] += lane_in[p] ? a * part[b] : 0.0f;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1117,6 +1285,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   load_wave_group<R, P, FMT>(g0, lb0, rl0, len0, wl, K, log2bs, log2s2);
   u32x4 xr[B][P][8];
   load_wave_x<B, P>(xr, x_buf<B>(d0, K), wl, K);
+  float xs[B][P];  // INT4: the lane's activation sums per pass
   const void* x_cur = d0.x;  // activations held in xr
   int mL = m0;
   LoadBufs lbL = lb0;
@@ -1130,8 +1299,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   load_wave_group<R, P, FMT>(g1, lbL, rl1, len1, wl, K, log2bs, log2s2);
 
   if (FMT == kFmtDouble && tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
-  build_pair_table(s_pairs, tid, blockDim.x);
-  const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
+  const uint32_t copy_off = build_decode_table<FMT>(s_pairs, tid, blockDim.x, lane);
+  auto sum_x = [&]() {
+    if constexpr (FMT == kFmtInt4) {
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          uint32_t w[32];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[4 * j + i] = xr[b][p][j][i];
+          xs[b][p] = pair_sum(w);
+        }
+    }
+  };
+  sum_x();
   __syncthreads();
 
   auto step = [&](WaveGroup<R, P, FMT>& cur, WaveGroup<R, P, FMT>& fut) {
@@ -1151,7 +1335,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     // (a chunked range may end inside a round: empty groups skip the work)
     if (len0 > 0) {
       float val[R * B];
-      wave_rows<B, R, P, FMT>(cur, xr, copy_off, s_pairs, s_code2, ob0.offset, lane_in, val);
+      wave_rows<B, R, P, FMT>(cur, xr, copy_off, s_pairs, s_code2, ob0.offset, lane_in, xs, val);
       // value v of the group ends up in lane 32 v (pair) or in row 16-lane
       // row r with v = 2 (r & 1) + (r >> 1) (quad)
       float tot;
@@ -1181,6 +1365,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
         load_wave_x<B, P>(xr, x_buf<B>(d1, K), wl, K);
         x_cur = d1.x;
         __builtin_amdgcn_s_waitcnt(0);  // rare; keeps these loads off the common path's counts
+        sum_x();
       }
     }
     ob0 = ob1;
@@ -1268,6 +1453,9 @@ __global__ __launch_bounds__(512) void gemv_vec_kernel(
       if constexpr (FMT == kFmtAbsmax32) {
         qv[rr] = reinterpret_cast<const uint32_t*>(absmax_q)[blk];
         a2v[rr] = 0.0f;
+      } else if constexpr (FMT == kFmtInt4) {
+        qv[rr] = reinterpret_cast<const uint16_t*>(absmax_q)[blk];  // scale
+        a2v[rr] = f16_to_f32(absmax2[blk]);                          // zero point
       } else {
         qv[rr] = absmax_q[blk];
         a2v[rr] = f16_to_f32(absmax2[blk >> log2s2]);
@@ -1280,13 +1468,15 @@ __global__ __launch_bounds__(512) void gemv_vec_kernel(
   }
   if constexpr (FMT == kFmtDouble)
     for (int i = threadIdx.x; i < 256; i += blockDim.x) s_code2[i] = f16_to_f32(code2[i]);
-  if (threadIdx.x < 16) s_nf4[threadIdx.x] = nf4_value(threadIdx.x);
+  if (threadIdx.x < 16) s_nf4[threadIdx.x] = code_value<FMT>(threadIdx.x);
   __syncthreads();
   float a[R];
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     if constexpr (FMT == kFmtAbsmax32) {
       a[rr] = __builtin_bit_cast(float, qv[rr]);
+    } else if constexpr (FMT == kFmtInt4) {
+      a[rr] = f16_to_f32(static_cast<uint16_t>(qv[rr]));
     } else {
       const float prod = s_code2[qv[rr]] * a2v[rr];
       a[rr] = prod + offset;
@@ -1322,8 +1512,14 @@ __global__ __launch_bounds__(512) void gemv_vec_kernel(
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
         const uint32_t wd = j == 0 ? pk[rr].x : j == 1 ? pk[rr].y : j == 2 ? pk[rr].z : pk[rr].w;
-        const float te = s_nf4[(wd >> (8 * i + 4)) & 15u];
-        const float to = s_nf4[(wd >> (8 * i)) & 15u];
+        float te, to;
+        if constexpr (FMT == kFmtInt4) {  // (q - z), exact; the scale comes after the sum
+          te = s_nf4[(wd >> (8 * i)) & 15u] - a2v[rr];
+          to = s_nf4[(wd >> (8 * i + 4)) & 15u] - a2v[rr];
+        } else {
+          te = s_nf4[(wd >> (8 * i + 4)) & 15u];
+          to = s_nf4[(wd >> (8 * i)) & 15u];
+        }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           part[rr][b] = __builtin_fmaf(te, xe[b], part[rr][b]);
@@ -1362,7 +1558,7 @@ __global__ __launch_bounds__(256) void gemv_any_kernel(
     int64_t N, int64_t K, int log2bs, int log2s2, const uint16_t* __restrict__ x,
     uint16_t* __restrict__ y) {
   __shared__ float s_nf4[16];
-  if (threadIdx.x < 16) s_nf4[threadIdx.x] = nf4_value(threadIdx.x);
+  if (threadIdx.x < 16) s_nf4[threadIdx.x] = code_value<FMT>(threadIdx.x);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -1373,10 +1569,10 @@ __global__ __launch_bounds__(256) void gemv_any_kernel(
   for (int64_t k = 2 * lane; k < K; k += 128) {
     const int64_t e = r * K + k;
     const uint8_t byte = packed8[e >> 1];
-    const float ve = s_nf4[byte >> 4] *
-                     block_scale<FMT>(absmax_q, absmax2, code2, offset, e >> log2bs, log2s2);
-    const float vo = s_nf4[byte & 15u] *
-                     block_scale<FMT>(absmax_q, absmax2, code2, offset, (e + 1) >> log2bs, log2s2);
+    const float ve = element_value<FMT>(s_nf4, nibble_of<FMT>(byte, 0), absmax_q, absmax2, code2,
+                                        offset, e >> log2bs, log2s2);
+    const float vo = element_value<FMT>(s_nf4, nibble_of<FMT>(byte, 1), absmax_q, absmax2, code2,
+                                        offset, (e + 1) >> log2bs, log2s2);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const float x0 = __builtin_bit_cast(float, static_cast<uint32_t>(x[b * K + k]) << 16);
@@ -1732,6 +1928,52 @@ nf4_status nf4_gemv_absmax32(const uint8_t* packed, const float* absmax, int64_t
     NF4_GEMV_SL_CASE(7)
     NF4_GEMV_SL_CASE(8)
 #undef NF4_GEMV_SL_CASE
+  }
+  return NF4_EINVAL;
+}
+
+nf4_status int4_dequant(const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                        int64_t n, int32_t group_size, void* out, int32_t out_dtype,
+                        void* stream) {
+  int lg = 0;
+  if (n < 0 || !pow2_log2(group_size, &lg) || lg < 1) return NF4_EINVAL;
+  if (out_dtype != NF4_BF16 && out_dtype != NF4_FP16) return NF4_EINVAL;
+  if (n == 0) return NF4_OK;
+  if (!packed || !scales || !zeros || !out) return NF4_EINVAL;
+  if (n >= kMaxElems) return NF4_EUNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* sc = reinterpret_cast<const uint8_t*>(scales);
+  if (out_dtype == NF4_BF16)
+    return dequant_launch<NF4_BF16, kFmtInt4>(packed, sc, zeros, nullptr, 0.0f, n, lg, 0, out, st);
+  return dequant_launch<NF4_FP16, kFmtInt4>(packed, sc, zeros, nullptr, 0.0f, n, lg, 0, out, st);
+}
+
+nf4_status int4_gemv(const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                     int64_t N, int64_t K, int32_t group_size, const uint16_t* x, int32_t batch,
+                     uint16_t* y, void* stream) {
+  int lg = 0;
+  if (N < 0 || K < 0 || (K & 1) || batch < 1 || batch > 8) return NF4_EINVAL;
+  if (!pow2_log2(group_size, &lg) || lg < 1) return NF4_EINVAL;
+  if (N == 0) return NF4_OK;
+  if (!y) return NF4_EINVAL;
+  if (K == 0) return gemv_fill_zero(y, N, batch, reinterpret_cast<hipStream_t>(stream));
+  if (!packed || !scales || !zeros || !x) return NF4_EINVAL;
+  if (N > kMaxElems / K) return NF4_EUNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* sc = reinterpret_cast<const uint8_t*>(scales);
+  switch (batch) {
+#define INT4_GEMV_CASE(BB) \
+  case BB:                 \
+    return gemv_launch_b<BB, kFmtInt4>(packed, sc, zeros, nullptr, 0.0f, N, K, lg, 0, x, y, st);
+    INT4_GEMV_CASE(1)
+    INT4_GEMV_CASE(2)
+    INT4_GEMV_CASE(3)
+    INT4_GEMV_CASE(4)
+    INT4_GEMV_CASE(5)
+    INT4_GEMV_CASE(6)
+    INT4_GEMV_CASE(7)
+    INT4_GEMV_CASE(8)
+#undef INT4_GEMV_CASE
   }
   return NF4_EINVAL;
 }

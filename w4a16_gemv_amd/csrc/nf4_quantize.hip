@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "int4.h"
 #include "nf4.h"
 #include "nf4_device.h"
 
@@ -161,6 +162,54 @@ __global__ __launch_bounds__(kThreads) void pack_codes_kernel(const float* __res
   }
 }
 
+// The INT4 asymmetric group encoder ([handbook] "量化公式"): one thread per
+// group of 2^lg elements (lg >= 1, so no byte is shared by two groups).
+// Readings: s = fp16(fp32(max - min) / 15), replaced by 1 when it is 0;
+// z = round(-min / s) with the stored s, kept as fp16; q = clamp(round(w / s)
+// + z, 0, 15); round is to nearest, halves away from zero; the first element
+// of each byte goes to the low nibble.
+__global__ __launch_bounds__(kThreads) void int4_group_kernel(const float* __restrict__ w,
+                                                               int64_t n, int lg,
+                                                               uint8_t* __restrict__ packed,
+                                                               uint16_t* __restrict__ scales,
+                                                               uint16_t* __restrict__ zeros) {
+  const int64_t ng = ((n - 1) >> lg) + 1;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; g < ng;
+       g += stride) {
+    const int64_t e0 = g << lg;
+    const int64_t e1 = (g + 1) << lg < n ? (g + 1) << lg : n;
+    float mn = w[e0], mx = w[e0];
+    for (int64_t e = e0 + 1; e < e1; ++e) {
+      const float v = w[e];
+      if (v < mn) mn = v;
+      if (v > mx) mx = v;
+    }
+    const float range = mx - mn;
+    uint16_t s16 = to_half_bits<NF4_FP16>(range / 15.0f);
+    float s = f16_to_f32(s16);
+    if (s == 0.0f) {
+      s16 = 0x3C00u;  // 1.0
+      s = 1.0f;
+    }
+    const uint16_t z16 = to_half_bits<NF4_FP16>(roundf(-mn / s));
+    const float z = f16_to_f32(z16);
+    scales[g] = s16;
+    zeros[g] = z16;
+    for (int64_t e = e0; e < e1; e += 2) {
+      uint32_t code[2] = {0u, 0u};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (e + h >= e1) continue;  // pad nibble of an odd-length tensor
+        float q = roundf(w[e + h] / s) + z;
+        q = q < 0.0f ? 0.0f : (q > 15.0f ? 15.0f : q);
+        code[h] = static_cast<uint32_t>(q);
+      }
+      packed[e >> 1] = static_cast<uint8_t>(code[0] | (code[1] << 4));
+    }
+  }
+}
+
 bool pow2_log2(int32_t v, int* lg) {
   if (v < 1 || v > (1 << 30) || (v & (v - 1)) != 0) return false;
   int l = 0;
@@ -236,6 +285,19 @@ nf4_status nf4_quantize_absmax32(const float* w, int64_t n, int32_t blocksize, u
                      absmax);
   hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for((n + 1) / 2)), dim3(kThreads), 0, st, w, n,
                      lbs, absmax, packed);
+  return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+nf4_status int4_quantize(const float* w, int64_t n, int32_t group_size, uint8_t* packed,
+                         uint16_t* scales, uint16_t* zeros, void* stream) {
+  int lg = 0;
+  if (n < 0 || !pow2_log2(group_size, &lg) || lg < 1) return NF4_EINVAL;
+  if (n == 0) return NF4_OK;
+  if (!w || !packed || !scales || !zeros) return NF4_EINVAL;
+  if (n >= (int64_t(1) << 40)) return NF4_EUNSUPPORTED;
+  const int64_t ng = ((n - 1) >> lg) + 1;
+  hipLaunchKernelGGL(int4_group_kernel, dim3(grid_for(ng)), dim3(kThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), w, n, lg, packed, scales, zeros);
   return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 

@@ -30,7 +30,8 @@ dequant), qwen_b1 (the 7 Qwen2.5-1.5B-shaped GEMVs), llama_b1 / llama_b4 /
 llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8), and each of these
 with the suffix _absmax32 for the single-level format (one fp32 absmax per
 block: nf4_dequant_absmax32 / nf4_gemv_absmax32, encoded by
-nf4_quantize_absmax32).  These run one
+nf4_quantize_absmax32) or _int4 for the INT4 asymmetric group format
+(int4_dequant / int4_gemv, group 128, encoded by int4_quantize).  These run one
 nf4_dequant / nf4_gemv call per matrix over copies of the encoded data rotated
 so that every step reads past the 256 MB MALL (cold HBM), timed from HIP
 graphs, and report the kernel of their largest matrix as the dominant one.
@@ -43,7 +44,8 @@ on the current kernel source; the CPU oracle timed on a bounded sample of the
 same workload.
 Algorithmic bytes: dequant ceil(n/2) + ceil(n/64) + 2 ceil(n/16384) + 516 + 2n;
 GEMV ceil(NK/2) + ceil(NK/64) + 2 ceil(NK/16384) + 516 + 2KB + 2NB; in the
-single-level format 4 ceil(n/64) bytes of scales replace the second-level terms.
+single-level format 4 ceil(n/64) bytes of scales replace the second-level terms,
+in the INT4 format 4 ceil(n/G) bytes of fp16 scales and zero points.
 """
 import argparse
 import hashlib
@@ -200,7 +202,7 @@ MALL_BYTES = 256 << 20
 VALU_PEAK_TFLOPS = 157.3
 
 
-def build_context(dev, name, bs=64):
+def build_context(dev, name, bs=None):
     """One of the smaller configurations, encoded once and copied into enough
     sets that one pass over all sets reads more than twice the MALL.
     Returns dict(sets, step_bytes, flops, launches, dominant, run)."""
@@ -210,8 +212,17 @@ def build_context(dev, name, bs=64):
     import w4a16_gemv_amd as nf4
     code2 = nf4.nf4_code2_linear().to(dev)
     single = name.endswith("_absmax32")        # the single-level format
-    base_name = name[: -len("_absmax32")] if single else name
-    if single:
+    int4 = name.endswith("_int4")              # the INT4 asymmetric group format
+    base_name = name.rsplit("_", 1)[0] if (single or int4) else name
+    if bs is None:
+        bs = 128 if int4 else 64
+    if int4:
+        def dq_bytes(n):
+            return (n + 1) // 2 + 4 * -(-n // bs) + 2 * n
+
+        def gv_bytes(N, K, B):
+            return (N * K + 1) // 2 + 4 * -(-N * K // bs) + 2 * K * B + 2 * N * B
+    elif single:
         def dq_bytes(n):
             return (n + 1) // 2 + 4 * -(-n // bs) + 2 * n
 
@@ -227,7 +238,9 @@ def build_context(dev, name, bs=64):
 
     def encode(seed, n, outliers=False):
         w = synth.weights_device(seed, n, dev, outliers=outliers)
-        if single:
+        if int4:
+            t = nf4.int4_quantize(w, bs)
+        elif single:
             t = nf4.nf4_quantize_absmax32(w, bs)
         else:
             ws = torch.empty(nf4.load().nf4_quantize_workspace_size(n, bs), dtype=torch.uint8,
@@ -238,6 +251,9 @@ def build_context(dev, name, bs=64):
         return t
 
     def clone(t):
+        if int4:
+            return nf4.Int4Tensor(t.packed.clone(), t.scales.clone(), t.zeros.clone(), t.n,
+                                  t.group_size)
         if single:
             return nf4.NF4Absmax32Tensor(t.packed.clone(), t.absmax.clone(), t.n, t.blocksize)
         return nf4.NF4Tensor(t.packed.clone(), t.absmax_q.clone(), t.absmax2.clone(), t.code2,
@@ -255,9 +271,9 @@ def build_context(dev, name, bs=64):
         def run(st, dominant_only=False):
             t, out = st
             t.dequant(out=out)
-        return dict(sets=sets, step_bytes=set_bytes, flops=0, launches=1, run=run,
+        return dict(sets=sets, step_bytes=set_bytes, flops=0, launches=1, run=run, blocksize=bs,
                     dominant=f"dequant_vec_kernel ({cfg.rows}x{cfg.cols}"
-                             f"{', fp32 absmax' if single else ''})",
+                             f"{', fp32 absmax' if single else ''}{', int4' if int4 else ''})",
                     dominant_bytes=set_bytes, dominant_flops=0)
 
     if base_name == "qwen_b1":
@@ -281,9 +297,9 @@ def build_context(dev, name, bs=64):
             if not dominant_only or i == dom:
                 t.gemv(g.N, g.K, xs[g.K], y)
     return dict(sets=sets, step_bytes=set_bytes, flops=sum(2 * g.N * g.K * batch for g in gemvs),
-                launches=len(gemvs), run=run, batch=batch,
-                dominant=f"{'nf4_gemv_absmax32' if single else 'nf4_gemv'} {gd.N}x{gd.K} "
-                         f"batch {batch}",
+                launches=len(gemvs), run=run, batch=batch, blocksize=bs,
+                dominant=f"{'int4_gemv' if int4 else 'nf4_gemv_absmax32' if single else 'nf4_gemv'}"
+                         f" {gd.N}x{gd.K} batch {batch}",
                 dominant_bytes=gv_bytes(gd.N, gd.K, batch), dominant_flops=2 * gd.N * gd.K * batch)
 
 
@@ -294,6 +310,7 @@ def bench_context(args, dev):
     over every set.  Per step / per launch = graph time / number of sets."""
     import torch
     wl = build_context(dev, args.workload, args.blocksize)
+    args.blocksize = wl["blocksize"]
     sets = wl["sets"]
     stream = torch.cuda.Stream(dev)
 
@@ -379,9 +396,11 @@ def main():
     ap.add_argument("--schedule", choices=("stream", "layered"), default="stream")
     ap.add_argument("--workload", default="sweep",
                     choices=("sweep",) + CONTEXT_WORKLOADS
-                    + tuple(w + "_absmax32" for w in CONTEXT_WORKLOADS))
-    ap.add_argument("--blocksize", type=int, default=64,
-                    help="first-level block size of the context workloads (the sweep uses 64)")
+                    + tuple(w + "_absmax32" for w in CONTEXT_WORKLOADS)
+                    + tuple(w + "_int4" for w in CONTEXT_WORKLOADS))
+    ap.add_argument("--blocksize", type=int, default=None,
+                    help="block (group) size of the context workloads: default 64, 128 for the "
+                         "_int4 workloads (the sweep always uses 64)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--prewarm", type=float, default=1.0,
                     help="seconds of untimed steps before the W warm-up steps")
@@ -411,7 +430,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic",
             "config": {"workload": args.workload, "batch": r["batch"], "blocksize": args.blocksize,
-                       "s2_blocksize": None if args.workload.endswith("_absmax32") else 256,
+                       "s2_blocksize": None if args.workload.endswith(("_absmax32", "_int4"))
+                       else 256,
                        "launches_per_step": r["launches"],
                        "bytes_per_step": r["step_bytes"], "rotating_sets": r["sets"],
                        "prewarm_s": args.prewarm},

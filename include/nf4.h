@@ -172,6 +172,33 @@ nf4_status nf4_gemv_absmax32(const uint8_t* packed, const float* absmax, int64_t
                              void* stream);
 
 /*
+ * nf4_gemm -- the product for any number of batch rows (prefill and batches
+ * past 8): y[m][n] = sum_k value(n*K + k) * x[m][k], m < M.  Batch growth
+ * makes the product compute-bound, so it runs on the matrix cores (bf16
+ * MFMA with exact products and fp32 sums).  Defined as nf4_gemv; [quanttax]
+ * "Kernel 实现" and its conclusions on prefill, [handbook] batch sensitivity.
+ *
+ *  packed, absmax_q, absmax2, code2, offset, N, K, blocksize, s2_blocksize :
+ *                  as for nf4_gemv.
+ *  M             : batch rows, 0 <= M < 2^27.
+ *  x             : device bf16 bits [M][K], row-major.
+ *  y             : device bf16 bits [M][N], row-major.
+ *  stream        : hipStream_t.
+ * The fast path needs K % 64 == 0, blocksize >= 64, packed 8-byte and x
+ * 16-byte aligned, N*K < 2^31 and (M + 64) K < 2^30; other shapes run the
+ * GEMV over chunks of 8 rows, with the same tolerance.  Weights are never
+ * rounded to 16 bits (each NF4 value enters as the sum of two bf16 values,
+ * within 2^-16 of it) and sums are fp32: each output is the bf16 rounding of
+ * a value within 2^-14 * sum_k |w x| of the exact sum.  Deterministic.
+ * Returns NF4_EINVAL for NULL pointers with M*N*K > 0, negative sizes, odd K
+ * or bad block sizes.
+ */
+nf4_status nf4_gemm(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
+                    const uint16_t* code2, float offset, int64_t M, int64_t N, int64_t K,
+                    int32_t blocksize, int32_t s2_blocksize, const uint16_t* x, uint16_t* y,
+                    void* stream);
+
+/*
  * One matrix of a grouped GEMV (64 bytes; all pointers are device pointers).
  */
 typedef struct nf4_gemv_desc {

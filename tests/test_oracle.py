@@ -429,7 +429,7 @@ def test_gemv_one_hot_reproduces_columns():
         assert np.array_equal(S[0], np.abs(W[:, k]).astype(np.float64))
 
 
-@pytest.mark.parametrize("N,K,B", [(64, 512, 1), (33, 1536, 4), (7, 128, 8)])
+@pytest.mark.parametrize("N,K,B", [(64, 512, 1), (33, 1536, 4), (7, 128, 8), (20, 256, 33)])
 def test_gemv_matches_float64_matmul(N, K, B):
     q = oracle.quantize(synth.weights(N + K, N * K), 64, 8)
     W = oracle.dequant_f32(q).reshape(N, K).astype(np.float64)

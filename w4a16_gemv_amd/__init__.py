@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     nf4_code2_linear,
     nf4_dequant,
     nf4_dequant_absmax32,
+    nf4_gemm,
     nf4_gemv,
     nf4_gemv_absmax32,
     nf4_quantize,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libnf4.so")
 NF4_OK, NF4_EINVAL, NF4_EUNSUPPORTED, NF4_EHIP = 0, 1, 2, 3
 NF4_BF16, NF4_FP16 = 0, 1
 
-EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv",
+EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv", "nf4_gemm",
             "nf4_dequant_absmax32", "nf4_gemv_absmax32", "nf4_gemv_grouped",
             "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
             "nf4_quantize", "nf4_quantize_absmax32", "int4_dequant", "int4_gemv",
@@ -55,6 +55,8 @@ def load() -> C.CDLL:
     lib.nf4_dequant_absmax32.argtypes = [p, p, i64, i32, p, i32, p]
     lib.nf4_gemv_absmax32.restype = C.c_int
     lib.nf4_gemv_absmax32.argtypes = [p, p, i64, i64, i32, p, i32, p, p]
+    lib.nf4_gemm.restype = C.c_int
+    lib.nf4_gemm.argtypes = [p, p, p, p, f32, i64, i64, i64, i32, i32, p, p, p]
     lib.nf4_gemv_grouped.restype = C.c_int
     lib.nf4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, i32, p, C.c_size_t, p]
     lib.nf4_gemv_sched_size.restype = C.c_size_t
@@ -153,6 +155,27 @@ def nf4_gemv(packed, absmax_q, absmax2, code2, offset: float, N: int, K: int, x:
     return y.view(int(N)) if squeeze and y.dim() == 2 else y
 
 
+def nf4_gemm(packed, absmax_q, absmax2, code2, offset: float, N: int, K: int, x: torch.Tensor,
+             blocksize: int = 64, s2_blocksize: int = 256,
+             y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[m][n] = sum_k W[n][k] x[m][k] for any number of rows M of x (bf16
+    [M][K]); returns y bf16 [M][N].  The matrix-core path for batches past 8."""
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [M, {K}], got shape {tuple(x.shape)}")
+    M = x.shape[0]
+    nbytes, nb, ng = format_sizes(int(N) * int(K), int(blocksize), int(s2_blocksize))
+    if y is None:
+        y = torch.empty(M, int(N), dtype=torch.bfloat16, device=x.device)
+    args = (_dev(packed, "packed", _U8, nbytes), _dev(absmax_q, "absmax_q", _U8, nb),
+            _dev(absmax2, "absmax2", _HALF_BITS, ng), _dev(code2, "code2", _HALF_BITS, 256))
+    px = _dev(x, "x", _BF16_BITS, M * int(K))
+    py = _dev(y, "y", _BF16_BITS, M * int(N))
+    st = load().nf4_gemm(*args, C.c_float(offset), int(M), int(N), int(K), int(blocksize),
+                         int(s2_blocksize), px, py, _stream(y))
+    _check("nf4_gemm", st)
+    return y
+
+
 _F32 = (torch.float32,)
 
 
@@ -240,6 +263,12 @@ class NF4Tensor:
         if N * K != self.n:
             raise ValueError(f"N*K={N * K} does not match the tensor's {self.n} elements")
         return nf4_gemv(self.packed, self.absmax_q, self.absmax2, self.code2, self.offset, N, K,
+                        x, self.blocksize, self.s2_blocksize, y)
+
+    def gemm(self, N: int, K: int, x, y=None):
+        if N * K != self.n:
+            raise ValueError(f"N*K={N * K} does not match the tensor's {self.n} elements")
+        return nf4_gemm(self.packed, self.absmax_q, self.absmax2, self.code2, self.offset, N, K,
                         x, self.blocksize, self.s2_blocksize, y)
 
 

@@ -1588,6 +1588,187 @@ __global__ __launch_bounds__(256) void gemv_any_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batched NF4 W4A16 GEMM on the matrix cores (batch 9 and up, prefill):
+// y[m][n] = sum_k value(n K + k) * x[m][k].
+//
+// v_mfma_f32_16x16x32_bf16 with the activations as A (16 batch rows x 32 k)
+// and the decoded weights as B (32 k x 16 columns n).  Lane layout (checked on
+// gfx950): A lane i + 16 g holds A[i][8 g .. 8 g + 7], B lane j + 16 g holds
+// B[8 g .. 8 g + 7][j], D lane j + 16 g holds D[4 g .. 4 g + 3][j] -- so a
+// lane's B column is also its D column.
+//
+// A workgroup of four waves owns 16 columns and up to 16 MT batch rows; the
+// waves split K into quarters.  Per 64-column block (one NF4 block of each
+// column: blocksize >= 64, K % 64 == 0) lane (j, g) loads the 8 packed bytes
+// of columns [16 g, 16 g + 16) of row n0 + j and decodes them through the pair
+// table into the bf16 hi pairs and lo pairs (hi + lo within 2^-16 of the NF4
+// value), read as separate dwords so they land in the MFMA operand registers.
+// Two k-steps of 32 times (hi, lo) are four MFMAs per 16-row tile, summed
+// unscaled; the block's absmax_real of column n then multiplies that sum into
+// the lane's fp32 accumulator (scale after accumulate, as in the GEMV).  The
+// four waves' accumulators meet in LDS in a fixed order: deterministic.
+// Loads of the next block are issued before the current one is computed.
+// Requirements (checked on the host): K % 64 == 0, blocksize >= 64, packed
+// 8-byte aligned, x 16-byte aligned, N K < 2^31, M K < 2^30.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kGemmWaves = 4;
+
+template <int MT>
+struct GemmStage {
+  uint2 w;            // 8 packed bytes of the lane's column and k-group
+  uint8_t q;          // absmax_q of the block
+  uint16_t a2;        // absmax2 of its group
+  u32x4 xa[MT][2];    // activations: tile mt, k-step t (8 bf16)
+};
+
+template <int MT>
+__device__ __forceinline__ void gemm_load(GemmStage<MT>& st, int kb, bool live,
+                                          __amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rq,
+                                          __amdgpu_buffer_rsrc_t ra2, __amdgpu_buffer_rsrc_t rx,
+                                          uint32_t wrow, uint32_t blk_row, int g, uint32_t xoff,
+                                          int K, int log2bs, int log2s2) {
+  const uint32_t far = live ? 0u : kFar;
+  const uint32_t kcol = static_cast<uint32_t>(kb) * 64u;
+  const uint32_t wo = wrow + kcol / 2u + 8u * static_cast<uint32_t>(g);
+  st.w.x = __builtin_amdgcn_raw_buffer_load_b32(rp, wo, far, kStreamLoad);
+  st.w.y = __builtin_amdgcn_raw_buffer_load_b32(rp, wo + 4u, far, kStreamLoad);
+  const uint32_t blk = (blk_row + kcol) >> log2bs;
+  st.q = __builtin_amdgcn_raw_buffer_load_b8(rq, blk, far, 0);
+  st.a2 = __builtin_amdgcn_raw_buffer_load_b16(ra2, (blk >> log2s2) * 2u, far, 0);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      st.xa[mt][t] = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, xoff + (static_cast<uint32_t>(mt) * 16u * static_cast<uint32_t>(K) + kcol +
+                      16u * static_cast<uint32_t>(g) + 8u * t) * 2u,
+          far, 0);
+}
+
+template <int MT>
+__device__ __forceinline__ void gemm_block(const GemmStage<MT>& st, const char* tab,
+                                           uint32_t copy_off, const float* s_code2, float offset,
+                                           f32x4 (&acc)[MT]) {
+  // B operands: byte 4 t + e of the lane's 8 bytes holds k 8 t + 2 e, + 1
+  uint32_t bh[2][4], bl[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t word = t == 0 ? st.w.x : st.w.y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t addr = __builtin_amdgcn_perm(copy_off, word, 0x0C0C0004u | (uint32_t(e) << 8));
+      bh[t][e] = *reinterpret_cast<const uint32_t*>(tab + addr);
+      bl[t][e] = *reinterpret_cast<const uint32_t*>(tab + addr + 4);
+    }
+  }
+  const float prod = s_code2[st.q] * f16_to_f32(st.a2);
+  const float a = prod + offset;
+  bf16x8 bhv[2], blv[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const u32x4 h = {bh[t][0], bh[t][1], bh[t][2], bh[t][3]};
+    const u32x4 l = {bl[t][0], bl[t][1], bl[t][2], bl[t][3]};
+    bhv[t] = __builtin_bit_cast(bf16x8, h);
+    blv[t] = __builtin_bit_cast(bf16x8, l);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const bf16x8 x0 = __builtin_bit_cast(bf16x8, st.xa[mt][0]);
+    const bf16x8 x1 = __builtin_bit_cast(bf16x8, st.xa[mt][1]);
+    f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, bhv[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, blv[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, bhv[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, blv[1], c, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[mt][r] += a * c[r];
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * kGemmWaves) void gemm_mfma_kernel(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ absmax_q,
+    const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset, int M,
+    int N, int K, int log2bs, int log2s2, const uint16_t* __restrict__ x,
+    uint16_t* __restrict__ y) {
+  __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
+  __shared__ float s_code2[256];
+  __shared__ f32x4 s_red[kGemmWaves - 1][MT][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int n = blockIdx.x * 16 + j;
+  const int m0 = blockIdx.y * 16 * MT;
+
+  const uint64_t nk = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
+  const uint64_t nb = ((nk - 1) >> log2bs) + 1;
+  const uint64_t ng = ((nb - 1) >> log2s2) + 1;
+  const auto rp = rsrc(packed, static_cast<uint32_t>(nk >> 1));
+  const auto rq = rsrc(absmax_q, static_cast<uint32_t>(nb));
+  const auto ra2 = rsrc(absmax2, static_cast<uint32_t>(ng * 2));
+  const auto rx = rsrc(x, static_cast<uint32_t>(static_cast<uint64_t>(M) * K * 2));
+  // the lane's weight row (pushed out of range past N) and its activation row
+  const uint32_t wrow = n < N ? static_cast<uint32_t>(n) * static_cast<uint32_t>(K >> 1) : kFar;
+  const uint32_t blk_row = static_cast<uint32_t>(n < N ? n : 0) * static_cast<uint32_t>(K);
+  const uint32_t xoff = static_cast<uint32_t>(m0 + j) * static_cast<uint32_t>(K) * 2u;
+
+  if (tid < 256) s_code2[tid] = f16_to_f32(code2[tid]);
+  build_pair_table(s_pairs, tid, blockDim.x);
+  const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
+  __syncthreads();
+  const char* tab = reinterpret_cast<const char*>(s_pairs);
+
+  // the wave's quarter of the K blocks
+  const int nkb = K >> 6;
+  const int kb0 = wave * nkb / kGemmWaves, kb1 = (wave + 1) * nkb / kGemmWaves;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  GemmStage<MT> s0, s1;
+  gemm_load<MT>(s0, kb0, kb0 < kb1, rp, rq, ra2, rx, wrow, blk_row, g, xoff, K, log2bs, log2s2);
+  // two blocks per round, the loads of block kb + 1 issued before block kb is
+  // computed; the round's second half loads past kb1 only as dead (out of
+  // range) loads, so every round has the same shape
+  for (int kb = kb0; kb < kb1; kb += 2) {
+    gemm_load<MT>(s1, kb + 1, kb + 1 < kb1, rp, rq, ra2, rx, wrow, blk_row, g, xoff, K, log2bs,
+                  log2s2);
+    gemm_block<MT>(s0, tab, copy_off, s_code2, offset, acc);
+    gemm_load<MT>(s0, kb + 2, kb + 2 < kb1, rp, rq, ra2, rx, wrow, blk_row, g, xoff, K, log2bs,
+                  log2s2);
+    if (kb + 1 < kb1) gemm_block<MT>(s1, tab, copy_off, s_code2, offset, acc);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // fixed-order sum of the four waves' accumulators, then one bf16 store per
+  // output (rows 4 g + r of each tile, column n)
+  if (wave > 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) s_red[wave - 1][mt][lane] = acc[mt];
+  }
+  __syncthreads();
+  if (wave == 0 && n < N) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 v = acc[mt];
+#pragma unroll
+      for (int w = 0; w < kGemmWaves - 1; ++w) {
+        const f32x4 p = s_red[w][mt][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += p[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * mt + 4 * g + r;
+        if (m < M) y[static_cast<int64_t>(m) * N + n] = to_half_bits<NF4_BF16>(v[r]);
+      }
+    }
+  }
+}
+
 // y = 0 for an empty reduction (K == 0).
 __global__ void fill_zero_kernel(uint16_t* __restrict__ y, int64_t count) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -1810,6 +1991,28 @@ nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const u
   return launch_status();
 }
 
+// The MFMA GEMM over all M batch rows: up to 64 rows per workgroup (MT tiles
+// of 16), 16 columns per workgroup.
+nf4_status gemm_launch(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
+                       const uint16_t* code2, float offset, int64_t M, int64_t N, int64_t K,
+                       int lbs, int ls2, const uint16_t* x, uint16_t* y, hipStream_t st) {
+  const int64_t tiles = (M + 15) / 16;
+  const int MT = tiles >= 4 ? 4 : static_cast<int>(tiles);
+  const int64_t gy = (M + 16 * MT - 1) / (16 * MT);
+  const int64_t gx = (N + 15) / 16;
+  if (gy > 65535 || gx > 0x7FFFFFFF) return NF4_EUNSUPPORTED;
+  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy));
+  const dim3 block(64 * kGemmWaves);
+  const int m = static_cast<int>(M), nn = static_cast<int>(N), k = static_cast<int>(K);
+  switch (MT) {
+    case 1: hipLaunchKernelGGL(gemm_mfma_kernel<1>, grid, block, 0, st, packed, absmax_q, absmax2, code2, offset, m, nn, k, lbs, ls2, x, y); break;
+    case 2: hipLaunchKernelGGL(gemm_mfma_kernel<2>, grid, block, 0, st, packed, absmax_q, absmax2, code2, offset, m, nn, k, lbs, ls2, x, y); break;
+    case 3: hipLaunchKernelGGL(gemm_mfma_kernel<3>, grid, block, 0, st, packed, absmax_q, absmax2, code2, offset, m, nn, k, lbs, ls2, x, y); break;
+    default: hipLaunchKernelGGL(gemm_mfma_kernel<4>, grid, block, 0, st, packed, absmax_q, absmax2, code2, offset, m, nn, k, lbs, ls2, x, y); break;
+  }
+  return launch_status();
+}
+
 // y = +0 for N x batch outputs (empty sums, K == 0).
 nf4_status gemv_fill_zero(uint16_t* y, int64_t N, int32_t batch, hipStream_t st) {
   if (N > kMaxElems) return NF4_EUNSUPPORTED;
@@ -1882,6 +2085,54 @@ nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16
 #undef NF4_GEMV_CASE
   }
   return NF4_EINVAL;
+}
+
+nf4_status nf4_gemm(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
+                    const uint16_t* code2, float offset, int64_t M, int64_t N, int64_t K,
+                    int32_t blocksize, int32_t s2_blocksize, const uint16_t* x, uint16_t* y,
+                    void* stream) {
+  int lbs = 0, ls2 = 0;
+  if (M < 0 || N < 0 || K < 0 || (K & 1)) return NF4_EINVAL;
+  if (!pow2_log2(blocksize, &lbs) || !pow2_log2(s2_blocksize, &ls2)) return NF4_EINVAL;
+  if (M == 0 || N == 0) return NF4_OK;
+  if (!y) return NF4_EINVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (M > (int64_t(1) << 31) / 16) return NF4_EUNSUPPORTED;
+  if (K == 0) {
+    if (N > kMaxElems / M) return NF4_EUNSUPPORTED;
+    return gemv_fill_zero(y, M * N, 1, st);
+  }
+  if (!packed || !absmax_q || !absmax2 || !code2 || !x) return NF4_EINVAL;
+  if (N > kMaxElems / K) return NF4_EUNSUPPORTED;
+  const bool fast = K % 64 == 0 && lbs >= 6 && aligned(packed, 8) && aligned(x, 16) &&
+                    N * K < (int64_t(1) << 31) && (M + 64) * K * 2 < (int64_t(1) << 31);
+  if (fast)
+    return gemm_launch(packed, absmax_q, absmax2, code2, offset, M, N, K, lbs, ls2, x, y, st);
+  // anything else: the GEMV over batch chunks of up to 8 rows
+  for (int64_t m0 = 0; m0 < M; m0 += 8) {
+    const int64_t b = M - m0 < 8 ? M - m0 : 8;
+    const uint16_t* xc = x + m0 * K;
+    uint16_t* yc = y + m0 * N;
+    nf4_status r = NF4_OK;
+    switch (b) {
+#define NF4_GEMM_CHUNK(BB)                                                                        \
+  case BB:                                                                                        \
+    r = gemv_launch_b<BB, kFmtDouble>(packed, absmax_q, absmax2, code2, offset, N, K, lbs, ls2, \
+                                      xc, yc, st);                                                \
+    break;
+      NF4_GEMM_CHUNK(1)
+      NF4_GEMM_CHUNK(2)
+      NF4_GEMM_CHUNK(3)
+      NF4_GEMM_CHUNK(4)
+      NF4_GEMM_CHUNK(5)
+      NF4_GEMM_CHUNK(6)
+      NF4_GEMM_CHUNK(7)
+      NF4_GEMM_CHUNK(8)
+#undef NF4_GEMM_CHUNK
+    }
+    if (r != NF4_OK) return r;
+  }
+  return NF4_OK;
 }
 
 nf4_status nf4_dequant_absmax32(const uint8_t* packed, const float* absmax, int64_t n,

@@ -27,8 +27,10 @@ milliseconds of load while its clocks settle.
 --workload picks another configuration as a context measurement (the default
 `sweep` is the headline): dequant_1k / dequant_4k (1024^2 and 4096^2 bf16
 dequant), qwen_b1 (the 7 Qwen2.5-1.5B-shaped GEMVs), llama_b1 / llama_b4 /
-llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8), and each of these
-with the suffix _absmax32 for the single-level format (one fp32 absmax per
+llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8), llama_b16 / llama_b64
+/ llama_b128 (the same 3 matrices times 16, 64, 128 activation rows through
+nf4_gemm, the matrix-core product; roofline against the bf16 MFMA peak), and
+each of the first six with the suffix _absmax32 for the single-level format (one fp32 absmax per
 block: nf4_dequant_absmax32 / nf4_gemv_absmax32, encoded by
 nf4_quantize_absmax32) or _int4 for the INT4 asymmetric group format
 (int4_dequant / int4_gemv, group 128, encoded by int4_quantize).  These run one
@@ -60,6 +62,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 CONTEXT_WORKLOADS = ("dequant_1k", "dequant_4k", "qwen_b1", "llama_b1", "llama_b4", "llama_b8")
+# batched products on the matrix cores (nf4_gemm), double-quantized format only
+GEMM_WORKLOADS = ("llama_b16", "llama_b64", "llama_b128")
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "NF4 dequant & fused GEMV: achieved HBM GB/s and % of MI355X peak (1 GPU)"
 
 
@@ -292,14 +297,25 @@ def build_context(dev, name, bs=None):
     dom = max(range(len(gemvs)), key=lambda i: gemvs[i].N * gemvs[i].K)
     gd = gemvs[dom]
 
+    gemm = batch > 8
+    ws = None
+    if gemm:
+        # one split-K scratch workspace for all the products (serial on one stream)
+        need = max(nf4.load().nf4_gemm_workspace_size(batch, g.N, g.K) for g in gemvs)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
     def run(st, dominant_only=False):
         for i, (g, t, y) in enumerate(st):
             if not dominant_only or i == dom:
-                t.gemv(g.N, g.K, xs[g.K], y)
+                if gemm:
+                    t.gemm(g.N, g.K, xs[g.K], y, workspace=ws)
+                else:
+                    t.gemv(g.N, g.K, xs[g.K], y)
+    kname = ("nf4_gemm" if gemm else "int4_gemv" if int4 else
+             "nf4_gemv_absmax32" if single else "nf4_gemv")
     return dict(sets=sets, step_bytes=set_bytes, flops=sum(2 * g.N * g.K * batch for g in gemvs),
-                launches=len(gemvs), run=run, batch=batch, blocksize=bs,
-                dominant=f"{'int4_gemv' if int4 else 'nf4_gemv_absmax32' if single else 'nf4_gemv'}"
-                         f" {gd.N}x{gd.K} batch {batch}",
+                launches=len(gemvs), run=run, batch=batch, blocksize=bs, gemm=gemm,
+                dominant=f"{kname} {gd.N}x{gd.K} batch {batch}",
                 dominant_bytes=gv_bytes(gd.N, gd.K, batch), dominant_flops=2 * gd.N * gd.K * batch)
 
 
@@ -337,14 +353,26 @@ def bench_context(args, dev):
     roof = {"bound": "hbm", "kernel": wl["dominant"], "achieved": round(dom_gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
             "traffic": None, "bytes_per_launch": wl["dominant_bytes"], "avg_launch_us": round(dom_us, 3)}
-    if wl["dominant_flops"]:
+    if wl.get("gemm"):
+        # a contraction on the matrix cores: useful flops 2 M N K against the
+        # dense bf16 MFMA peak (the exact hi + lo weight split issues twice that)
+        tf = wl["dominant_flops"] / (dom_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": wl["dominant"], "achieved": round(tf, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": wl["dominant_flops"], "avg_launch_us": round(dom_us, 3),
+                "hbm": {"achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                        "bytes_per_launch": wl["dominant_bytes"]}}
+    elif wl["dominant_flops"]:
         tf = wl["dominant_flops"] / (dom_us * 1e-6) / 1e12
         roof["alu"] = {"achieved_tflops": round(tf, 2), "peak_tflops": VALU_PEAK_TFLOPS,
                        "frac": round(tf / VALU_PEAK_TFLOPS, 4)}
     log(f"[bench] {args.workload}: step {ms * 1e3:.1f} us ({value:.0f} GB/s); dominant "
         f"{dom_us:.1f} us ({dom_gbs:.0f} GB/s); {len(sets)} rotating sets, {reps} graph replays")
     return dict(value=value, ms=ms, roofline=roof, sets=len(sets), launches=wl["launches"],
-                step_bytes=wl["step_bytes"], batch=wl.get("batch", 1), steps=reps * len(sets))
+                step_bytes=wl["step_bytes"], batch=wl.get("batch", 1), steps=reps * len(sets),
+                step_tflops=wl["flops"] / (ms * 1e-3) / 1e12 if wl["flops"] else None)
 
 
 def cpu_baseline(wl, seconds: float):
@@ -395,7 +423,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--schedule", choices=("stream", "layered"), default="stream")
     ap.add_argument("--workload", default="sweep",
-                    choices=("sweep",) + CONTEXT_WORKLOADS
+                    choices=("sweep",) + CONTEXT_WORKLOADS + GEMM_WORKLOADS
                     + tuple(w + "_absmax32" for w in CONTEXT_WORKLOADS)
                     + tuple(w + "_int4" for w in CONTEXT_WORKLOADS))
     ap.add_argument("--blocksize", type=int, default=None,
@@ -427,7 +455,8 @@ def main():
         print(json.dumps({
             "metric": METRIC, "value": round(r["value"], 1), "unit": "GB/s", "n_gpus": 1,
             "steps": r["steps"], "warmup": args.warmup, "ms_per_step": round(r["ms"], 5),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if args.workload in GEMM_WORKLOADS else "f32",
             "data": "synthetic",
             "config": {"workload": args.workload, "batch": r["batch"], "blocksize": args.blocksize,
                        "s2_blocksize": None if args.workload.endswith(("_absmax32", "_int4"))
@@ -436,6 +465,7 @@ def main():
                        "bytes_per_step": r["step_bytes"], "rotating_sets": r["sets"],
                        "prewarm_s": args.prewarm},
             "pct_of_peak": round(100 * r["value"] / HBM_PEAK_GBS, 2),
+            "step_tflops": None if r["step_tflops"] is None else round(r["step_tflops"], 2),
             "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
         return
     wl = build_workload(dev)

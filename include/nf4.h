@@ -183,20 +183,39 @@ nf4_status nf4_gemv_absmax32(const uint8_t* packed, const float* absmax, int64_t
  *  M             : batch rows, 0 <= M < 2^27.
  *  x             : device bf16 bits [M][K], row-major.
  *  y             : device bf16 bits [M][N], row-major.
+ *  workspace     : optional DEVICE scratch buffer of workspace_bytes bytes,
+ *                  256-byte aligned, any contents, or NULL.  With
+ *                  nf4_gemm_workspace_size(M, N, K) bytes the product may split
+ *                  K over several workgroups: their fp32 partial sums go
+ *                  there and a second kernel adds them in a fixed order.  The
+ *                  split changes the fp32 summation order, so results may
+ *                  differ from a NULL-workspace call in the last bits (both
+ *                  within the tolerance below).  Nothing is kept between
+ *                  calls; calls that may overlap in time (other streams) need
+ *                  separate workspaces.  Caller-owned; never freed or resized
+ *                  by the library.
  *  stream        : hipStream_t.
  * The fast path needs K % 64 == 0, blocksize >= 64, packed 8-byte and x
- * 16-byte aligned, N*K < 2^31 and (M + 64) K < 2^30; other shapes run the
+ * 16-byte aligned, N*K < 2^31 and (M + 128) K < 2^30; other shapes run the
  * GEMV over chunks of 8 rows, with the same tolerance.  Weights are never
  * rounded to 16 bits (each NF4 value enters as the sum of two bf16 values,
  * within 2^-16 of it) and sums are fp32: each output is the bf16 rounding of
- * a value within 2^-14 * sum_k |w x| of the exact sum.  Deterministic.
- * Returns NF4_EINVAL for NULL pointers with M*N*K > 0, negative sizes, odd K
- * or bad block sizes.
+ * a value within 2^-14 * sum_k |w x| of the exact sum.  Deterministic: the
+ * same arguments (workspace size included) give the same bits.
+ * Returns NF4_EINVAL for NULL pointers with M*N*K > 0, negative sizes, odd K,
+ * bad block sizes or a workspace that is not 256-byte aligned.
  */
 nf4_status nf4_gemm(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
                     const uint16_t* code2, float offset, int64_t M, int64_t N, int64_t K,
                     int32_t blocksize, int32_t s2_blocksize, const uint16_t* x, uint16_t* y,
-                    void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nf4_gemm_workspace_size -- bytes of workspace nf4_gemm can use for an
+ * M x N x K product on the current device (0: it would not split K, or the
+ * shape takes the GEMV path).  Depends on the device's compute-unit count.
+ */
+size_t nf4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
  * One matrix of a grouped GEMV (64 bytes; all pointers are device pointers).

@@ -204,20 +204,22 @@ def test_int4_empty_oversized_and_quantize_validation(lib):
     assert lib.int4_quantize(None, 0, 128, None, None, None, None) == 0
 
 
-def _gm(lib, M=16, N=4, K=64, bs=64, s2=256, x=FAKE, y=FAKE, packed=FAKE):
-    return lib.nf4_gemm(packed, FAKE, FAKE, FAKE, C.c_float(0.0), M, N, K, bs, s2, x, y, None)
+def _gm(lib, M=16, N=4, K=64, bs=64, s2=256, x=FAKE, y=FAKE, packed=FAKE, ws=None):
+    return lib.nf4_gemm(packed, FAKE, FAKE, FAKE, C.c_float(0.0), M, N, K, bs, s2, x, y, ws, 0,
+                        None)
 
 
 @pytest.mark.parametrize("kw", [dict(M=-1), dict(N=-1), dict(K=-2), dict(K=63), dict(bs=24),
-                                dict(s2=0), dict(x=None), dict(y=None), dict(packed=None)])
+                                dict(s2=0), dict(x=None), dict(y=None), dict(packed=None),
+                                dict(ws=C.c_void_p(0x1008))])
 def test_gemm_rejects_bad_arguments(lib, kw):
     assert _gm(lib, **kw) == 1
 
 
 def test_gemm_empty_and_oversized(lib):
     assert lib.nf4_gemm(None, None, None, None, C.c_float(0.0), 0, 64, 64, 64, 256, None, None,
-                        None) == 0
+                        None, 0, None) == 0
     assert lib.nf4_gemm(None, None, None, None, C.c_float(0.0), 16, 0, 64, 64, 256, None, None,
-                        None) == 0
+                        None, 0, None) == 0
     assert _gm(lib, M=1 << 30) == 2
     assert _gm(lib, N=1 << 30, K=1 << 12) == 2

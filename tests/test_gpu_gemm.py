@@ -21,7 +21,9 @@ def _lib():
     nf4.load()
 
 
-def run_gemm(q, N, K, xbits, x_offset=0):
+def run_gemm(q, N, K, xbits, x_offset=0, workspace="auto"):
+    """workspace: "auto" (a fresh zeroed one of nf4_gemm_workspace_size bytes),
+    None, or a tensor to reuse."""
     M = xbits.shape[0]
     d = G.fmt_to_device(q)
     x = G.x_to_device(xbits)
@@ -30,17 +32,20 @@ def run_gemm(q, N, K, xbits, x_offset=0):
         buf[x_offset:] = x.reshape(-1)
         x = buf[x_offset:].view(M, K)
     base, yv = G.guarded(M * N, torch.bfloat16)
-    print(f"[gemm] M={M} N={N} K={K} bs={q.blocksize} s2={q.s2_blocksize} x_off={x_offset}",
-          flush=True)
+    if isinstance(workspace, str):
+        workspace = nf4.nf4_gemm_workspace(M, N, K)
+    wsb = 0 if workspace is None else workspace.numel()
+    print(f"[gemm] M={M} N={N} K={K} bs={q.blocksize} s2={q.s2_blocksize} x_off={x_offset} "
+          f"workspace={wsb}", flush=True)
     nf4.nf4_gemm(d["packed"], d["absmax_q"], d["absmax2"], d["code2"], q.offset, N, K, x,
-                 q.blocksize, q.s2_blocksize, y=yv.view(M, N))
+                 q.blocksize, q.s2_blocksize, y=yv.view(M, N), workspace=workspace)
     torch.cuda.synchronize()
     assert G.guards_intact(base, M * N), "write outside y"
     return G.bf16_to_f64(G.bits16(yv)).reshape(M, N)
 
 
-def check_gemm(q, N, K, xbits, rows=None, x_offset=0):
-    y = run_gemm(q, N, K, xbits, x_offset)
+def check_gemm(q, N, K, xbits, rows=None, x_offset=0, workspace="auto"):
+    y = run_gemm(q, N, K, xbits, x_offset, workspace)
     yr, S = oracle.gemv(q, N, K, xbits, rows)
     if rows is not None:
         y = y[:, rows]
@@ -98,6 +103,55 @@ def test_gemm_is_deterministic_and_matches_gemv_shape():
     xb = synth.activations(65, M, K)
     a = run_gemm(q, N, K, xb)
     b = run_gemm(q, N, K, xb)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (16, 4096, 11008), (40, 1376, 4096)])
+def test_gemm_split_k(M, N, K):
+    """With a workspace the product splits K over workgroups and sums the fp32
+    partials in a fixed order: the same bits twice in a row on the same
+    workspace (the second time over the first call's partials), and both the split and
+    the unsplit product within the GEMV tolerance of the oracle on sampled
+    columns (the split changes the fp32 summation order, so the two may differ
+    in the last bits)."""
+    nbytes = nf4.load().nf4_gemm_workspace_size(M, N, K)
+    assert nbytes > 0, "these shapes leave compute units idle without a split"
+    q = oracle.quantize(synth.weights(70 + M, N * K))
+    xb = synth.activations(71 + M, M, K)
+    ws = nf4.nf4_gemm_workspace(M, N, K)
+    a = run_gemm(q, N, K, xb, workspace=ws)
+    b = run_gemm(q, N, K, xb, workspace=ws)
+    c = run_gemm(q, N, K, xb, workspace=None)
+    assert np.array_equal(a, b)
+    cols = np.sort(np.random.default_rng(M + N).choice(N, 96, replace=False))
+    yr, S = oracle.gemv(q, N, K, xb, cols)
+    for name, y in (("split", a), ("unsplit", c)):
+        ok, worst = G.gemv_within_tolerance(y[:, cols], yr, S)
+        assert ok, f"{name} GEMM: worst error/bound = {worst:.3g}"
+
+
+def test_gemm_workspace_reused_for_a_smaller_shape():
+    """A workspace sized for a larger product serves a smaller one next."""
+    ws = nf4.nf4_gemm_workspace(128, 4096, 4096)
+    for (M, N, K) in [(128, 4096, 4096), (24, 1024, 2048)]:
+        q = oracle.quantize(synth.weights(80 + M, N * K))
+        xb = synth.activations(81 + M, M, K)
+        cols = np.sort(np.random.default_rng(M).choice(N, 64, replace=False))
+        y = run_gemm(q, N, K, xb, workspace=ws)
+        yr, S = oracle.gemv(q, N, K, xb, cols)
+        ok, worst = G.gemv_within_tolerance(y[:, cols], yr, S)
+        assert ok, f"M={M} N={N} K={K}: worst error/bound = {worst:.3g}"
+
+
+def test_gemm_workspace_contents_do_not_matter():
+    """The workspace is scratch: garbage in it changes nothing."""
+    M, N, K = 128, 4096, 4096
+    q = oracle.quantize(synth.weights(90, N * K))
+    xb = synth.activations(91, M, K)
+    ws = nf4.nf4_gemm_workspace(M, N, K)
+    a = run_gemm(q, N, K, xb, workspace=ws)
+    ws.fill_(0xA5)
+    b = run_gemm(q, N, K, xb, workspace=ws)
     assert np.array_equal(a, b)
 
 

@@ -4,7 +4,8 @@ AMD Instinct MI355X (gfx950).
 The compute lives in libnf4.so (HIP, C ABI in include/nf4.h); this package is
 its Python binding.  See nf4_dequant / nf4_gemv (double-quantized format) and
 nf4_dequant_absmax32 / nf4_gemv_absmax32 (one fp32 absmax per block), and
-int4_dequant / int4_gemv (INT4 asymmetric groups, include/int4.h).
+int4_dequant / int4_gemv (INT4 asymmetric groups, include/int4.h); nf4_gemm
+is the matrix-core product for batches past 8.
 """
 from ._binding import (  # noqa: F401
     EXPORTED,
@@ -29,6 +30,7 @@ from ._binding import (  # noqa: F401
     nf4_dequant,
     nf4_dequant_absmax32,
     nf4_gemm,
+    nf4_gemm_workspace,
     nf4_gemv,
     nf4_gemv_absmax32,
     nf4_quantize,

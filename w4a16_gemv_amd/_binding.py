@@ -19,6 +19,7 @@ NF4_OK, NF4_EINVAL, NF4_EUNSUPPORTED, NF4_EHIP = 0, 1, 2, 3
 NF4_BF16, NF4_FP16 = 0, 1
 
 EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv", "nf4_gemm",
+            "nf4_gemm_workspace_size",
             "nf4_dequant_absmax32", "nf4_gemv_absmax32", "nf4_gemv_grouped",
             "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
             "nf4_quantize", "nf4_quantize_absmax32", "int4_dequant", "int4_gemv",
@@ -56,7 +57,9 @@ def load() -> C.CDLL:
     lib.nf4_gemv_absmax32.restype = C.c_int
     lib.nf4_gemv_absmax32.argtypes = [p, p, i64, i64, i32, p, i32, p, p]
     lib.nf4_gemm.restype = C.c_int
-    lib.nf4_gemm.argtypes = [p, p, p, p, f32, i64, i64, i64, i32, i32, p, p, p]
+    lib.nf4_gemm.argtypes = [p, p, p, p, f32, i64, i64, i64, i32, i32, p, p, p, C.c_size_t, p]
+    lib.nf4_gemm_workspace_size.restype = C.c_size_t
+    lib.nf4_gemm_workspace_size.argtypes = [i64, i64, i64]
     lib.nf4_gemv_grouped.restype = C.c_int
     lib.nf4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, i32, p, C.c_size_t, p]
     lib.nf4_gemv_sched_size.restype = C.c_size_t
@@ -155,11 +158,28 @@ def nf4_gemv(packed, absmax_q, absmax2, code2, offset: float, N: int, K: int, x:
     return y.view(int(N)) if squeeze and y.dim() == 2 else y
 
 
+def nf4_gemm_workspace(M: int, N: int, K: int, device=None) -> torch.Tensor | None:
+    """A scratch workspace for nf4_gemm of an M x N x K product on `device`
+    (None when the product would not use one).  Reusable by later calls of
+    the same or smaller shapes on one stream (nothing is kept between calls)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        nbytes = load().nf4_gemm_workspace_size(int(M), int(N), int(K))
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
 def nf4_gemm(packed, absmax_q, absmax2, code2, offset: float, N: int, K: int, x: torch.Tensor,
              blocksize: int = 64, s2_blocksize: int = 256,
-             y: torch.Tensor | None = None) -> torch.Tensor:
+             y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y[m][n] = sum_k W[n][k] x[m][k] for any number of rows M of x (bf16
-    [M][K]); returns y bf16 [M][N].  The matrix-core path for batches past 8."""
+    [M][K]); returns y bf16 [M][N].  The matrix-core path for batches past 8.
+
+    workspace: uint8 device tensor from nf4_gemm_workspace (or None: K is not
+    split, which is slower when N / 64 column tiles leave compute units idle;
+    the split sums K in pieces, so the two may differ in the last bits, both
+    within the same tolerance)."""
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"x must be [M, {K}], got shape {tuple(x.shape)}")
     M = x.shape[0]
@@ -170,8 +190,12 @@ def nf4_gemm(packed, absmax_q, absmax2, code2, offset: float, N: int, K: int, x:
             _dev(absmax2, "absmax2", _HALF_BITS, ng), _dev(code2, "code2", _HALF_BITS, 256))
     px = _dev(x, "x", _BF16_BITS, M * int(K))
     py = _dev(y, "y", _BF16_BITS, M * int(N))
+    pw, wbytes = None, 0
+    if workspace is not None:
+        pw = _dev(workspace, "workspace", _U8, 0)
+        wbytes = workspace.numel()
     st = load().nf4_gemm(*args, C.c_float(offset), int(M), int(N), int(K), int(blocksize),
-                         int(s2_blocksize), px, py, _stream(y))
+                         int(s2_blocksize), px, py, pw, C.c_size_t(wbytes), _stream(y))
     _check("nf4_gemm", st)
     return y
 
@@ -265,11 +289,11 @@ class NF4Tensor:
         return nf4_gemv(self.packed, self.absmax_q, self.absmax2, self.code2, self.offset, N, K,
                         x, self.blocksize, self.s2_blocksize, y)
 
-    def gemm(self, N: int, K: int, x, y=None):
+    def gemm(self, N: int, K: int, x, y=None, workspace=None):
         if N * K != self.n:
             raise ValueError(f"N*K={N * K} does not match the tensor's {self.n} elements")
         return nf4_gemm(self.packed, self.absmax_q, self.absmax2, self.code2, self.offset, N, K,
-                        x, self.blocksize, self.s2_blocksize, y)
+                        x, self.blocksize, self.s2_blocksize, y, workspace)
 
 
 def nf4_quantize(w: torch.Tensor, blocksize: int = 64, s2_blocksize: int = 256,

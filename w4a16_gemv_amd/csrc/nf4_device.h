@@ -65,4 +65,72 @@ __device__ __forceinline__ uint16_t to_half_bits(float v) {
   return static_cast<uint16_t>(pack_pair<OUT>(v, 0.0f) & 0xFFFFu);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [p, p + bytes): loads beyond `bytes` return zeros and
+// stores beyond it are dropped, so masked lanes need no branch (a branch
+// around a load makes the compiler wait for every load in flight, including
+// the prefetch of the next row group).
+// A resource over a NULL pointer is always empty, so that a skipped matrix
+// (whose descriptor is zeroed) can never be read or written.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                           p ? static_cast<int>(bytes) : 0, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond every resource (< 2^31 bytes)
+constexpr uint32_t kFar = 0x40000000u;  // added to an in-range offset: still < 2^31, never wraps
+// Cache-policy operand of the packed-weight loads: the nt (streaming) bit.
+// Every weight byte is read once per launch, so there is nothing to keep.
+constexpr int kStreamLoad = 2;
+
+constexpr int kPairCopies = 32;
+
+// The decode table: entry b = (hi, lo) where hi holds the bf16 pair
+// (NF4[b >> 4], NF4[b & 15]) and lo the bf16 pair of the exact differences
+// v - bf16(v), replicated kPairCopies times (copy c of entry b at uint2 index
+// 32 b + c).  Each of the 256 entries is computed once by two threads, each
+// of which writes 16 of its copies; the copy order is rotated by the entry,
+// so the 64 lanes of a wave write 32 distinct bank pairs at a time.
+__device__ __forceinline__ void build_pair_table(uint2* s_pairs, int tid, int nthreads) {
+  static_assert(kPairCopies == 32, "two threads per entry, 16 copies each");
+  for (int w = tid; w < 512; w += nthreads) {
+    const int b = w & 255, half = w >> 8;
+    const float ve = nf4_value(b >> 4), vo = nf4_value(b & 15);
+    const uint32_t hi = pack_pair<NF4_BF16>(ve, vo);
+    const float he = __builtin_bit_cast(float, hi << 16);
+    const float ho = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+    const uint32_t lo2 = pack_pair<NF4_BF16>(ve - he, vo - ho);  // exact differences
+    const uint2 entry = make_uint2(hi, lo2);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s_pairs[b * kPairCopies + ((b + 16 * half + k) & 31)] = entry;
+  }
+}
+
+
+
+// --- host helpers ---
+
+// Compute units of the current device (cached per device id; a benign race
+// writes the same value).
+inline int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline nf4_status launch_status() {
+  return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+
 }  // namespace nf4dev

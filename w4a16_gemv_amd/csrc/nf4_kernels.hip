@@ -23,6 +23,7 @@
 #include "int4.h"
 #include "nf4.h"
 #include "nf4_device.h"
+#include "nf4_gemm.h"
 
 namespace {
 
@@ -128,7 +129,6 @@ __device__ __forceinline__ float code_value(uint32_t i) {
 // aligned, blocksize >= 8 so that a step never straddles a block.
 // ---------------------------------------------------------------------------
 constexpr int kDqThreads = 256;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int OUT, int U, int FMT = kFmtDouble>
 __global__ __launch_bounds__(kDqThreads) void dequant_vec_kernel(
@@ -357,31 +357,8 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
 // 32, packed and x 16-byte aligned, blockDim = 64 * nw * T <= 512.
 // ---------------------------------------------------------------------------
 constexpr int kSlab = 2048;
-constexpr int kPairCopies = 32;
 
 constexpr int kMaxDescs = 1024;  // matrices per grouped launch
-
-// The decode table: entry b = (hi, lo) where hi holds the bf16 pair
-// (NF4[b >> 4], NF4[b & 15]) and lo the bf16 pair of the exact differences
-// v - bf16(v), replicated kPairCopies times (copy c of entry b at uint2 index
-// 32 b + c).  Each of the 256 entries is computed once by two threads, each
-// of which writes 16 of its copies; the copy order is rotated by the entry,
-// so the 64 lanes of a wave write 32 distinct bank pairs at a time.
-__device__ __forceinline__ void build_pair_table(uint2* s_pairs, int tid, int nthreads) {
-  static_assert(kPairCopies == 32, "two threads per entry, 16 copies each");
-  for (int w = tid; w < 512; w += nthreads) {
-    const int b = w & 255, half = w >> 8;
-    const float ve = nf4_value(b >> 4), vo = nf4_value(b & 15);
-    const uint32_t hi = pack_pair<NF4_BF16>(ve, vo);
-    const float he = __builtin_bit_cast(float, hi << 16);
-    const float ho = __builtin_bit_cast(float, hi & 0xFFFF0000u);
-    const uint32_t lo2 = pack_pair<NF4_BF16>(ve - he, vo - ho);  // exact differences
-    const uint2 entry = make_uint2(hi, lo2);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) s_pairs[b * kPairCopies + ((b + 16 * half + k) & 31)] = entry;
-  }
-}
-
 
 // The INT4 decode table (same 64 KiB of LDS): entry b is the exact bf16 pair
 // (b & 15, b >> 4) -- the even element, in the low nibble, in the low half --
@@ -421,19 +398,6 @@ __device__ __forceinline__ float pair_sum(const uint32_t (&x)[N]) {
   return acc;
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource over [p, p + bytes): loads beyond `bytes` return zeros and
-// stores beyond it are dropped, so masked lanes need no branch (a branch
-// around a load makes the compiler wait for every load in flight, including
-// the prefetch of the next row group).
-// A resource over a NULL pointer is always empty, so that a skipped matrix
-// (whose descriptor is zeroed) can never be read or written.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
-                                           p ? static_cast<int>(bytes) : 0, 0x00020000);
-}
-constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond every resource (< 2^31 bytes)
 
 // Buffer resources a team needs to load row groups of one matrix.
 struct LoadBufs {
@@ -503,10 +467,6 @@ struct LaneOffsets {
   uint32_t x;
   uint32_t k0;
 };
-constexpr uint32_t kFar = 0x40000000u;  // added to an in-range offset: still < 2^31, never wraps
-// Cache-policy operand of the packed-weight loads: the nt (streaming) bit.
-// Every weight byte is read once per launch, so there is nothing to keep.
-constexpr int kStreamLoad = 2;
 
 template <int R, int FMT>
 __device__ __forceinline__ void load_row_group(RowGroup<R, FMT>& rg, const LoadBufs& mb, int rl,
@@ -1588,187 +1548,6 @@ __global__ __launch_bounds__(256) void gemv_any_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Batched NF4 W4A16 GEMM on the matrix cores (batch 9 and up, prefill):
-// y[m][n] = sum_k value(n K + k) * x[m][k].
-//
-// v_mfma_f32_16x16x32_bf16 with the activations as A (16 batch rows x 32 k)
-// and the decoded weights as B (32 k x 16 columns n).  Lane layout (checked on
-// gfx950): A lane i + 16 g holds A[i][8 g .. 8 g + 7], B lane j + 16 g holds
-// B[8 g .. 8 g + 7][j], D lane j + 16 g holds D[4 g .. 4 g + 3][j] -- so a
-// lane's B column is also its D column.
-//
-// A workgroup of four waves owns 16 columns and up to 16 MT batch rows; the
-// waves split K into quarters.  Per 64-column block (one NF4 block of each
-// column: blocksize >= 64, K % 64 == 0) lane (j, g) loads the 8 packed bytes
-// of columns [16 g, 16 g + 16) of row n0 + j and decodes them through the pair
-// table into the bf16 hi pairs and lo pairs (hi + lo within 2^-16 of the NF4
-// value), read as separate dwords so they land in the MFMA operand registers.
-// Two k-steps of 32 times (hi, lo) are four MFMAs per 16-row tile, summed
-// unscaled; the block's absmax_real of column n then multiplies that sum into
-// the lane's fp32 accumulator (scale after accumulate, as in the GEMV).  The
-// four waves' accumulators meet in LDS in a fixed order: deterministic.
-// Loads of the next block are issued before the current one is computed.
-// Requirements (checked on the host): K % 64 == 0, blocksize >= 64, packed
-// 8-byte aligned, x 16-byte aligned, N K < 2^31, M K < 2^30.
-// ---------------------------------------------------------------------------
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int kGemmWaves = 4;
-
-template <int MT>
-struct GemmStage {
-  uint2 w;            // 8 packed bytes of the lane's column and k-group
-  uint8_t q;          // absmax_q of the block
-  uint16_t a2;        // absmax2 of its group
-  u32x4 xa[MT][2];    // activations: tile mt, k-step t (8 bf16)
-};
-
-template <int MT>
-__device__ __forceinline__ void gemm_load(GemmStage<MT>& st, int kb, bool live,
-                                          __amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rq,
-                                          __amdgpu_buffer_rsrc_t ra2, __amdgpu_buffer_rsrc_t rx,
-                                          uint32_t wrow, uint32_t blk_row, int g, uint32_t xoff,
-                                          int K, int log2bs, int log2s2) {
-  const uint32_t far = live ? 0u : kFar;
-  const uint32_t kcol = static_cast<uint32_t>(kb) * 64u;
-  const uint32_t wo = wrow + kcol / 2u + 8u * static_cast<uint32_t>(g);
-  st.w.x = __builtin_amdgcn_raw_buffer_load_b32(rp, wo, far, kStreamLoad);
-  st.w.y = __builtin_amdgcn_raw_buffer_load_b32(rp, wo + 4u, far, kStreamLoad);
-  const uint32_t blk = (blk_row + kcol) >> log2bs;
-  st.q = __builtin_amdgcn_raw_buffer_load_b8(rq, blk, far, 0);
-  st.a2 = __builtin_amdgcn_raw_buffer_load_b16(ra2, (blk >> log2s2) * 2u, far, 0);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      st.xa[mt][t] = __builtin_amdgcn_raw_buffer_load_b128(
-          rx, xoff + (static_cast<uint32_t>(mt) * 16u * static_cast<uint32_t>(K) + kcol +
-                      16u * static_cast<uint32_t>(g) + 8u * t) * 2u,
-          far, 0);
-}
-
-template <int MT>
-__device__ __forceinline__ void gemm_block(const GemmStage<MT>& st, const char* tab,
-                                           uint32_t copy_off, const float* s_code2, float offset,
-                                           f32x4 (&acc)[MT]) {
-  // B operands: byte 4 t + e of the lane's 8 bytes holds k 8 t + 2 e, + 1
-  uint32_t bh[2][4], bl[2][4];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const uint32_t word = t == 0 ? st.w.x : st.w.y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t addr = __builtin_amdgcn_perm(copy_off, word, 0x0C0C0004u | (uint32_t(e) << 8));
-      bh[t][e] = *reinterpret_cast<const uint32_t*>(tab + addr);
-      bl[t][e] = *reinterpret_cast<const uint32_t*>(tab + addr + 4);
-    }
-  }
-  const float prod = s_code2[st.q] * f16_to_f32(st.a2);
-  const float a = prod + offset;
-  bf16x8 bhv[2], blv[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const u32x4 h = {bh[t][0], bh[t][1], bh[t][2], bh[t][3]};
-    const u32x4 l = {bl[t][0], bl[t][1], bl[t][2], bl[t][3]};
-    bhv[t] = __builtin_bit_cast(bf16x8, h);
-    blv[t] = __builtin_bit_cast(bf16x8, l);
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const bf16x8 x0 = __builtin_bit_cast(bf16x8, st.xa[mt][0]);
-    const bf16x8 x1 = __builtin_bit_cast(bf16x8, st.xa[mt][1]);
-    f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, bhv[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, blv[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, bhv[1], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, blv[1], c, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[mt][r] += a * c[r];
-  }
-}
-
-template <int MT>
-__global__ __launch_bounds__(64 * kGemmWaves) void gemm_mfma_kernel(
-    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ absmax_q,
-    const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset, int M,
-    int N, int K, int log2bs, int log2s2, const uint16_t* __restrict__ x,
-    uint16_t* __restrict__ y) {
-  __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
-  __shared__ float s_code2[256];
-  __shared__ f32x4 s_red[kGemmWaves - 1][MT][64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = lane & 15, g = lane >> 4;
-  const int n = blockIdx.x * 16 + j;
-  const int m0 = blockIdx.y * 16 * MT;
-
-  const uint64_t nk = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
-  const uint64_t nb = ((nk - 1) >> log2bs) + 1;
-  const uint64_t ng = ((nb - 1) >> log2s2) + 1;
-  const auto rp = rsrc(packed, static_cast<uint32_t>(nk >> 1));
-  const auto rq = rsrc(absmax_q, static_cast<uint32_t>(nb));
-  const auto ra2 = rsrc(absmax2, static_cast<uint32_t>(ng * 2));
-  const auto rx = rsrc(x, static_cast<uint32_t>(static_cast<uint64_t>(M) * K * 2));
-  // the lane's weight row (pushed out of range past N) and its activation row
-  const uint32_t wrow = n < N ? static_cast<uint32_t>(n) * static_cast<uint32_t>(K >> 1) : kFar;
-  const uint32_t blk_row = static_cast<uint32_t>(n < N ? n : 0) * static_cast<uint32_t>(K);
-  const uint32_t xoff = static_cast<uint32_t>(m0 + j) * static_cast<uint32_t>(K) * 2u;
-
-  if (tid < 256) s_code2[tid] = f16_to_f32(code2[tid]);
-  build_pair_table(s_pairs, tid, blockDim.x);
-  const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
-  __syncthreads();
-  const char* tab = reinterpret_cast<const char*>(s_pairs);
-
-  // the wave's quarter of the K blocks
-  const int nkb = K >> 6;
-  const int kb0 = wave * nkb / kGemmWaves, kb1 = (wave + 1) * nkb / kGemmWaves;
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  GemmStage<MT> s0, s1;
-  gemm_load<MT>(s0, kb0, kb0 < kb1, rp, rq, ra2, rx, wrow, blk_row, g, xoff, K, log2bs, log2s2);
-  // two blocks per round, the loads of block kb + 1 issued before block kb is
-  // computed; the round's second half loads past kb1 only as dead (out of
-  // range) loads, so every round has the same shape
-  for (int kb = kb0; kb < kb1; kb += 2) {
-    gemm_load<MT>(s1, kb + 1, kb + 1 < kb1, rp, rq, ra2, rx, wrow, blk_row, g, xoff, K, log2bs,
-                  log2s2);
-    gemm_block<MT>(s0, tab, copy_off, s_code2, offset, acc);
-    gemm_load<MT>(s0, kb + 2, kb + 2 < kb1, rp, rq, ra2, rx, wrow, blk_row, g, xoff, K, log2bs,
-                  log2s2);
-    if (kb + 1 < kb1) gemm_block<MT>(s1, tab, copy_off, s_code2, offset, acc);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-
-  // fixed-order sum of the four waves' accumulators, then one bf16 store per
-  // output (rows 4 g + r of each tile, column n)
-  if (wave > 0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) s_red[wave - 1][mt][lane] = acc[mt];
-  }
-  __syncthreads();
-  if (wave == 0 && n < N) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 v = acc[mt];
-#pragma unroll
-      for (int w = 0; w < kGemmWaves - 1; ++w) {
-        const f32x4 p = s_red[w][mt][lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] += p[r];
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 16 * mt + 4 * g + r;
-        if (m < M) y[static_cast<int64_t>(m) * N + n] = to_half_bits<NF4_BF16>(v[r]);
-      }
-    }
-  }
-}
-
 // y = 0 for an empty reduction (K == 0).
 __global__ void fill_zero_kernel(uint16_t* __restrict__ y, int64_t count) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -1788,28 +1567,6 @@ bool pow2_log2(int32_t v, int* lg) {
   while ((1 << l) < v) ++l;
   *lg = l;
   return true;
-}
-
-// Compute units of the current device (cached per device id; a benign race
-// writes the same value).
-int device_cus() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    cache[dev] = cus;
-  }
-  return cache[dev];
-}
-
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-nf4_status launch_status() {
-  return hipGetLastError() == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 
 template <int OUT, int FMT>
@@ -1991,28 +1748,6 @@ nf4_status gemv_launch_b(const uint8_t* packed, const uint8_t* absmax_q, const u
   return launch_status();
 }
 
-// The MFMA GEMM over all M batch rows: up to 64 rows per workgroup (MT tiles
-// of 16), 16 columns per workgroup.
-nf4_status gemm_launch(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
-                       const uint16_t* code2, float offset, int64_t M, int64_t N, int64_t K,
-                       int lbs, int ls2, const uint16_t* x, uint16_t* y, hipStream_t st) {
-  const int64_t tiles = (M + 15) / 16;
-  const int MT = tiles >= 4 ? 4 : static_cast<int>(tiles);
-  const int64_t gy = (M + 16 * MT - 1) / (16 * MT);
-  const int64_t gx = (N + 15) / 16;
-  if (gy > 65535 || gx > 0x7FFFFFFF) return NF4_EUNSUPPORTED;
-  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy));
-  const dim3 block(64 * kGemmWaves);
-  const int m = static_cast<int>(M), nn = static_cast<int>(N), k = static_cast<int>(K);
-  switch (MT) {
-    case 1: hipLaunchKernelGGL(gemm_mfma_kernel<1>, grid, block, 0, st, packed, absmax_q, absmax2, code2, offset, m, nn, k, lbs, ls2, x, y); break;
-    case 2: hipLaunchKernelGGL(gemm_mfma_kernel<2>, grid, block, 0, st, packed, absmax_q, absmax2, code2, offset, m, nn, k, lbs, ls2, x, y); break;
-    case 3: hipLaunchKernelGGL(gemm_mfma_kernel<3>, grid, block, 0, st, packed, absmax_q, absmax2, code2, offset, m, nn, k, lbs, ls2, x, y); break;
-    default: hipLaunchKernelGGL(gemm_mfma_kernel<4>, grid, block, 0, st, packed, absmax_q, absmax2, code2, offset, m, nn, k, lbs, ls2, x, y); break;
-  }
-  return launch_status();
-}
-
 // y = +0 for N x batch outputs (empty sums, K == 0).
 nf4_status gemv_fill_zero(uint16_t* y, int64_t N, int32_t batch, hipStream_t st) {
   if (N > kMaxElems) return NF4_EUNSUPPORTED;
@@ -2087,12 +1822,20 @@ nf4_status nf4_gemv(const uint8_t* packed, const uint8_t* absmax_q, const uint16
   return NF4_EINVAL;
 }
 
+size_t nf4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0 || M > (int64_t(1) << 31) / 16 ||
+      N * K >= (int64_t(1) << 31) || (M + 128) * K * 2 >= (int64_t(1) << 31))
+    return 0;
+  return nf4gemm::plan(M, N, K, ~size_t(0)).ws_bytes;
+}
+
 nf4_status nf4_gemm(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t* absmax2,
                     const uint16_t* code2, float offset, int64_t M, int64_t N, int64_t K,
                     int32_t blocksize, int32_t s2_blocksize, const uint16_t* x, uint16_t* y,
-                    void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream) {
   int lbs = 0, ls2 = 0;
   if (M < 0 || N < 0 || K < 0 || (K & 1)) return NF4_EINVAL;
+  if (workspace && !aligned(workspace, 256)) return NF4_EINVAL;
   if (!pow2_log2(blocksize, &lbs) || !pow2_log2(s2_blocksize, &ls2)) return NF4_EINVAL;
   if (M == 0 || N == 0) return NF4_OK;
   if (!y) return NF4_EINVAL;
@@ -2105,9 +1848,10 @@ nf4_status nf4_gemm(const uint8_t* packed, const uint8_t* absmax_q, const uint16
   if (!packed || !absmax_q || !absmax2 || !code2 || !x) return NF4_EINVAL;
   if (N > kMaxElems / K) return NF4_EUNSUPPORTED;
   const bool fast = K % 64 == 0 && lbs >= 6 && aligned(packed, 8) && aligned(x, 16) &&
-                    N * K < (int64_t(1) << 31) && (M + 64) * K * 2 < (int64_t(1) << 31);
+                    N * K < (int64_t(1) << 31) && (M + 128) * K * 2 < (int64_t(1) << 31);
   if (fast)
-    return gemm_launch(packed, absmax_q, absmax2, code2, offset, M, N, K, lbs, ls2, x, y, st);
+    return nf4gemm::launch(packed, absmax_q, absmax2, code2, offset, M, N, K, lbs, ls2, x, y,
+                           workspace, workspace_bytes, st);
   // anything else: the GEMV over batch chunks of up to 8 rows
   for (int64_t m0 = 0; m0 < M; m0 += 8) {
     const int64_t b = M - m0 < 8 ? M - m0 : 8;

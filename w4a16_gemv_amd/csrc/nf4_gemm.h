@@ -9,10 +9,11 @@
 
 namespace nf4gemm {
 
-// Launch shape: MT row tiles of 16 per workgroup, gx x gy workgroups over
-// columns and rows, SK splits of the K blocks; ws_bytes of workspace used.
+// Launch shape: MT row tiles of 16 and 64 NT columns per workgroup, gx x gy
+// workgroups over columns and rows, SK splits of the K blocks; ws_bytes of
+// workspace used.
 struct Plan {
-  int MT, SK;
+  int MT, NT, SK;
   int64_t gx, gy;
   size_t ws_bytes;
 };

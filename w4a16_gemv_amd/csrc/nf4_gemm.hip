@@ -64,18 +64,19 @@ constexpr int kGemmXRow = 144;  // LDS bytes per activation row (128 + 16 of pad
 template <int MT>
 constexpr int gemm_xloads() { return MT >= 2 ? MT / 2 : 1; }
 
-template <int MT>
+template <int MT, int NT>
 struct GemmStage {
   u32x4 xg[gemm_xloads<MT>()];  // activation chunks this thread loads
-  uint2 w;                      // 8 packed bytes of the lane's column, its block of the pair
-  uint32_t q;                   // absmax_q of that block
-  uint32_t a2;                  // absmax2 of its group
+  uint2 w[NT];                  // 8 packed bytes per column of the lane, its block of the pair
+  uint32_t q[NT];               // absmax_q of that block
+  uint32_t a2[NT];              // absmax2 of its group
 };
 
+template <int NT>
 struct GemmLane {
   __amdgpu_buffer_rsrc_t rp, rq, ra2, rx;
-  uint32_t wrow;     // byte offset of the lane's weight row (kFar past N)
-  uint32_t blk_row;  // flat index of that row's first element
+  uint32_t wrow[NT];     // byte offset of the lane's weight rows (kFar past N)
+  uint32_t blk_row[NT];  // flat index of each row's first element
   uint32_t g;        // k-group of the lane (0..3)
   uint32_t par;      // block of the pair the wave computes (0 or 1)
   uint32_t xg_off[4];  // byte offsets of this thread's activation chunks (pair 0)
@@ -83,16 +84,21 @@ struct GemmLane {
   int log2bs, log2s2;
 };
 
-template <int MT>
-__device__ __forceinline__ void gemm_load(GemmStage<MT>& st, int kp, int kb1, const GemmLane& L) {
+template <int MT, int NT>
+__device__ __forceinline__ void gemm_load(GemmStage<MT, NT>& st, int kp, int kb1,
+                                          const GemmLane<NT>& L) {
   const uint32_t kb = 2u * static_cast<uint32_t>(kp) + L.par;
   const uint32_t far = static_cast<int>(kb) < kb1 ? 0u : kFar;
   const uint32_t kcol = kb * 64u;
-  st.w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                       L.rp, L.wrow + kcol / 2u + 8u * L.g, far, kStreamLoad));
-  const uint32_t blk = (L.blk_row + kcol) >> L.log2bs;
-  st.q = __builtin_amdgcn_raw_buffer_load_b8(L.rq, blk, far, 0);
-  st.a2 = __builtin_amdgcn_raw_buffer_load_b16(L.ra2, (blk >> L.log2s2) * 2u, far, 0);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    st.w[nt] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             L.rp, L.wrow[nt] + kcol / 2u + 8u * L.g, far,
+                                             kStreamLoad));
+    const uint32_t blk = (L.blk_row[nt] + kcol) >> L.log2bs;
+    st.q[nt] = __builtin_amdgcn_raw_buffer_load_b8(L.rq, blk, far, 0);
+    st.a2[nt] = __builtin_amdgcn_raw_buffer_load_b16(L.ra2, (blk >> L.log2s2) * 2u, far, 0);
+  }
   // the pair's activations (a block past kb1 reads as zeros)
   const uint32_t pfar = 2 * kp < kb1 && L.xg_live ? 0u : kFar;
 #pragma unroll
@@ -103,8 +109,8 @@ __device__ __forceinline__ void gemm_load(GemmStage<MT>& st, int kp, int kb1, co
 
 // This thread's activation chunks of a stage into an LDS buffer; chunk c of
 // the pair is block c / (128 MT), row (c / 8) % (16 MT), bytes (c % 8) 16.
-template <int MT>
-__device__ __forceinline__ void gemm_stash(const GemmStage<MT>& st, char* buf, int tid) {
+template <int MT, int NT>
+__device__ __forceinline__ void gemm_stash(const GemmStage<MT, NT>& st, char* buf, int tid) {
   constexpr int XTILE = 16 * MT * kGemmXRow;
   if (MT >= 2 || tid < 256) {
 #pragma unroll
@@ -116,45 +122,54 @@ __device__ __forceinline__ void gemm_stash(const GemmStage<MT>& st, char* buf, i
   }
 }
 
-template <int MT>
-__device__ __forceinline__ void gemm_block(const GemmStage<MT>& st, const char* tab,
+template <int MT, int NT>
+__device__ __forceinline__ void gemm_block(const GemmStage<MT, NT>& st, const char* tab,
                                            const char* xbuf, uint32_t copy_off, int lane,
-                                           const float* s_code2, float offset, f32x4 (&acc)[MT]) {
+                                           const float* s_code2, float offset,
+                                           f32x4 (&acc)[MT][NT]) {
   const int i = lane & 15, g = lane >> 4;
-  // B operands: byte 4 t + e of the lane's 8 bytes holds k 16 g + 8 t + 2 e, + 1
-  bf16x8 bhv[2], blv[2];
+  // B operands: byte 4 t + e of the lane's 8 bytes holds k 16 g + 8 t + 2 e, + 1;
+  // one 8-byte table read gives its hi and lo pairs (conflict-free: lanes l
+  // and l + 16 read the two halves of one bank pair)
+  bf16x8 bhv[NT][2], blv[NT][2];
+  float a[NT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const uint32_t word = t == 0 ? st.w.x : st.w.y;
-    uint32_t bh[4], bl[4];
+  for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t addr = __builtin_amdgcn_perm(copy_off, word, 0x0C0C0004u | (uint32_t(e) << 8));
-      bh[e] = *reinterpret_cast<const uint32_t*>(tab + addr);
-      bl[e] = *reinterpret_cast<const uint32_t*>(tab + addr + 4);
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t word = t == 0 ? st.w[nt].x : st.w[nt].y;
+      uint2 e2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t addr = __builtin_amdgcn_perm(copy_off, word, 0x0C0C0004u | (uint32_t(e) << 8));
+        e2[e] = *reinterpret_cast<const uint2*>(tab + addr);
+      }
+      bhv[nt][t] = __builtin_bit_cast(bf16x8, (u32x4){e2[0].x, e2[1].x, e2[2].x, e2[3].x});
+      blv[nt][t] = __builtin_bit_cast(bf16x8, (u32x4){e2[0].y, e2[1].y, e2[2].y, e2[3].y});
     }
-    bhv[t] = __builtin_bit_cast(bf16x8, (u32x4){bh[0], bh[1], bh[2], bh[3]});
-    blv[t] = __builtin_bit_cast(bf16x8, (u32x4){bl[0], bl[1], bl[2], bl[3]});
+    const float prod = s_code2[st.q[nt] & 0xFFu] * f16_to_f32(static_cast<uint16_t>(st.a2[nt]));
+    a[nt] = prod + offset;
   }
-  const float prod = s_code2[st.q & 0xFFu] * f16_to_f32(static_cast<uint16_t>(st.a2));
-  const float a = prod + offset;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     // A operands: row 16 mt + i, k 16 g + 8 t .. + 7
     const char* row = xbuf + (16 * mt + i) * kGemmXRow + 32 * g;
     const bf16x8 x0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row));
     const bf16x8 x1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16));
-    f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, bhv[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, blv[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, bhv[1], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, blv[1], c, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[mt][r] += a * c[r];
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, bhv[nt][0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, blv[nt][0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, bhv[nt][1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, blv[nt][1], c, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[mt][nt][r] += a[nt] * c[r];
+    }
   }
 }
 
-template <int MT>
+template <int MT, int NT>
 __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ absmax_q,
     const uint16_t* __restrict__ absmax2, const uint16_t* __restrict__ code2, float offset, int M,
@@ -162,7 +177,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
     uint16_t* __restrict__ y, float* __restrict__ part, int SK) {
   constexpr int BM = 16 * MT;
   constexpr int XPAIR = 2 * BM * kGemmXRow;  // LDS bytes of one pair's activations
-  static_assert(4 * MT * 64 * sizeof(f32x4) <= 256 * kPairCopies * sizeof(uint2),
+  static_assert(4 * MT * NT * 64 * sizeof(f32x4) <= 256 * kPairCopies * sizeof(uint2),
                 "the odd-block sums fit in the decode table's LDS");
   __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
   __shared__ float s_code2[256];
@@ -171,11 +186,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g = lane >> 4;
-  const int n = blockIdx.x * 64 + (wave & 3) * 16 + j;  // the lane's column
+  // the lane's columns: n0 + 16 nt, nt < NT
+  const int n0 = blockIdx.x * (64 * NT) + (wave & 3) * (16 * NT) + j;
   const int m0 = blockIdx.y * BM;
   const int split = blockIdx.z;
 
-  GemmLane L;
+  GemmLane<NT> L;
   const uint64_t nk = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
   const uint64_t nb = ((nk - 1) >> log2bs) + 1;
   const uint64_t ng = ((nb - 1) >> log2s2) + 1;
@@ -183,8 +199,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
   L.rq = rsrc(absmax_q, static_cast<uint32_t>(nb));
   L.ra2 = rsrc(absmax2, static_cast<uint32_t>(ng * 2));
   L.rx = rsrc(x, static_cast<uint32_t>(static_cast<uint64_t>(M) * K * 2));
-  L.wrow = n < N ? static_cast<uint32_t>(n) * static_cast<uint32_t>(K >> 1) : kFar;
-  L.blk_row = static_cast<uint32_t>(n < N ? n : 0) * static_cast<uint32_t>(K);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * nt;
+    L.wrow[nt] = n < N ? static_cast<uint32_t>(n) * static_cast<uint32_t>(K >> 1) : kFar;
+    L.blk_row[nt] = static_cast<uint32_t>(n < N ? n : 0) * static_cast<uint32_t>(K);
+  }
   L.g = static_cast<uint32_t>(g);
   L.par = static_cast<uint32_t>(wave >> 2);
   L.xg_live = MT >= 2 || tid < 256;
@@ -202,20 +222,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
   const int nkb = K >> 6;
   const int kb0 = (split * nkb / SK) & ~1, kb1 = split + 1 == SK ? nkb : ((split + 1) * nkb / SK) & ~1;
   const int kp0 = kb0 >> 1, kp1 = (kb1 + 1) >> 1;
-  GemmStage<MT> st[3];
-  gemm_load<MT>(st[0], kp0, kb1, L);
-  gemm_load<MT>(st[1], kp0 + 1, kb1, L);
+  GemmStage<MT, NT> st[3];
+  gemm_load<MT, NT>(st[0], kp0, kb1, L);
+  gemm_load<MT, NT>(st[1], kp0 + 1, kb1, L);
 
   if (tid < 256) s_code2[tid] = f16_to_f32(code2[tid]);
   build_pair_table(s_pairs, tid, blockDim.x);
   const uint32_t copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
-  gemm_stash<MT>(st[0], s_x, tid);
+  gemm_stash<MT, NT>(st[0], s_x, tid);
   __syncthreads();
   const char* tab = reinterpret_cast<const char*>(s_pairs);
 
-  f32x4 acc[MT];
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // pair kp: its activations are in LDS buffer (kp - kp0) & 1, the wave's
   // weights in st[(kp - kp0) % 3]; the loads of pair kp + 2 go out before it
   // is computed and pair kp + 1's activations are stashed after it
@@ -224,12 +246,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
     for (int u = 0; u < 3; ++u) {
       const int p = kp + u;
       if (p < kp1) {
-        gemm_load<MT>(st[(u + 2) % 3], p + 2, kb1, L);
+        gemm_load<MT, NT>(st[(u + 2) % 3], p + 2, kb1, L);
         if (2 * p + static_cast<int>(L.par) < kb1) {
           const char* xbuf = s_x + ((p - kp0) & 1) * XPAIR + L.par * (XPAIR / 2);
-          gemm_block<MT>(st[u], tab, xbuf, copy_off, lane, s_code2, offset, acc);
+          gemm_block<MT, NT>(st[u], tab, xbuf, copy_off, lane, s_code2, offset, acc);
         }
-        gemm_stash<MT>(st[(u + 1) % 3], s_x + ((p + 1 - kp0) & 1) * XPAIR, tid);
+        gemm_stash<MT, NT>(st[(u + 1) % 3], s_x + ((p + 1 - kp0) & 1) * XPAIR, tid);
         __syncthreads();
       }
     }
@@ -238,41 +260,42 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
 
   // the odd-block waves' sums go to the even-block waves through the table's
   // LDS (every wave is past its last table read: the loop ends on a barrier)
-  f32x4* s_red = reinterpret_cast<f32x4*>(s_pairs);  // [4 waves][MT][64]
+  f32x4* s_red = reinterpret_cast<f32x4*>(s_pairs);  // [4 waves][MT][NT][64]
   if (wave >= 4) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) s_red[((wave - 4) * MT + mt) * 64 + lane] = acc[mt];
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        s_red[(((wave - 4) * MT + mt) * NT + nt) * 64 + lane] = acc[mt][nt];
   }
   __syncthreads();
-  if (wave < 4) {
+  if (wave >= 4) return;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 o = s_red[(wave * MT + mt) * 64 + lane];
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mt][r] += o[r];
+    for (int nt = 0; nt < NT; ++nt) {
+      const f32x4 o = s_red[((wave * MT + mt) * NT + nt) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[mt][nt][r] += o[r];
     }
-  }
-  if (SK == 1) {
-    if (wave < 4 && n < N) {
+  // SK == 1: the bf16 tile; else the partial tile into plane `split` of the
+  // workspace (summed by gemm_reduce_kernel)
+  float* dst = SK > 1 ? part + static_cast<int64_t>(split) * M * N : nullptr;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + 16 * mt + 4 * g + r;
-          if (m < M) y[static_cast<int64_t>(m) * N + n] = to_half_bits<NF4_BF16>(acc[mt][r]);
-        }
-    }
-    return;
-  }
-  // split K: the partial tile (summed by gemm_reduce_kernel)
-  if (wave < 4 && n < N) {
-    float* dst = part + static_cast<int64_t>(split) * M * N;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * nt;
+    if (n >= N) continue;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + 16 * mt + 4 * g + r;
-        if (m < M) dst[static_cast<int64_t>(m) * N + n] = acc[mt][r];
+        if (m >= M) continue;
+        const int64_t o = static_cast<int64_t>(m) * N + n;
+        if (SK > 1)
+          dst[o] = acc[mt][nt][r];
+        else
+          y[o] = to_half_bits<NF4_BF16>(acc[mt][nt][r]);
       }
   }
 }
@@ -330,7 +353,8 @@ Plan plan(int64_t M, int64_t N, int64_t K, size_t ws_avail) {
   Plan p{};
   const int64_t tm = (M + 15) / 16;
   p.MT = tm >= 5 ? 8 : tm >= 3 ? 4 : static_cast<int>(tm);
-  p.gx = (N + 63) / 64;
+  p.NT = 1;  // 32 columns per wave (NT = 2) measured slower: fewer workgroups, same stalls
+  p.gx = (N + 64 * p.NT - 1) / (64 * p.NT);
   p.gy = (M + 16 * p.MT - 1) / (16 * p.MT);
   const int64_t tiles = p.gx * p.gy;
   // one workgroup per CU (two at MT = 1: LDS)
@@ -364,16 +388,16 @@ nf4_status launch(const uint8_t* packed, const uint8_t* absmax_q, const uint16_t
   const dim3 block(kGemmThreads);
   float* part = p.SK > 1 ? static_cast<float*>(ws) : nullptr;
   const int m = static_cast<int>(M), nn = static_cast<int>(N), k = static_cast<int>(K);
-  switch (p.MT) {
-#define NF4_GEMM_MT(T)                                                                          \
-  case T:                                                                                       \
-    hipLaunchKernelGGL((gemm_mfma_kernel<T>), grid, block, 0, st, packed, absmax_q, absmax2,   \
+  switch (p.MT * 4 + p.NT) {
+#define NF4_GEMM_MT(T, U)                                                                       \
+  case T * 4 + U:                                                                               \
+    hipLaunchKernelGGL((gemm_mfma_kernel<T, U>), grid, block, 0, st, packed, absmax_q, absmax2, \
                        code2, offset, m, nn, k, lbs, ls2, x, y, part, p.SK);                     \
     break;
-    NF4_GEMM_MT(1)
-    NF4_GEMM_MT(2)
-    NF4_GEMM_MT(4)
-    NF4_GEMM_MT(8)
+    NF4_GEMM_MT(1, 1)
+    NF4_GEMM_MT(2, 1)
+    NF4_GEMM_MT(4, 1)
+    NF4_GEMM_MT(8, 1)
 #undef NF4_GEMM_MT
     default: return NF4_EINVAL;
   }

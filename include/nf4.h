@@ -195,7 +195,7 @@ nf4_status nf4_gemv_absmax32(const uint8_t* packed, const float* absmax, int64_t
  *                  separate workspaces.  Caller-owned; never freed or resized
  *                  by the library.
  *  stream        : hipStream_t.
- * The fast path needs K % 64 == 0, blocksize >= 64, packed 8-byte and x
+ * The fast path needs K % 64 == 0, blocksize >= 64, packed and x
  * 16-byte aligned, N*K < 2^31 and (M + 128) K < 2^30; other shapes run the
  * GEMV over chunks of 8 rows, with the same tolerance.  Weights are never
  * rounded to 16 bits (each NF4 value enters as the sum of two bf16 values,

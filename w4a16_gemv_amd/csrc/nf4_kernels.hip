@@ -1847,7 +1847,7 @@ nf4_status nf4_gemm(const uint8_t* packed, const uint8_t* absmax_q, const uint16
   }
   if (!packed || !absmax_q || !absmax2 || !code2 || !x) return NF4_EINVAL;
   if (N > kMaxElems / K) return NF4_EUNSUPPORTED;
-  const bool fast = K % 64 == 0 && lbs >= 6 && aligned(packed, 8) && aligned(x, 16) &&
+  const bool fast = K % 64 == 0 && lbs >= 6 && aligned(packed, 16) && aligned(x, 16) &&
                     N * K < (int64_t(1) << 31) && (M + 128) * K * 2 < (int64_t(1) << 31);
   if (fast)
     return nf4gemm::launch(packed, absmax_q, absmax2, code2, offset, M, N, K, lbs, ls2, x, y,

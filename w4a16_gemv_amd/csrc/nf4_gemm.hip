@@ -129,11 +129,14 @@ __device__ __forceinline__ void gemm_load(GemmStage<MT>& st, int grp, int kb1, c
   constexpr int R = gemm_r<MT>();
   const uint32_t kbw = static_cast<uint32_t>(grp) * (2u * R) + L.half * R;  // the wave's first block
   if constexpr (R == 4) {
-    // block kbw + g of the lane's row, whole (its 4 units are transposed later)
-    const uint32_t far = static_cast<int>(kbw + L.g) < kb1 ? 0u : kFar;
-    const uint32_t wo = L.wrow + (kbw + L.g) * 32u;
-    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(L.rp, wo, far, kStreamLoad);
-    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(L.rp, wo + 16u, far, kStreamLoad);
+    // block kbw + g of the lane's row, whole (its 4 units are transposed
+    // later); a block past kb1 is pushed out of range in the lane's VGPR
+    // offset: a lane-dependent scalar offset would make the compiler loop
+    // over its distinct values around every load
+    const uint32_t wo = L.wrow + (kbw + L.g) * 32u +
+                        (static_cast<int>(kbw + L.g) < kb1 ? 0u : kFar);
+    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(L.rp, wo, 0u, kStreamLoad);
+    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(L.rp, wo + 16u, 0u, kStreamLoad);
     st.w[0][0] = lo[0]; st.w[0][1] = lo[1]; st.w[1][0] = lo[2]; st.w[1][1] = lo[3];
     st.w[2][0] = hi[0]; st.w[2][1] = hi[1]; st.w[3][0] = hi[2]; st.w[3][1] = hi[3];
   } else {
@@ -153,7 +156,7 @@ __device__ __forceinline__ void gemm_load(GemmStage<MT>& st, int grp, int kb1, c
     st.a2[r] = __builtin_amdgcn_raw_buffer_load_b16(L.ra2, (blk >> L.log2s2) * 2u, far, 0);
   }
   // the group's activations (blocks past kb1 read as zeros or are never used)
-  const uint32_t gfar = static_cast<int>(grp * 2 * R) < kb1 && L.xg_live ? 0u : kFar;
+  const uint32_t gfar = static_cast<int>(grp * 2 * R) < kb1 ? 0u : kFar;  // uniform
 #pragma unroll
   for (int i = 0; i < gemm_xloads<MT>(); ++i)
     st.xg[i] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -256,8 +259,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
   for (int i = 0; i < gemm_xloads<MT>(); ++i) {
     const int c = tid + kGemmThreads * i;
     const int b = c / (128 * MT), r = (c >> 3) % (16 * MT);
+    // threads without a chunk load from out of range (in the VGPR offset)
     L.xg_off[i] = static_cast<uint32_t>(m0 + r) * static_cast<uint32_t>(K) * 2u +
-                  static_cast<uint32_t>(b) * 128u + static_cast<uint32_t>(c & 7) * 16u;
+                  static_cast<uint32_t>(b) * 128u + static_cast<uint32_t>(c & 7) * 16u +
+                  (L.xg_live ? 0u : kFar);
   }
   L.log2bs = log2bs;
   L.log2s2 = log2s2;
@@ -285,29 +290,35 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
   // group p: its activations are in LDS buffer (p - gp0) & 1, the wave's
   // weights in st[(p - gp0) % S]; the loads of group p + S - 1 go out before it
   // is computed and group p + 1's activations are stashed after it
+  // The loop runs whole rounds of S groups: every group of a round issues its
+  // loads (past gp1 they are dead, out of range), stashes and meets the
+  // barrier, and only the compute of blocks past kb1 is skipped.  A guard around the loads
+  // instead would give the loop header paths with different numbers of loads
+  // in flight, and the compiler then waits for all of them (vmcnt(0)) at the
+  // top of every group, which undoes the prefetch.
   for (int gp = gp0; gp < gp1; gp += S) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
       const int p = gp + u;
-      if (p < gp1) {
-        gemm_load<MT>(st[(u + S - 1) % S], p + S - 1, kb1, L);
-        uint32_t wl[R][2];
+      gemm_load<MT>(st[(u + S - 1) % S], p + S - 1, kb1, L);
+      uint32_t wl[R][2];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          wl[r][0] = st[u].w[r][0];
-          wl[r][1] = st[u].w[r][1];
-        }
-        if constexpr (R == 4) transpose_units(wl);
-        const char* xbuf = s_x + ((p - gp0) & 1) * XGROUP + L.half * (R * XTILE);
-        const int kbw = p * 2 * R + static_cast<int>(L.half) * R;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (kbw + r < kb1)
-            gemm_block<MT>(wl[r], st[u].q[r], st[u].a2[r], tab, xbuf + r * XTILE, copy_off, lane,
-                           s_code2, offset, acc);
-        gemm_stash<MT>(st[(u + 1) % S], s_x + ((p + 1 - gp0) & 1) * XGROUP, tid);
-        __syncthreads();
+      for (int r = 0; r < R; ++r) {
+        wl[r][0] = st[u].w[r][0];
+        wl[r][1] = st[u].w[r][1];
       }
+      if constexpr (R == 4) transpose_units(wl);
+      const char* xbuf = s_x + ((p - gp0) & 1) * XGROUP + L.half * (R * XTILE);
+      const int kbw = p * 2 * R + static_cast<int>(L.half) * R;
+      // (computing dead blocks too, with scale 0, measured 1.8x slower at
+      // 128 rows and no faster at 16)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (kbw + r < kb1)
+          gemm_block<MT>(wl[r], st[u].q[r], st[u].a2[r], tab, xbuf + r * XTILE, copy_off, lane,
+                         s_code2, offset, acc);
+      gemm_stash<MT>(st[(u + 1) % S], s_x + ((p + 1 - gp0) & 1) * XGROUP, tid);
+      __syncthreads();
     }
   }
   __builtin_amdgcn_s_waitcnt(0);

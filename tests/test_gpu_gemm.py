@@ -130,6 +130,23 @@ def test_gemm_split_k(M, N, K):
         assert ok, f"{name} GEMM: worst error/bound = {worst:.3g}"
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (130, 1000, 4096),   # ragged rows (two row groups) and columns, split K
+    (17, 100, 8192),     # four-block groups, ragged, split over 2^7 blocks
+    (9, 4096, 11008),    # 172 blocks: splits of 43, the last group half dead
+    (33, 64, 1984),      # 31 blocks: an odd count, the last pair half dead
+])
+def test_gemm_split_and_ragged_shapes(M, N, K):
+    q = oracle.quantize(synth.weights(M + 7 * N + K, N * K, outliers=True))
+    xb = synth.activations(M + K, M, K)
+    cols = np.sort(np.random.default_rng(N).choice(N, min(N, 80), replace=False))
+    for ws in ("auto", None):
+        y = run_gemm(q, N, K, xb, workspace=ws)
+        yr, S = oracle.gemv(q, N, K, xb, cols)
+        ok, worst = G.gemv_within_tolerance(y[:, cols], yr, S)
+        assert ok, f"M={M} N={N} K={K} ws={ws}: worst error/bound = {worst:.3g}"
+
+
 def test_gemm_workspace_reused_for_a_smaller_shape():
     """A workspace sized for a larger product serves a smaller one next."""
     ws = nf4.nf4_gemm_workspace(128, 4096, 4096)

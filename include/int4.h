@@ -67,6 +67,40 @@ nf4_status int4_gemv(const uint8_t* packed, const uint16_t* scales, const uint16
                      uint16_t* y, void* stream);
 
 /*
+ * One matrix of a grouped INT4 GEMV (64 bytes, the layout of nf4_gemv_desc
+ * with the scales and zero points in the second and third slots; device
+ * pointers).
+ */
+typedef struct int4_gemv_desc {
+  const uint8_t* packed;      /* packed codes of W [N][K], 16-byte aligned */
+  const uint16_t* scales;     /* fp16 per group, 2-byte aligned */
+  const uint16_t* zeros;      /* fp16 per group, 2-byte aligned */
+  const uint16_t* x;          /* bf16 [batch][K], 16-byte aligned */
+  uint16_t* y;                /* bf16 [batch][N] output */
+  int64_t N;                  /* rows of W */
+  int64_t row_begin;          /* sum of N over the preceding descriptors */
+  float reserved1;            /* set to 0 */
+  int32_t reserved2;          /* set to 0 */
+} int4_gemv_desc;
+
+/*
+ * int4_gemv_grouped -- int4_gemv over a list of matrices in one launch
+ * (independent products that share K, the group size and the batch), as
+ * nf4_gemv_grouped does for the NF4 format.  Same arithmetic and tolerance
+ * as int4_gemv.
+ *  descs, count, total_rows, K, batch, sched, sched_bytes, stream : as for
+ *                  nf4_gemv_grouped.
+ *  group_size    : G, a power of two >= 32.
+ * Returns NF4_EINVAL / NF4_EUNSUPPORTED as nf4_gemv_grouped does; a matrix
+ * whose packed or x pointer is not 16-byte aligned, whose scales or zeros
+ * are not 2-byte aligned, whose pointers are NULL or whose N disagrees with
+ * the row_begin sequence is skipped (its y is left unwritten).
+ */
+nf4_status int4_gemv_grouped(const int4_gemv_desc* descs, int32_t count, int64_t total_rows,
+                             int64_t K, int32_t group_size, int32_t batch, void* sched,
+                             size_t sched_bytes, void* stream);
+
+/*
  * int4_quantize -- encode n fp32 weights into the format above on the GPU
  * ([handbook] "量化公式"): per group, s = fp16(fp32(max - min) / 15), taken
  * as 1 when that is 0; z = round(-min / s) stored as fp16; q = clamp(round(w

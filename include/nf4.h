@@ -278,6 +278,40 @@ nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t t
 size_t nf4_gemv_sched_size(void);
 
 /*
+ * One matrix of a grouped single-level GEMV (64 bytes, the layout of
+ * nf4_gemv_desc with the fp32 absmax in the second slot; device pointers).
+ */
+typedef struct nf4_absmax32_gemv_desc {
+  const uint8_t* packed;      /* packed codes of W [N][K], 16-byte aligned */
+  const float* absmax;        /* fp32 absmax per block, 4-byte aligned */
+  const void* reserved0;      /* set to NULL */
+  const uint16_t* x;          /* bf16 [batch][K], 16-byte aligned */
+  uint16_t* y;                /* bf16 [batch][N] output */
+  int64_t N;                  /* rows of W */
+  int64_t row_begin;          /* sum of N over the preceding descriptors */
+  float reserved1;            /* set to 0 */
+  int32_t reserved2;          /* set to 0 */
+} nf4_absmax32_gemv_desc;
+
+/*
+ * nf4_gemv_grouped_absmax32 -- nf4_gemv_absmax32 over a list of matrices in
+ * one launch (independent products that share K, the block size and the
+ * batch), as nf4_gemv_grouped does for the double-quantized format.  Same
+ * arithmetic and tolerance as nf4_gemv_absmax32.
+ *  descs, count, total_rows, K, batch, sched, sched_bytes, stream : as for
+ *                  nf4_gemv_grouped.
+ *  blocksize     : power of two >= 32.
+ * Returns NF4_EINVAL / NF4_EUNSUPPORTED as nf4_gemv_grouped does; a matrix
+ * whose packed or x pointer is not 16-byte aligned, whose absmax is not
+ * 4-byte aligned, whose pointers are NULL or whose N disagrees with the
+ * row_begin sequence is skipped (its y is left unwritten).
+ */
+nf4_status nf4_gemv_grouped_absmax32(const nf4_absmax32_gemv_desc* descs, int32_t count,
+                                     int64_t total_rows, int64_t K, int32_t blocksize,
+                                     int32_t batch, void* sched, size_t sched_bytes,
+                                     void* stream);
+
+/*
  * nf4_code2_linear -- the linear second-level code table: out[i] = the fp16
  * nearest to -1 + 2 i / 255, i = 0..255 (host function, no GPU work).  The
  * report's §1.2 fixes code2 as fp16[256]; evenly spaced values are this

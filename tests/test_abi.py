@@ -137,6 +137,45 @@ def test_gemv_grouped_empty_is_a_no_op(lib):
     assert lib.nf4_gemv_grouped(None, 0, 0, 64, 64, 256, None, 1, None, 0, None) == 0
 
 
+@pytest.mark.parametrize("fn", ["nf4_gemv_grouped_absmax32", "int4_gemv_grouped"])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(sched=C.c_void_p(0x1010)), 1),        # misaligned workspace
+    (dict(sched_bytes=16), 1),                   # too small
+    (dict(K=63), 1), (dict(bs=3), 1), (dict(bs=0), 1), (dict(count=-1), 1),
+    (dict(descs=None), 1), (dict(descs=C.c_void_p(0x1004)), 1),   # NULL / misaligned descs
+    (dict(bs=16), 2), (dict(K=96 + 16), 2), (dict(batch=9), 2), (dict(count=1025), 2),
+])
+def test_grouped_formats_reject_bad_arguments(lib, fn, kw, expect):
+    sched = kw.get("sched", C.c_void_p(0x1000))
+    sched_bytes = kw.get("sched_bytes", lib.nf4_gemv_sched_size())
+    rc = getattr(lib, fn)(kw.get("descs", FAKE), kw.get("count", 2), 100, kw.get("K", 64),
+                          kw.get("bs", 64), kw.get("batch", 1), sched, sched_bytes, None)
+    assert rc == expect
+
+
+@pytest.mark.parametrize("fn", ["nf4_gemv_grouped_absmax32", "int4_gemv_grouped"])
+def test_grouped_formats_empty_is_a_no_op(lib, fn):
+    assert getattr(lib, fn)(None, 0, 0, 64, 64, 1, None, 0, None) == 0
+    assert getattr(lib, fn)(None, 3, 0, 64, 64, 1, None, 0, None) == 0
+
+
+def test_descriptor_layouts_match():
+    """The three descriptor types have the same 64-byte layout (the binding
+    writes all of them through one record type)."""
+    import numpy as np
+
+    from w4a16_gemv_amd._binding import _DESC_DTYPE
+    assert np.dtype(_DESC_DTYPE).itemsize == 64
+    src = open(os.path.join(ROOT, "include", "nf4.h"), encoding="utf-8").read()
+    src += open(os.path.join(ROOT, "include", "int4.h"), encoding="utf-8").read()
+    for name in ("nf4_gemv_desc", "nf4_absmax32_gemv_desc", "int4_gemv_desc"):
+        body = re.search(r"typedef struct " + name + r" \{(.*?)\} " + name + ";", src, re.S)
+        assert body, name
+        fields = re.findall(r"^\s*([\w\s\*]+?)\s*(\w+);", re.sub(r"/\*.*?\*/", "", body.group(1)),
+                            flags=re.M)
+        assert len(fields) == 9, (name, fields)
+
+
 def _dq32(lib, n=16, bs=64, dtype=0, packed=FAKE, absmax=FAKE, out=FAKE):
     return lib.nf4_dequant_absmax32(packed, absmax, n, bs, out, dtype, None)
 

@@ -21,6 +21,7 @@ NF4_BF16, NF4_FP16 = 0, 1
 EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv", "nf4_gemm",
             "nf4_gemm_workspace_size",
             "nf4_dequant_absmax32", "nf4_gemv_absmax32", "nf4_gemv_grouped",
+            "nf4_gemv_grouped_absmax32", "int4_gemv_grouped",
             "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
             "nf4_quantize", "nf4_quantize_absmax32", "int4_dequant", "int4_gemv",
             "int4_quantize")
@@ -62,6 +63,10 @@ def load() -> C.CDLL:
     lib.nf4_gemm_workspace_size.argtypes = [i64, i64, i64]
     lib.nf4_gemv_grouped.restype = C.c_int
     lib.nf4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, i32, p, C.c_size_t, p]
+    lib.nf4_gemv_grouped_absmax32.restype = C.c_int
+    lib.nf4_gemv_grouped_absmax32.argtypes = [p, i32, i64, i64, i32, i32, p, C.c_size_t, p]
+    lib.int4_gemv_grouped.restype = C.c_int
+    lib.int4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, C.c_size_t, p]
     lib.nf4_gemv_sched_size.restype = C.c_size_t
     lib.nf4_gemv_sched_size.argtypes = []
     lib.nf4_code2_linear.restype = None
@@ -455,11 +460,14 @@ MAX_GROUP = 1024
 
 class GemvGroup:
     """A reusable list of independent GEMVs y_i = W_i x_i launched as one
-    nf4_gemv_grouped call.  All W_i share K, the block sizes, code2 and the
-    batch (1..8).  The descriptor table is built and uploaded once; launch()
-    only enqueues the kernel (so it can be captured in a HIP graph).
+    grouped call: nf4_gemv_grouped for NF4Tensor items, nf4_gemv_grouped_absmax32
+    for NF4Absmax32Tensor items, int4_gemv_grouped for Int4Tensor items (one
+    format per group).  All W_i share K, the block (group) size and the batch
+    (1..8), and for NF4Tensor code2 too.  The descriptor table is built and
+    uploaded once; launch() only enqueues the kernel (so it can be captured in
+    a HIP graph).
 
-    items: list of (w: NF4Tensor, N, x: bf16 [batch][K] tensor, y: bf16 [batch][N] tensor).
+    items: list of (w, N, x: bf16 [batch][K] tensor, y: bf16 [batch][N] tensor).
     dynamic: give the launch a scheduling workspace (owned by the group), so
     that rows go to the waves in chunks as they free up; False: fixed split.
     The results are bit-identical either way.  The group's workspace serves
@@ -473,39 +481,66 @@ class GemvGroup:
         self.K = int(K)
         self.items = list(items)
         w0 = items[0][0]
-        self.blocksize, self.s2_blocksize, self.code2 = w0.blocksize, w0.s2_blocksize, w0.code2
+        self.kind = type(w0)
+        if self.kind not in (NF4Tensor, NF4Absmax32Tensor, Int4Tensor):
+            raise ValueError(f"unsupported tensor type {self.kind.__name__}")
+        if self.kind is Int4Tensor:
+            self.blocksize, self.s2_blocksize, self.code2 = w0.group_size, None, None
+        elif self.kind is NF4Absmax32Tensor:
+            self.blocksize, self.s2_blocksize, self.code2 = w0.blocksize, None, None
+        else:
+            self.blocksize, self.s2_blocksize, self.code2 = w0.blocksize, w0.s2_blocksize, w0.code2
         self.batch = items[0][2].shape[0] if items[0][2].dim() == 2 else 1
         if not 1 <= self.batch <= 8:
             raise ValueError("grouped GEMV supports batch 1..8")
         if K % 32 or K <= 0 or K > 16384:
             raise ValueError("grouped GEMV needs K % 32 == 0 and 0 < K <= 16384")
         if self.blocksize < 32:
-            raise ValueError("grouped GEMV needs blocksize >= 32")
+            raise ValueError("grouped GEMV needs a block (group) size >= 32")
         table = np.zeros(len(items), dtype=np.dtype(_DESC_DTYPE))
         row = 0
         for i, (w, N, x, y) in enumerate(items):
+            if type(w) is not self.kind:
+                raise ValueError(f"item {i}: one tensor format per group")
             if w.n != N * K:
                 raise ValueError(f"item {i}: tensor has {w.n} elements, expected {N}x{K}")
-            if (w.blocksize, w.s2_blocksize) != (self.blocksize, self.s2_blocksize):
-                raise ValueError(f"item {i}: block sizes differ from the group's")
-            if w.code2.data_ptr() != self.code2.data_ptr() and not torch.equal(w.code2, self.code2):
-                raise ValueError(f"item {i}: code2 differs from the group's")
             xb = x if x.dim() == 2 else x.unsqueeze(0)
             if xb.shape != (self.batch, K):
                 raise ValueError(f"item {i}: x must be [{self.batch}, {K}]")
-            nbytes, nb, ng = format_sizes(w.n, w.blocksize, w.s2_blocksize)
-            pp = _dev(w.packed, "packed", _U8, nbytes)
             px = _dev(xb, "x", _BF16_BITS, self.batch * K)
             py = _dev(y, "y", _BF16_BITS, self.batch * N)
+            nblk = -(-w.n // self.blocksize)
+            if self.kind is Int4Tensor:
+                if w.group_size != self.blocksize:
+                    raise ValueError(f"item {i}: group size differs from the group's")
+                pp = _dev(w.packed, "packed", _U8, (w.n + 1) // 2)
+                ps = _dev(w.scales, "scales", _HALF_BITS, nblk)
+                pz = _dev(w.zeros, "zeros", _HALF_BITS, nblk)
+                entry = (pp, ps, pz, px, py, N, row, 0.0, 0)
+            elif self.kind is NF4Absmax32Tensor:
+                if w.blocksize != self.blocksize:
+                    raise ValueError(f"item {i}: block size differs from the group's")
+                pp = _dev(w.packed, "packed", _U8, (w.n + 1) // 2)
+                pa = _dev(w.absmax, "absmax", _F32, nblk)
+                entry = (pp, pa, 0, px, py, N, row, 0.0, 0)
+            else:
+                if (w.blocksize, w.s2_blocksize) != (self.blocksize, self.s2_blocksize):
+                    raise ValueError(f"item {i}: block sizes differ from the group's")
+                if w.code2.data_ptr() != self.code2.data_ptr() and not torch.equal(w.code2, self.code2):
+                    raise ValueError(f"item {i}: code2 differs from the group's")
+                nbytes, nb, ng = format_sizes(w.n, w.blocksize, w.s2_blocksize)
+                pp = _dev(w.packed, "packed", _U8, nbytes)
+                entry = (pp, _dev(w.absmax_q, "absmax_q", _U8, nb),
+                         _dev(w.absmax2, "absmax2", _HALF_BITS, ng), px, py, N, row, w.offset, 0)
             if pp % 16 or px % 16:
                 raise ValueError(f"item {i}: packed and x must be 16-byte aligned")
-            table[i] = (pp, _dev(w.absmax_q, "absmax_q", _U8, nb),
-                        _dev(w.absmax2, "absmax2", _HALF_BITS, ng), px, py, N, row, w.offset, 0)
+            table[i] = entry
             row += N
         self.total_rows = row
         dev = items[0][0].packed.device
         self.table = torch.from_numpy(table.view(np.uint8)).to(dev)
-        _dev(self.code2, "code2", _HALF_BITS, 256)
+        if self.code2 is not None:
+            _dev(self.code2, "code2", _HALF_BITS, 256)
         self.sched = None
         if dynamic:
             nbytes = int(load().nf4_gemv_sched_size())
@@ -515,8 +550,21 @@ class GemvGroup:
 
     def launch(self) -> None:
         sp, sn = (self.sched.data_ptr(), self.sched.numel() * 4) if self.sched is not None else (None, 0)
-        st = load().nf4_gemv_grouped(self.table.data_ptr(), len(self.items), self.total_rows,
-                                     self.K, self.blocksize, self.s2_blocksize,
-                                     self.code2.data_ptr(), self.batch, sp, sn,
-                                     _stream(self.table))
-        _check("nf4_gemv_grouped", st)
+        lib = load()
+        if self.kind is Int4Tensor:
+            name = "int4_gemv_grouped"
+            st = lib.int4_gemv_grouped(self.table.data_ptr(), len(self.items), self.total_rows,
+                                       self.K, self.blocksize, self.batch, sp, sn,
+                                       _stream(self.table))
+        elif self.kind is NF4Absmax32Tensor:
+            name = "nf4_gemv_grouped_absmax32"
+            st = lib.nf4_gemv_grouped_absmax32(self.table.data_ptr(), len(self.items),
+                                               self.total_rows, self.K, self.blocksize,
+                                               self.batch, sp, sn, _stream(self.table))
+        else:
+            name = "nf4_gemv_grouped"
+            st = lib.nf4_gemv_grouped(self.table.data_ptr(), len(self.items), self.total_rows,
+                                      self.K, self.blocksize, self.s2_blocksize,
+                                      self.code2.data_ptr(), self.batch, sp, sn,
+                                      _stream(self.table))
+        _check(name, st)

@@ -562,8 +562,15 @@ __device__ __forceinline__ bool desc_usable(const nf4_gemv_desc& d, int rows, in
   // every offset the kernel forms must stay below 2^30 (see kFar)
   const bool small = d.N >= 0 && static_cast<uint64_t>(d.N) * static_cast<uint64_t>(K) <
                                      (uint64_t(1) << 31);
+  // the scale arrays: fp32 absmax 4-byte, fp16 scales and zero points 2-byte
+  // aligned (the absmax_q bytes and absmax2 halves of the double format too)
+  const uintptr_t sa = reinterpret_cast<uintptr_t>(d.absmax_q);
+  const uintptr_t za = reinterpret_cast<uintptr_t>(d.absmax2);
+  const bool scales_ok = FMT == kFmtAbsmax32 ? (sa & 3) == 0
+                         : FMT == kFmtInt4   ? ((sa | za) & 1) == 0
+                                             : (za & 1) == 0;
   return (a & 15) == 0 && d.N == rows && small && d.packed && d.absmax_q &&
-         (FMT == kFmtAbsmax32 || d.absmax2) && d.x && d.y;
+         (FMT == kFmtAbsmax32 || d.absmax2) && d.x && d.y && scales_ok;
 }
 
 // Field-wise copy of descriptor m (or of the by-value descriptor when the
@@ -1657,12 +1664,11 @@ nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   if constexpr (B == 1) {
     if (P == 1) return wave_launch<1, 2, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
   }
-  // the other configurations serve grouped launches only, which take the
-  // double-quantized format
-  if constexpr (B == 1 && FMT == kFmtDouble) {
+  // the other configurations serve grouped launches only
+  if constexpr (B == 1) {
     if (P == 2) return wave_launch<1, 1, 2, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
     if (P == 3) return wave_launch<1, 1, 3, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
-  } else if constexpr (B == 2 && FMT == kFmtDouble) {
+  } else if constexpr (B == 2) {
     if (P == 1) return wave_launch<2, 1, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
     if (P == 2) return wave_launch<2, 1, 2, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
   }
@@ -1756,6 +1762,58 @@ nf4_status gemv_fill_zero(uint16_t* y, int64_t N, int32_t batch, hipStream_t st)
   hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>(blocks < 4096 ? blocks : 4096)),
                      dim3(256), 0, st, y, count);
   return launch_status();
+}
+
+// The descriptors of the other formats share nf4_gemv_desc's layout, so the
+// kernels read them as nf4_gemv_desc (the scale arrays in the absmax_q and
+// absmax2 slots, as in the single-matrix entry points).
+static_assert(sizeof(nf4_absmax32_gemv_desc) == sizeof(nf4_gemv_desc) &&
+                  offsetof(nf4_absmax32_gemv_desc, absmax) == offsetof(nf4_gemv_desc, absmax_q) &&
+                  offsetof(nf4_absmax32_gemv_desc, x) == offsetof(nf4_gemv_desc, x) &&
+                  offsetof(nf4_absmax32_gemv_desc, y) == offsetof(nf4_gemv_desc, y) &&
+                  offsetof(nf4_absmax32_gemv_desc, N) == offsetof(nf4_gemv_desc, N) &&
+                  offsetof(nf4_absmax32_gemv_desc, row_begin) == offsetof(nf4_gemv_desc, row_begin),
+              "single-level descriptor layout");
+static_assert(sizeof(int4_gemv_desc) == sizeof(nf4_gemv_desc) &&
+                  offsetof(int4_gemv_desc, scales) == offsetof(nf4_gemv_desc, absmax_q) &&
+                  offsetof(int4_gemv_desc, zeros) == offsetof(nf4_gemv_desc, absmax2) &&
+                  offsetof(int4_gemv_desc, x) == offsetof(nf4_gemv_desc, x) &&
+                  offsetof(int4_gemv_desc, y) == offsetof(nf4_gemv_desc, y) &&
+                  offsetof(int4_gemv_desc, N) == offsetof(nf4_gemv_desc, N) &&
+                  offsetof(int4_gemv_desc, row_begin) == offsetof(nf4_gemv_desc, row_begin),
+              "INT4 descriptor layout");
+
+// Shared checks and dispatch of the grouped entry points of the single-level
+// and INT4 formats (ls2 and code2 are not used by those formats).
+template <int FMT>
+nf4_status grouped_other(const void* descs, int32_t count, int64_t total_rows, int64_t K,
+                         int32_t blocksize, int32_t batch, void* sched, size_t sched_bytes,
+                         void* stream) {
+  int lbs = 0;
+  if (!pow2_log2(blocksize, &lbs)) return NF4_EINVAL;
+  if (count < 0 || total_rows < 0 || K < 0 || (K & 1)) return NF4_EINVAL;
+  if (sched != nullptr && (!aligned(sched, 256) || sched_bytes < nf4_gemv_sched_size()))
+    return NF4_EINVAL;
+  if (count == 0 || total_rows == 0) return NF4_OK;
+  if (!descs || !aligned(descs, 8)) return NF4_EINVAL;
+  if (count > kMaxDescs || total_rows >= 0x7FFFFFFF || K == 0 || K % 32 != 0 ||
+      K > 8 * kSlab || lbs < 5 || batch < 1 || batch > 8)
+    return NF4_EUNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const nf4_gemv_desc* d = static_cast<const nf4_gemv_desc*>(descs);
+  const nf4_gemv_desc none{};
+  unsigned* sc = static_cast<unsigned*>(sched);
+  const int tr = static_cast<int>(total_rows), k = static_cast<int>(K);
+  switch (batch) {
+    case 1: return stream_launch<1, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
+    case 2: return stream_launch<2, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
+    case 3: return stream_launch<3, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
+    case 4: return stream_launch<4, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
+    case 5: return stream_launch<5, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
+    case 6: return stream_launch<6, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
+    case 7: return stream_launch<7, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
+    default: return stream_launch<8, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
+  }
 }
 
 }  // namespace
@@ -1975,6 +2033,21 @@ nf4_status int4_gemv(const uint8_t* packed, const uint16_t* scales, const uint16
 
 size_t nf4_gemv_sched_size(void) {
   return sizeof(unsigned) * kSchedRegions * kSchedStride;
+}
+
+nf4_status nf4_gemv_grouped_absmax32(const nf4_absmax32_gemv_desc* descs, int32_t count,
+                                     int64_t total_rows, int64_t K, int32_t blocksize,
+                                     int32_t batch, void* sched, size_t sched_bytes,
+                                     void* stream) {
+  return grouped_other<kFmtAbsmax32>(descs, count, total_rows, K, blocksize, batch, sched,
+                                     sched_bytes, stream);
+}
+
+nf4_status int4_gemv_grouped(const int4_gemv_desc* descs, int32_t count, int64_t total_rows,
+                             int64_t K, int32_t group_size, int32_t batch, void* sched,
+                             size_t sched_bytes, void* stream) {
+  return grouped_other<kFmtInt4>(descs, count, total_rows, K, group_size, batch, sched,
+                                 sched_bytes, stream);
 }
 
 nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t total_rows,

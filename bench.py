@@ -19,14 +19,16 @@ The step is captured once in a HIP graph and replayed.
 
 The timed steps are launched eagerly on one stream (three launches per step
 in the stream schedule), with HIP events bracketing the dominant kernel -- the
-K=4096 grouped GEMV, 192 matrices, 1.33 GB per launch -- in every step.  Before
+K=4096 grouped GEMV, 192 matrices, 2.60 GB per launch -- in every step.  Before
 the W warm-up steps, the captured step is replayed for at least --prewarm
 seconds: a cold GPU runs this path about 10% slower for its first few hundred
 milliseconds of load while its clocks settle.
 
 --workload picks another configuration as a context measurement (the default
-`sweep` is the headline): dequant_1k / dequant_4k (1024^2 and 4096^2 bf16
-dequant), qwen_b1 (the 7 Qwen2.5-1.5B-shaped GEMVs), llama_b1 / llama_b4 /
+`sweep` is the headline): sweep_absmax32 / sweep_int4 (the same sweep and big
+dequant in the single-level and INT4 formats, grouped launches of
+nf4_gemv_grouped_absmax32 / int4_gemv_grouped; no CPU baseline), dequant_1k /
+dequant_4k (1024^2 and 4096^2 bf16 dequant), qwen_b1 (the 7 Qwen2.5-1.5B-shaped GEMVs), llama_b1 / llama_b4 /
 llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8), llama_b16 / llama_b64
 / llama_b128 (the same 3 matrices times 16, 64, 128 activation rows through
 nf4_gemm, the matrix-core product; roofline against the bf16 MFMA peak), and
@@ -82,7 +84,33 @@ def gemv_bytes(N: int, K: int, B: int = 1) -> int:
 
 
 
-def build_workload(dev):
+SWEEP_WORKLOADS = ("sweep", "sweep_absmax32", "sweep_int4")
+
+
+def sweep_format(workload: str) -> str:
+    return "double" if workload == "sweep" else workload.split("_", 1)[1]
+
+
+def format_bytes(fmt: str):
+    """(dequant_bytes(n), gemv_bytes(N, K, B)) of a format at the sweep's
+    block sizes (64 and 256; INT4 groups of 128)."""
+    if fmt == "double":
+        return dequant_bytes, gemv_bytes
+    g = 64 if fmt == "absmax32" else 128
+
+    def dq(n):
+        return (n + 1) // 2 + 4 * -(-n // g) + 2 * n
+
+    def gv(N, K, B=1):
+        return (N * K + 1) // 2 + 4 * -(-N * K // g) + 2 * K * B + 2 * N * B
+    return dq, gv
+
+
+def build_workload(dev, fmt: str = "double"):
+    """The sweep's 224 matrices and the 8192 x 28672 weight, drawn on the GPU
+    and encoded by the library's own quantizer of the format (double: NF4
+    double-quantized, bs 64 / s2 256; absmax32: NF4 with one fp32 absmax per
+    64-block; int4: INT4 asymmetric, groups of 128)."""
     import torch
 
     import synth
@@ -91,35 +119,47 @@ def build_workload(dev):
     t0 = time.time()
     code2 = nf4.nf4_code2_linear().to(dev)
     ws = None
+
+    def encode(w):
+        nonlocal ws
+        if fmt == "absmax32":
+            return nf4.nf4_quantize_absmax32(w, 64)
+        if fmt == "int4":
+            return nf4.int4_quantize(w, 128)
+        need = nf4.load().nf4_quantize_workspace_size(w.numel(), 64)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        return nf4.nf4_quantize(w, 64, 256, code2=code2, workspace=ws)
+
     xs = {K: synth.activations_device(synth.SWEEP_X_SEED, 1, K, dev) for K in (4096, 11008)}
     layers = []
     for L in range(synth.SWEEP_LAYERS):
         mats = []
         for g in synth.sweep_layer(L):
             w = synth.weights_device(g.seed, g.N * g.K, dev)
-            if ws is None:
-                need = nf4.load().nf4_quantize_workspace_size(11008 * 4096, 64)
-                ws = torch.empty(need, dtype=torch.uint8, device=dev)
-            t = nf4.nf4_quantize(w, 64, 256, code2=code2, workspace=ws)
+            t = encode(w)
             del w
             y = torch.empty(1, g.N, dtype=torch.bfloat16, device=dev)
             mats.append((g, t, y))
         layers.append(mats)
     big = synth.DEQUANT_BIG
     wb = synth.weights_device(big.seed, big.n, dev)
-    tb = nf4.nf4_quantize(wb, 64, 256, code2=code2,
-                          workspace=torch.empty(nf4.load().nf4_quantize_workspace_size(big.n, 64),
-                                                dtype=torch.uint8, device=dev))
-    del wb
+    tb = encode(wb)
+    del wb, ws
     out = torch.empty(big.n, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
-    log(f"[bench] workload encoded on the GPU in {time.time() - t0:.1f} s")
-    return dict(layers=layers, xs=xs, big=(big, tb, out), code2=code2)
+    log(f"[bench] workload ({fmt}) encoded on the GPU in {time.time() - t0:.1f} s")
+    return dict(layers=layers, xs=xs, big=(big, tb, out), code2=code2, fmt=fmt)
 
 
 DOMINANT_K = 4096
 DOMINANT_KERNEL = ("gemv_wave_kernel<1, 2, 1, 4, true, 0> (nf4_gemv_grouped, K=4096, "
                    "192 matrices)")
+DOMINANT_KERNEL_FMT = {
+    "absmax32": "gemv_wave_kernel<1, 2, 1, 4, true, 1> (nf4_gemv_grouped_absmax32, K=4096, "
+                "192 matrices)",
+    "int4": "gemv_wave_kernel<1, 2, 1, 4, true, 2> (int4_gemv_grouped, K=4096, 192 matrices)",
+}
 KERNEL_SOURCE = os.path.join(ROOT, "w4a16_gemv_amd", "csrc", "nf4_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_wave_k4096_sweep_traffic.txt")
 
@@ -423,7 +463,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--schedule", choices=("stream", "layered"), default="stream")
     ap.add_argument("--workload", default="sweep",
-                    choices=("sweep",) + CONTEXT_WORKLOADS + GEMM_WORKLOADS
+                    choices=SWEEP_WORKLOADS + CONTEXT_WORKLOADS + GEMM_WORKLOADS
                     + tuple(w + "_absmax32" for w in CONTEXT_WORKLOADS)
                     + tuple(w + "_int4" for w in CONTEXT_WORKLOADS))
     ap.add_argument("--blocksize", type=int, default=None,
@@ -450,7 +490,7 @@ def main():
     nf4.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.workload != "sweep":
+    if args.workload not in SWEEP_WORKLOADS:
         r = bench_context(args, dev)
         print(json.dumps({
             "metric": METRIC, "value": round(r["value"], 1), "unit": "GB/s", "n_gpus": 1,
@@ -468,21 +508,27 @@ def main():
             "step_tflops": None if r["step_tflops"] is None else round(r["step_tflops"], 2),
             "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
         return
-    wl = build_workload(dev)
+    fmt = sweep_format(args.workload)
+    dq_bytes_f, gv_bytes_f = format_bytes(fmt)
+    wl = build_workload(dev, fmt)
     stream = torch.cuda.Stream(dev)
 
+    # A captured graph keeps device pointers only: the groups (descriptor
+    # tables, scheduling workspaces) it launches must outlive it, so each
+    # graph is stored with the step functions that own them.
     per_step = {}
     for sched in ("stream", "layered"):
         gemvs, dequant, nlaunch = make_step(wl, sched)
         g_step = capture(lambda: (gemvs(), dequant()), stream)
         g_gemv = capture(gemvs, stream)
-        per_step[sched] = dict(graph=g_step, gemv_graph=g_gemv, launches=nlaunch)
-    _, dequant, _ = make_step(wl, "stream")
-    g_dq = capture(dequant, stream)
+        per_step[sched] = dict(graph=g_step, gemv_graph=g_gemv, launches=nlaunch,
+                               owners=(gemvs, dequant))
+    dq_owner = make_step(wl, "stream")
+    g_dq = capture(dq_owner[1], stream)
 
-    n_gemv_bytes = sum(gemv_bytes(g.N, g.K) for mats in wl["layers"] for (g, _, _) in mats)
+    n_gemv_bytes = sum(gv_bytes_f(g.N, g.K) for mats in wl["layers"] for (g, _, _) in mats)
     big = wl["big"][0]
-    n_dq_bytes = dequant_bytes(big.n)
+    n_dq_bytes = dq_bytes_f(big.n)
     step_bytes = n_gemv_bytes + n_dq_bytes
 
     # pre-warm (clocks to steady state), then W warm-up steps
@@ -493,7 +539,7 @@ def main():
             torch.cuda.synchronize()
     gemvs, dequant, launches = make_step(wl, args.schedule)
     dom = [g for g in gemvs.groups if g.K == DOMINANT_K] if args.schedule == "stream" else []
-    dom_bytes = sum(gemv_bytes(it[1], DOMINANT_K) for it in dom[0].items) if dom else 0
+    dom_bytes = sum(gv_bytes_f(it[1], DOMINANT_K) for it in dom[0].items) if dom else 0
 
     def step(ev=None):
         for grp in gemvs.groups:
@@ -552,7 +598,7 @@ def main():
         f"{other} schedule step {other_ms:.3f} ms")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and fmt == "double":
         cpu = cpu_baseline(wl, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cpu}")
 
@@ -570,9 +616,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "decode_sweep_7b_32layers_224gemv_b1+dequant_8192x28672",
+            "workload": "decode_sweep_7b_32layers_224gemv_b1+dequant_8192x28672"
+                        + ("" if fmt == "double" else "_" + fmt),
             "gemv_weights": sum(g.N * g.K for mats in wl["layers"] for (g, _, _) in mats),
-            "batch": 1, "blocksize": 64, "s2_blocksize": 256,
+            "batch": 1, "blocksize": 128 if fmt == "int4" else 64,
+            "s2_blocksize": 256 if fmt == "double" else None,
             "dequant_elems": big.n, "dequant_out": "bf16",
             "schedule": args.schedule, "gemv_launches_per_step": launches,
             "bytes_per_step": step_bytes, "prewarm_s": args.prewarm,
@@ -580,12 +628,12 @@ def main():
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": None if not dom else {
             "bound": "hbm",
-            "kernel": DOMINANT_KERNEL,
+            "kernel": DOMINANT_KERNEL if fmt == "double" else DOMINANT_KERNEL_FMT[fmt],
             "achieved": round(dom_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-            "traffic": committed_traffic(),
+            "traffic": committed_traffic() if fmt == "double" else None,
             "bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_us, 3),
             "kernel_source_sha256_16": source_digest(),
@@ -593,7 +641,8 @@ def main():
         "all_gemvs": None if args.no_context else {"gbs": round(gemv_gbs, 1), "ms": round(gemv_ms, 4),
                                                    "launches": launches},
         "dequant": None if args.no_context else {
-            "kernel": "dequant_vec_kernel<0, 4, 0> (bf16, 4 steps per lane)", "gbs": round(dq_gbs, 1),
+            "kernel": f"dequant_vec_kernel<0, 4, {('double', 'absmax32', 'int4').index(fmt)}> "
+                      f"(bf16, 4 steps per lane)", "gbs": round(dq_gbs, 1),
             "us": round(dq_ms * 1e3, 2), "frac": round(dq_gbs / HBM_PEAK_GBS, 4)},
         f"{other}_schedule": None if args.no_context else {
             "ms_per_step": round(other_ms, 4),

@@ -479,6 +479,9 @@ def main():
                          "(1 GiB read, 1 GiB written): the reference for scaling the HBM "
                          "byte counters of a profiler run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the bandwidth probes (plain streaming read of the dominant "
+                         "launch's bytes; the dequant's 1:4 read:write stream)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the NF4 dequant / GEMV path has no multi-GPU mode "
@@ -571,6 +574,37 @@ def main():
     value = step_bytes / (ms * 1e-3) / 1e9
     dom_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / args.steps if dom else None
 
+    ceiling = None
+    if not args.no_ceiling:
+        # the hot path's memory streams without its arithmetic (bandwidth
+        # probes in libnf4): a plain streaming read of the dominant launch's
+        # bytes, and the dequant's 1 : 4 read : write stream
+        rd = torch.empty((dom_bytes + 15) // 16 * 16 if dom else 1 << 30, dtype=torch.uint8,
+                         device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        src = torch.empty((big.n + 1) // 2 // 4 * 4, dtype=torch.uint8, device=dev)
+        dst = torch.empty(4 * src.numel(), dtype=torch.uint8, device=dev)
+
+        def timed(fn, reps=5):
+            with torch.cuda.stream(stream):
+                fn()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(reps):
+                    fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps * 1e-3  # s
+
+        t_rd = timed(lambda: nf4.probe_stream_read(rd, sink))
+        t_cp = timed(lambda: nf4.probe_expand_copy(src, dst))
+        ceiling = {"stream_read": {"bytes": rd.numel(), "gbs": round(rd.numel() / t_rd / 1e9, 1)},
+                   "expand_copy_1to4": {"bytes": 5 * src.numel(),
+                                        "gbs": round(5 * src.numel() / t_cp / 1e9, 1)}}
+        log(f"[bench] ceilings: streaming read {ceiling['stream_read']['gbs']:.0f} GB/s, "
+            f"1:4 expand copy {ceiling['expand_copy_1to4']['gbs']:.0f} GB/s")
+        del rd, src, dst
+
     if args.calibration_copy:
         src = torch.full((1 << 30,), 0x5A, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -637,13 +671,18 @@ def main():
             "bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_us, 3),
             "kernel_source_sha256_16": source_digest(),
+            "frac_of_read_ceiling": None if ceiling is None else
+            round(dom_gbs / ceiling["stream_read"]["gbs"], 4),
         },
         "all_gemvs": None if args.no_context else {"gbs": round(gemv_gbs, 1), "ms": round(gemv_ms, 4),
                                                    "launches": launches},
         "dequant": None if args.no_context else {
             "kernel": f"dequant_vec_kernel<0, 4, {('double', 'absmax32', 'int4').index(fmt)}> "
                       f"(bf16, 4 steps per lane)", "gbs": round(dq_gbs, 1),
-            "us": round(dq_ms * 1e3, 2), "frac": round(dq_gbs / HBM_PEAK_GBS, 4)},
+            "us": round(dq_ms * 1e3, 2), "frac": round(dq_gbs / HBM_PEAK_GBS, 4),
+            "frac_of_copy_ceiling": None if ceiling is None else
+            round(dq_gbs / ceiling["expand_copy_1to4"]["gbs"], 4)},
+        "ceiling": ceiling,
         f"{other}_schedule": None if args.no_context else {
             "ms_per_step": round(other_ms, 4),
             "value": round(step_bytes / (other_ms * 1e-3) / 1e9, 1)},

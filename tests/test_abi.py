@@ -262,3 +262,14 @@ def test_gemm_empty_and_oversized(lib):
                         None, 0, None) == 0
     assert _gm(lib, M=1 << 30) == 2
     assert _gm(lib, N=1 << 30, K=1 << 12) == 2
+
+
+def test_probes_validate_arguments(lib):
+    assert lib.nf4_probe_stream_read(None, 0, None, None) == 0
+    assert lib.nf4_probe_stream_read(None, 64, FAKE, None) == 1
+    assert lib.nf4_probe_stream_read(C.c_void_p(0x1008), 64, FAKE, None) == 1   # misaligned
+    assert lib.nf4_probe_stream_read(FAKE, 40, FAKE, None) == 1                  # not 16 * k
+    assert lib.nf4_probe_expand_copy(None, 0, None, None) == 0
+    assert lib.nf4_probe_expand_copy(FAKE, 64, None, None) == 1
+    assert lib.nf4_probe_expand_copy(FAKE, 64, C.c_void_p(0x1008), None) == 1   # dst misaligned
+    assert lib.nf4_probe_expand_copy(FAKE, 6, FAKE, None) == 1                   # not 4 * k

@@ -35,5 +35,7 @@ from ._binding import (  # noqa: F401
     nf4_gemv_absmax32,
     nf4_quantize,
     nf4_quantize_absmax32,
+    probe_expand_copy,
+    probe_stream_read,
     status_string,
 )

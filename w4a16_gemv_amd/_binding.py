@@ -22,6 +22,7 @@ EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv", "
             "nf4_gemm_workspace_size",
             "nf4_dequant_absmax32", "nf4_gemv_absmax32", "nf4_gemv_grouped",
             "nf4_gemv_grouped_absmax32", "int4_gemv_grouped",
+            "nf4_probe_stream_read", "nf4_probe_expand_copy",
             "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
             "nf4_quantize", "nf4_quantize_absmax32", "int4_dequant", "int4_gemv",
             "int4_quantize")
@@ -65,6 +66,10 @@ def load() -> C.CDLL:
     lib.nf4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, i32, p, C.c_size_t, p]
     lib.nf4_gemv_grouped_absmax32.restype = C.c_int
     lib.nf4_gemv_grouped_absmax32.argtypes = [p, i32, i64, i64, i32, i32, p, C.c_size_t, p]
+    lib.nf4_probe_stream_read.restype = C.c_int
+    lib.nf4_probe_stream_read.argtypes = [p, C.c_size_t, p, p]
+    lib.nf4_probe_expand_copy.restype = C.c_int
+    lib.nf4_probe_expand_copy.argtypes = [p, C.c_size_t, p, p]
     lib.int4_gemv_grouped.restype = C.c_int
     lib.int4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, C.c_size_t, p]
     lib.nf4_gemv_sched_size.restype = C.c_size_t
@@ -206,6 +211,23 @@ def nf4_gemm(packed, absmax_q, absmax2, code2, offset: float, N: int, K: int, x:
 
 
 _F32 = (torch.float32,)
+
+
+def probe_stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Bandwidth probe: read all of src (uint8, 16-byte aligned, a multiple of
+    16 bytes) once; sink is a device int32 scalar tensor."""
+    _check("nf4_probe_stream_read",
+           load().nf4_probe_stream_read(_dev(src, "src", _U8, 0), src.numel(),
+                                        _dev(sink, "sink", (torch.int32,), 1), _stream(src)))
+
+
+def probe_expand_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Bandwidth probe: read src (uint8) and write 4x its bytes to dst (uint8)."""
+    if dst.numel() < 4 * src.numel():
+        raise ValueError("dst must hold 4x the bytes of src")
+    _check("nf4_probe_expand_copy",
+           load().nf4_probe_expand_copy(_dev(src, "src", _U8, 0), src.numel(),
+                                        _dev(dst, "dst", _U8, 4 * src.numel()), _stream(src)))
 
 
 def _gemv_io(x: torch.Tensor, N: int, K: int, y: torch.Tensor | None):

@@ -16,7 +16,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("nf4_kernels.hip", "nf4_gemm.hip", "nf4_quantize.hip")]
+SRCS = [os.path.join(PKG, "csrc", f)
+        for f in ("nf4_kernels.hip", "nf4_gemm.hip", "nf4_quantize.hip", "nf4_probe.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnf4.so")
 

@@ -160,7 +160,8 @@ SL_GEMV_EDGE = [
     (1, 64, 64), (3, 64, 64), (5, 2048, 64), (7, 2080, 64), (33, 32, 32), (17, 96, 32),
     (9, 16384, 64), (3, 16416, 64), (11, 1000, 64), (13, 2, 64), (6, 130, 2),
     (300, 1536, 128), (257, 1536, 16), (64, 4096, 1 << 12), (1376, 4096, 64),
-    (4096, 1376, 64), (100, 8192, 64), (50, 12288, 64), (40, 12352, 64),
+    (4096, 1376, 64), (100, 8192, 64), (50, 12288, 64), (40, 12352, 64), (21, 2112, 64),
+    (19, 4160, 128),
 ]
 
 

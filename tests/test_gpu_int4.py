@@ -163,7 +163,7 @@ INT4_GEMV_EDGE = [
     (1, 128, 128), (3, 256, 128), (5, 2048, 128), (7, 2080, 32), (33, 32, 32), (17, 96, 32),
     (9, 16384, 128), (3, 16416, 32), (11, 1000, 8), (13, 2, 2), (6, 130, 2), (300, 1536, 128),
     (257, 1536, 16), (64, 4096, 4096), (1376, 4096, 128), (4096, 1376, 32), (100, 8192, 256),
-    (50, 12288, 128), (4096, 4096, 64), (40, 12352, 64),
+    (50, 12288, 128), (4096, 4096, 64), (40, 12352, 64), (21, 2112, 64), (19, 4160, 64),
 ]
 
 

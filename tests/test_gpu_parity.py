@@ -207,6 +207,9 @@ GEMV_EDGE = [
     (1376, 4096, 64, 256), (4096, 1376, 64, 256),
     # two and three 4096-column passes per wave, at their upper ends
     (100, 8192, 64, 256), (50, 12288, 64, 256), (40, 12352, 64, 256),
+    # one 64-column block past a wave load's start: only lanes 0 and 1 of the
+    # second load (2112) or of the second pass's first load (4160) hold columns
+    (21, 2112, 64, 256), (19, 4160, 128, 2),
 ]
 
 

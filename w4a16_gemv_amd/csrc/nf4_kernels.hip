@@ -940,18 +940,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 // ---------------------------------------------------------------------------
 // The wave-per-row streaming GEMV (K a multiple of 64, blocksize >= 64).
 //
-// Every wave works alone: lane l owns the 64 columns [64 l + 4096 p, +64) of
-// pass p < P (P = ceil(K / 4096)), which is exactly one 64-aligned piece of a
-// first-level block, so the lane loads 32 contiguous packed bytes and one
-// absmax_q / absmax2 pair per row and pass, and applies one absmax_real to the
-// sum of its 64 products.  A wave reduces its own rows (no cross-wave sums, no
-// barriers), so the waves of a workgroup share only the decode table and
-// code2.  The concatenated rows of all matrices are split evenly into
-// contiguous ranges, one per wave; a wave walks its range in groups of up to R
-// rows with the loads of the group after next issued before the current group
-// is computed (three register buffers, loop unrolled by three).
+// Every wave works alone.  Pass p < P (P = ceil(K / 4096)) covers the columns
+// [4096 p, +4096) of a row, 2 KiB of packed bytes, read by two 16-byte loads
+// per lane: load h (h = 0, 1) of lane l takes the 32 columns
+// [4096 p + 2048 h + 32 l, +32), so each load instruction of the wave reads
+// one contiguous KiB (a lane-strided pair of loads that each cover half of
+// every line reads about a fifth slower on this part).  A 32-column piece lies
+// inside one first-level block, so lanes 2j and 2j+1 hold the two halves of
+// block j of the pass (first load) and of block 32 + j (second load).  Each
+// lane sums its 32 products per load; one DPP swap inside the lane pair adds
+// the partner's half, after which lane 2j holds the sum of block j and lane
+// 2j+1 that of block 32 + j.  So each lane still loads one absmax_q / absmax2
+// pair per row and pass -- that of the block it finishes -- and applies one
+// absmax_real to the block's 64-product sum.  A wave reduces its own rows (no
+// cross-wave sums, no barriers), so the waves of a workgroup share only the
+// decode table and code2.  The concatenated rows of all matrices are split
+// evenly into contiguous ranges, one per wave; a wave walks its range in
+// groups of up to R rows with the loads of the group after next issued before
+// the current group is computed (three register buffers, loop unrolled by
+// three).
 // ---------------------------------------------------------------------------
-constexpr int kWaveCols = 4096;  // columns per pass of a wave (64 lanes x 64)
+constexpr int kWaveCols = 4096;  // columns per pass of a wave (2 loads x 64 lanes x 32)
 
 template <int R, int P, int FMT>
 struct WaveGroup {
@@ -960,13 +969,13 @@ struct WaveGroup {
   uint16_t a2[R][P];  // double-quantized format only
 };
 
-// Per-lane offsets of pass p: packed byte offset inside a row and activation
-// byte offset (pushed out of range when the lane's columns are past K), and
-// the lane's first column.
+// Per-lane offsets of load h of pass p: packed byte offset inside a row and
+// activation byte offset (pushed out of range when the load's columns are past
+// K), and the first column of the block the lane finishes in pass p.
 template <int P>
 struct WaveLane {
-  uint32_t pk[P];
-  uint32_t x[P];
+  uint32_t pk[P][2];
+  uint32_t x[P][2];
   uint32_t c0[P];
 };
 
@@ -982,8 +991,9 @@ __device__ __forceinline__ void load_wave_group(WaveGroup<R, P, FMT>& g, const L
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint32_t blk = (row * static_cast<uint32_t>(K) + wl.c0[p]) >> log2bs;
-      g.pk[rr][p][0] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p], srow, kStreamLoad);
-      g.pk[rr][p][1] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p] + 16u, srow,
+      g.pk[rr][p][0] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p][0], srow,
+                                                              kStreamLoad);
+      g.pk[rr][p][1] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p][1], srow,
                                                               kStreamLoad);
       if constexpr (FMT == kFmtAbsmax32) {
         g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b32(mb.absmax_q, blk * 4u, sfar, 0);
@@ -999,7 +1009,8 @@ __device__ __forceinline__ void load_wave_group(WaveGroup<R, P, FMT>& g, const L
   }
 }
 
-// The lane's 64 activations per pass and batch row (raw bf16 pairs).
+// The lane's 64 activations per pass and batch row (raw bf16 pairs): xr[.][p]
+// [0..3] are the 32 columns of load 0, [4..7] those of load 1.
 template <int B, int P>
 __device__ __forceinline__ void load_wave_x(u32x4 (&xr)[B][P][8], __amdgpu_buffer_rsrc_t xb,
                                             const WaveLane<P>& wl, int K) {
@@ -1009,22 +1020,28 @@ __device__ __forceinline__ void load_wave_x(u32x4 (&xr)[B][P][8], __amdgpu_buffe
     for (int p = 0; p < P; ++p)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        xr[b][p][j] = __builtin_amdgcn_raw_buffer_load_b128(xb, wl.x[p] + 16u * j,
+        xr[b][p][j] = __builtin_amdgcn_raw_buffer_load_b128(xb, wl.x[p][j >> 2] + 16u * (j & 3),
                                                              static_cast<uint32_t>(b * K * 2), 0);
 }
 
-// val[rr * B + b] = sum over the lane's columns of row rr of weight * x.  The
-// lane's R P 8 packed dwords are walked in order with the four table reads of
-// the next dword issued before the eight v_dot2c_f32_bf16 of the current one
+// Sum over a lane pair (2j, 2j+1) with DPP quad_perm [1,0,3,2]; both lanes get
+// the same bits (the add is commutative).
+__device__ __forceinline__ float pair_lane_sum(float v) { return dpp_add<0xB1, 0xF>(v); }
+
+// val[rr * B + b] = the lane's share of row rr of weight * x.  The lane's
+// R P 8 packed dwords are walked in order with the four table reads of the
+// next dword issued before the eight v_dot2c_f32_bf16 of the current one
 // (same decode table as the team kernel); the scheduling barriers keep the
 // compiler from hoisting more reads, whose results would not fit in
-// registers.  Each (row, pass) piece is one 64-column block piece: its sum is
-// scaled by the block's absmax_real and added to the row's value.
+// registers.  Each load's 32 products are summed on their own; at the end of
+// a (row, pass) the two half sums of each block are completed across the lane
+// pair, and the lane scales the block it owns (odd lanes: the second load's)
+// by its absmax_real.
 template <int B, int R, int P, int FMT>
 __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u32x4 (&xr)[B][P][8],
                                           uint32_t copy_off, const uint2* s_pairs,
-                                          const float* s_code2, float offset,
-                                          const bool (&lane_in)[P], const float (&xs)[B][P],
+                                          const float* s_code2, float offset, bool odd,
+                                          const bool (&own_in)[P], const float (&xs)[B][P],
                                           float (&val)[R * B]) {
   constexpr int U = R * P * 8;
   const char* tab = reinterpret_cast<const char*>(s_pairs);
@@ -1043,14 +1060,14 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
   };
 #pragma unroll
   for (int v = 0; v < R * B; ++v) val[v] = 0.0f;
-  float part[B];
+  float part[B], half0[B];
   fetch(0, t[0]);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u + 1 < U) fetch(u + 1, t[(u + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
     const int rr = u / (P * 8), p = (u / 8) % P, hj = u % 8;
-    if (hj == 0) {
+    if ((hj & 3) == 0) {
 #pragma unroll
       for (int b = 0; b < B; ++b) part[b] = 0.0f;
     }
@@ -1070,15 +1087,28 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
                                                     part[b], false);
       }
     }
+    if (hj == 3) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) half0[b] = part[b];
+    }
     if (hj == 7) {
+      // the 64-product sum of the lane's block: its own half plus the
+      // partner's half of the same load
+      float blk[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float s0 = pair_lane_sum(half0[b]);
+        const float s1 = pair_lane_sum(part[b]);
+        blk[b] = odd ? s1 : s0;
+      }
       if constexpr (FMT == kFmtInt4) {
-        // s (sum q x - z sum x) over the lane's 64 columns of one group
+        // s (sum q x - z sum x) over the 64 columns of one group
         const float sc = f16_to_f32(g.q[rr][p]);
         const float z = f16_to_f32(g.a2[rr][p]);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           const float zt = z * xs[b][p];
-          val[rr * B + b] += lane_in[p] ? sc * (part[b] - zt) : 0.0f;
+          val[rr * B + b] += own_in[p] ? sc * (blk[b] - zt) : 0.0f;
         }
       } else {
         float a;
@@ -1089,7 +1119,7 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
           a = prod + offset;
         }
 #pragma unroll
-        for (int b = 0; b < B; ++b) val[rr * B + b] += lane_in[p] ? a * part[b] : 0.0f;
+        for (int b = 0; b < B; ++b) val[rr * B + b] += own_in[p] ? a * blk[b] : 0.0f;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1221,13 +1251,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   }
 
   WaveLane<P> wl;
-  bool lane_in[P];
+  const bool odd = (lane & 1) != 0;
+  bool own_in[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    const int c0 = kWaveCols * p + 64 * lane;
-    lane_in[p] = c0 < K;
-    wl.pk[p] = lane_in[p] ? static_cast<uint32_t>(c0 >> 1) : kFar;
-    wl.x[p] = lane_in[p] ? static_cast<uint32_t>(c0 * 2) : kFar;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = kWaveCols * p + 2048 * h + 32 * lane;
+      const bool in = c < K;
+      wl.pk[p][h] = in ? static_cast<uint32_t>(c >> 1) : kFar;
+      wl.x[p][h] = in ? static_cast<uint32_t>(c * 2) : kFar;
+    }
+    // the block this lane finishes: first load's (even) or second load's (odd)
+    const int c0 = kWaveCols * p + (odd ? 2048 : 0) + 32 * (lane & ~1);
+    own_in[p] = c0 < K;
     wl.c0[p] = static_cast<uint32_t>(c0);
   }
 
@@ -1273,12 +1310,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
       for (int b = 0; b < B; ++b)
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          uint32_t w[32];
+          // over the 64 columns of the lane's block: the lane's half of each
+          // load completed across the lane pair, as for the products
+          float hs[2];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
+          for (int h = 0; h < 2; ++h) {
+            uint32_t w[16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w[4 * j + i] = xr[b][p][j][i];
-          xs[b][p] = pair_sum(w);
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) w[4 * j + i] = xr[b][p][4 * h + j][i];
+            hs[h] = pair_lane_sum(pair_sum(w));
+          }
+          xs[b][p] = odd ? hs[1] : hs[0];
         }
     }
   };
@@ -1302,7 +1346,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     // (a chunked range may end inside a round: empty groups skip the work)
     if (len0 > 0) {
       float val[R * B];
-      wave_rows<B, R, P, FMT>(cur, xr, copy_off, s_pairs, s_code2, ob0.offset, lane_in, xs, val);
+      wave_rows<B, R, P, FMT>(cur, xr, copy_off, s_pairs, s_code2, ob0.offset, odd, own_in, xs,
+                              val);
       // value v of the group ends up in lane 32 v (pair) or in row 16-lane
       // row r with v = 2 (r & 1) + (r >> 1) (quad)
       float tot;

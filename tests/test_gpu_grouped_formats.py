@@ -51,6 +51,8 @@ CASES = [
     (1536, [(1536, 910), (256, 911), (8960, 912)], 64),
     (11008, [(300, 920), (5, 921)], 64),          # three 4096-column passes
     (8192, [(200, 930)], 256),                     # two passes
+    (4160, [(64, 935), (3, 936)], 64),             # second pass: one 64-column block
+    (12352, [(40, 950), (3, 951)], 64),            # four passes: the team kernel
     (96, [(33, 940), (7, 941)], 32),               # the team kernel only
 ]
 

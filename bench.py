@@ -317,6 +317,7 @@ def build_context(dev, name, bs=None):
             t, out = st
             t.dequant(out=out)
         return dict(sets=sets, step_bytes=set_bytes, flops=0, launches=1, run=run, blocksize=bs,
+                    copy_read_bytes=set_bytes - 2 * cfg.n,
                     dominant=f"dequant_vec_kernel ({cfg.rows}x{cfg.cols}"
                              f"{', fp32 absmax' if single else ''}{', int4' if int4 else ''})",
                     dominant_bytes=set_bytes, dominant_flops=0)
@@ -410,7 +411,28 @@ def bench_context(args, dev):
                        "frac": round(tf / VALU_PEAK_TFLOPS, 4)}
     log(f"[bench] {args.workload}: step {ms * 1e3:.1f} us ({value:.0f} GB/s); dominant "
         f"{dom_us:.1f} us ({dom_gbs:.0f} GB/s); {len(sets)} rotating sets, {reps} graph replays")
-    return dict(value=value, ms=ms, roofline=roof, sets=len(sets), launches=wl["launches"],
+    ceiling = None
+    if wl.get("copy_read_bytes") and not args.no_ceiling:
+        # the same stream without the decode, at the same size and rotation:
+        # read R bytes, write 4 R with streaming stores (nf4_probe_expand_copy)
+        import w4a16_gemv_amd as nf4
+        rb = wl["copy_read_bytes"] // 16 * 16
+        pairs = [(torch.full((rb,), 7, dtype=torch.uint8, device=dev),
+                  torch.empty(4 * rb, dtype=torch.uint8, device=dev)) for _ in sets]
+
+        def all_copies():
+            for src, dst in pairs:
+                nf4.probe_expand_copy(src, dst)
+        g_copy = capture(all_copies, stream)
+        copy_us = 1e3 * time_graph(g_copy, reps, args.warmup, stream) / len(sets)
+        ceiling = {"expand_copy_1to4": {"bytes": 5 * rb, "us": round(copy_us, 3),
+                                        "gbs": round(5 * rb / (copy_us * 1e-6) / 1e9, 1)}}
+        roof["frac_of_copy_ceiling"] = round(dom_gbs / ceiling["expand_copy_1to4"]["gbs"], 4)
+        log(f"[bench] ceiling: 1:4 expand copy of {5 * rb} bytes {copy_us:.2f} us "
+            f"({ceiling['expand_copy_1to4']['gbs']:.0f} GB/s); dequant at "
+            f"{roof['frac_of_copy_ceiling']:.3f} of its rate")
+        del pairs
+    return dict(value=value, ms=ms, roofline=roof, sets=len(sets), launches=wl["launches"], ceiling=ceiling,
                 step_bytes=wl["step_bytes"], batch=wl.get("batch", 1), steps=reps * len(sets),
                 step_tflops=wl["flops"] / (ms * 1e-3) / 1e12 if wl["flops"] else None)
 
@@ -509,7 +531,7 @@ def main():
                        "prewarm_s": args.prewarm},
             "pct_of_peak": round(100 * r["value"] / HBM_PEAK_GBS, 2),
             "step_tflops": None if r["step_tflops"] is None else round(r["step_tflops"], 2),
-            "roofline": r["roofline"], "cpu_baseline": None}), flush=True)
+            "roofline": r["roofline"], "ceiling": r["ceiling"], "cpu_baseline": None}), flush=True)
         return
     fmt = sweep_format(args.workload)
     dq_bytes_f, gv_bytes_f = format_bytes(fmt)

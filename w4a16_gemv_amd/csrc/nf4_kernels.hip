@@ -1037,16 +1037,23 @@ __device__ __forceinline__ float pair_lane_sum(float v) { return dpp_add<0xB1, 0
 // a (row, pass) the two half sums of each block are completed across the lane
 // pair, and the lane scales the block it owns (odd lanes: the second load's)
 // by its absmax_real.
-template <int B, int R, int P, int FMT>
+//
+// XL: the activations come from the workgroup's LDS copy s_x (lane-major:
+// the 8 columns of dword hj of pass p for batch row b and lane l at
+// s_x[((b P + p) 8 + hj) 64 + l]), read with the table entries one dword
+// ahead, instead of from the registers xr.
+template <int B, int R, int P, int FMT, bool XL = false>
 __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u32x4 (&xr)[B][P][8],
                                           uint32_t copy_off, const uint2* s_pairs,
                                           const float* s_code2, float offset, bool odd,
                                           const bool (&own_in)[P], const float (&xs)[B][P],
-                                          float (&val)[R * B]) {
+                                          float (&val)[R * B], const u32x4* s_x = nullptr,
+                                          int lane = 0) {
   constexpr int U = R * P * 8;
   const char* tab = reinterpret_cast<const char*>(s_pairs);
   uint2 t[2][4];
-  auto fetch = [&](int u, uint2 (&tt)[4]) {
+  u32x4 xv[2][B];
+  auto fetch = [&](int u, uint2 (&tt)[4], u32x4 (&xx)[B]) {
     const int rr = u / (P * 8), p = (u / 8) % P, hj = u % 8;
     const uint32_t d = g.pk[rr][p][hj >> 2][hj & 3];
 #pragma unroll
@@ -1057,14 +1064,18 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
       else
         tt[i] = *reinterpret_cast<const uint2*>(tab + addr);
     }
+    if constexpr (XL) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) xx[b] = s_x[((b * P + p) * 8 + hj) * 64 + lane];
+    }
   };
 #pragma unroll
   for (int v = 0; v < R * B; ++v) val[v] = 0.0f;
   float part[B], half0[B];
-  fetch(0, t[0]);
+  fetch(0, t[0], xv[0]);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (u + 1 < U) fetch(u + 1, t[(u + 1) & 1]);
+    if (u + 1 < U) fetch(u + 1, t[(u + 1) & 1], xv[(u + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
     const int rr = u / (P * 8), p = (u / 8) % P, hj = u % 8;
     if ((hj & 3) == 0) {
@@ -1078,7 +1089,7 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
       for (int b = 0; b < B; ++b) {
         // copied out first: a bit_cast of a vector-element lvalue reads
         // element 0 whatever the index
-        const uint32_t xw = xr[b][p][hj][i];
+        const uint32_t xw = XL ? xv[u & 1][b][i] : xr[b][p][hj][i];
         const bf16x2 xp = __builtin_bit_cast(bf16x2, xw);
         part[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.x), xp, part[b],
                                                   false);
@@ -1423,6 +1434,202 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 }
 
 // ---------------------------------------------------------------------------
+// The shared-activation GEMV (grouped launches, batch 1-2, 4096 < K <= 16384,
+// K % 64 == 0, blocksize >= 64).
+//
+// With more than one pass the wave kernel keeps 32 B P VGPRs of activations
+// per wave and fits only two waves per SIMD: too few independent instruction
+// streams to keep the VALU and LDS busy.  Here a 1024-thread workgroup (16
+// waves, four per SIMD, one workgroup per CU) keeps the activations of the
+// matrix it works on in LDS, in the lane order in which the wave kernel holds
+// them in registers, so each ds_read_b128 of the 64 lanes reads 1 KiB of
+// consecutive banks.  The lane layout, decode and per-row arithmetic are the
+// wave kernel's (wave_rows with XL).
+//
+// The concatenated rows are split evenly into one contiguous range per
+// workgroup.  The workgroup walks its range one matrix at a time: it stages
+// that matrix's activations (a barrier before and after), then its waves
+// claim groups of R rows from an LDS counter until the matrix's part of the
+// range is used up.  Each wave computes one group while the loads of its next
+// group are in flight (two register buffers, whole rounds of two steps).
+// ---------------------------------------------------------------------------
+constexpr int kXlThreads = 1024;
+
+template <int B, int R, int P, int NBUF, int FMT>
+__global__ __launch_bounds__(kXlThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_xlds_kernel(
+    const nf4_gemv_desc* __restrict__ descs, int count, int total_rows, int K, int log2bs,
+    int log2s2, const uint16_t* __restrict__ code2) {
+  static_assert(R * B <= 4, "one pair or quad reduction per group");
+  static_assert(NBUF == 2 || NBUF == 3, "two or three register buffers");
+  __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
+  __shared__ float s_code2[256];
+  __shared__ int s_rowbeg[kMaxDescs + 1];
+  __shared__ u32x4 s_x[B * P * 8 * 64];  // activations, 8 KiB per pass and batch row
+  __shared__ unsigned s_next;            // next row group of the current matrix
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const uint16_t code2_bits = __builtin_amdgcn_raw_buffer_load_b16(
+      rsrc(FMT == kFmtDouble ? code2 : nullptr, 512), static_cast<uint32_t>(tid) * 2u, 0u, 0);
+  for (int i = tid; i < count; i += blockDim.x) s_rowbeg[i] = static_cast<int>(descs[i].row_begin);
+  if (tid == 0) s_rowbeg[count] = total_rows;
+  if (FMT == kFmtDouble && tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
+  const uint32_t copy_off = build_decode_table<FMT>(s_pairs, tid, blockDim.x, lane);
+  __syncthreads();
+  const RowBegins rbeg{s_rowbeg, total_rows};
+  int lo, hi;
+  split_rows(static_cast<uint32_t>(total_rows), gridDim.x, blockIdx.x, &lo, &hi);
+
+  // the lane's columns, as in the wave kernel
+  WaveLane<P> wl;
+  const bool odd = (lane & 1) != 0;
+  bool own_in[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = kWaveCols * p + 2048 * h + 32 * lane;
+      wl.pk[p][h] = c < K ? static_cast<uint32_t>(c >> 1) : kFar;
+      wl.x[p][h] = kFar;  // activations come from LDS
+    }
+    const int c0 = kWaveCols * p + (odd ? 2048 : 0) + 32 * (lane & ~1);
+    own_in[p] = c0 < K;
+    wl.c0[p] = static_cast<uint32_t>(c0);
+  }
+
+  int m = 0;  // last matrix whose first row is <= lo
+  {
+    int a = 0, z = count - 1;
+    while (a < z) {
+      const int mid = (a + z + 1) >> 1;
+      if (rbeg(mid) <= lo) a = mid; else z = mid - 1;
+    }
+    m = a;
+  }
+  u32x4 xr_unused[B][P][8];  // wave_rows reads the LDS copy instead
+  for (; m < count && rbeg(m) < hi; ++m) {
+    const int beg = rbeg(m), end = rbeg(m + 1);
+    const int s0 = max(lo, beg), s1 = min(hi, end);
+    if (s1 <= s0) continue;
+    const nf4_gemv_desc d = open_desc<FMT>(descs, nf4_gemv_desc{}, m, s1 - s0, rbeg, K);
+    __syncthreads();  // every wave is done with the previous matrix's activations
+    {
+      // entry e = ((b P + p) 8 + hj) 64 + l: columns 4096 p + 2048 (hj >> 2) +
+      // 32 l + 8 (hj & 3), 8 of them, of batch row b (zeros past K)
+      const __amdgpu_buffer_rsrc_t xb = rsrc(d.x, static_cast<uint32_t>(B * K * 2));
+      for (int e = tid; e < B * P * 8 * 64; e += kXlThreads) {
+        const int l = e & 63, hj = (e >> 6) & 7, bp = e >> 9;
+        const int b = bp / P, p = bp - b * P;
+        const int c = kWaveCols * p + 2048 * (hj >> 2) + 32 * l + 8 * (hj & 3);
+        s_x[e] = __builtin_amdgcn_raw_buffer_load_b128(
+            xb, c < K ? static_cast<uint32_t>((b * K + c) * 2) : kFar, 0u, 0);
+      }
+    }
+    if (tid == 0) s_next = 0;
+    __syncthreads();
+    if (d.packed == nullptr) continue;  // a skipped matrix (the same for every wave)
+    const LoadBufs lb = load_bufs<FMT>(d, K, log2bs, log2s2);
+    const OutBufs ob = out_bufs<B>(d);
+    float xs[B][P];  // INT4: the activation sums of the lane's blocks
+    if constexpr (FMT == kFmtInt4) {
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          float hs[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uint32_t w[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const u32x4 q = s_x[((b * P + p) * 8 + 4 * h + j) * 64 + lane];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) w[4 * j + i] = q[i];
+            }
+            hs[h] = pair_lane_sum(pair_sum(w));
+          }
+          xs[b][p] = odd ? hs[1] : hs[0];
+        }
+    }
+    const int base = s0 - beg;  // first row of this part, inside the matrix
+    const int nrows = s1 - s0;
+    auto claim = [&](int* rl, int* len) {
+      uint32_t g = 0;
+      if (lane == 0) g = atomicAdd(&s_next, 1u);
+      g = __builtin_amdgcn_readfirstlane(g);
+      const int r = static_cast<int>(g) * R;
+      *rl = base + r;
+      *len = r < nrows ? min(R, nrows - r) : 0;
+    };
+    // the group's rows and y: reduce the R B row values over the lanes and
+    // store them
+    auto finish = [&](const float (&val)[R * B], int rl, int len) {
+      float tot;
+      int v;
+      bool first;
+      if constexpr (R * B <= 2) {
+        tot = wave_sum_pair(val[0], R * B > 1 ? val[R * B - 1] : 0.0f);
+        v = lane >> 5;
+        first = (lane & 31) == 0;
+      } else {
+        tot = wave_sum_quad(val[0], val[1], val[2], R * B > 3 ? val[3] : 0.0f);
+        const int row16 = lane >> 4;
+        v = ((row16 & 1) << 1) | (row16 >> 1);
+        first = (lane & 15) == 0;
+      }
+      const int rr = v / B, b = v % B;
+      const bool store = first && v < R * B && rr < len;
+      const uint32_t off = static_cast<uint32_t>((b * ob.N + rl + rr) * 2);
+      __builtin_amdgcn_raw_buffer_store_b16(to_half_bits<NF4_BF16>(tot), ob.y,
+                                            store ? off : kOutOfRange, 0, 0);
+    };
+    auto compute = [&](const WaveGroup<R, P, FMT>& g, int rl, int len) {
+      if (len > 0) {
+        float val[R * B];
+        wave_rows<B, R, P, FMT, true>(g, xr_unused, copy_off, s_pairs, s_code2, ob.offset, odd,
+                                      own_in, xs, val, s_x, lane);
+        finish(val, rl, len);
+      }
+    };
+    WaveGroup<R, P, FMT> ga, gb;
+    int rla, lena, rlb, lenb;
+    claim(&rla, &lena);
+    load_wave_group<R, P, FMT>(ga, lb, rla, lena, wl, K, log2bs, log2s2);
+    claim(&rlb, &lenb);
+    load_wave_group<R, P, FMT>(gb, lb, rlb, lenb, wl, K, log2bs, log2s2);
+    if constexpr (NBUF == 2) {
+      // compute a group, then load the group after next into its buffer
+      auto step = [&](WaveGroup<R, P, FMT>& g, int& rl, int& len) {
+        compute(g, rl, len);
+        claim(&rl, &len);
+        load_wave_group<R, P, FMT>(g, lb, rl, len, wl, K, log2bs, log2s2);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      while (lena > 0 || lenb > 0) {
+        step(ga, rla, lena);
+        step(gb, rlb, lenb);
+      }
+    } else {
+      // load the group after next into the third buffer, then compute; the
+      // buffers change roles over a round of three steps
+      WaveGroup<R, P, FMT> gc;
+      int rlc = 0, lenc = 0;
+      auto step = [&](WaveGroup<R, P, FMT>& cur, int rl, int len, WaveGroup<R, P, FMT>& fut,
+                      int& rlf, int& lenf) {
+        claim(&rlf, &lenf);
+        load_wave_group<R, P, FMT>(fut, lb, rlf, lenf, wl, K, log2bs, log2s2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur, rl, len);
+      };
+      while (lena > 0) {
+        step(ga, rla, lena, gc, rlc, lenc);
+        step(gb, rlb, lenb, ga, rla, lena);
+        step(gc, rlc, lenc, gb, rlb, lenb);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Fused dequant-GEMV, batched path (batch 3-8).
 //
 // A workgroup owns R consecutive rows and has one wave per 2048-column slab
@@ -1698,6 +1905,19 @@ nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, 
   return launch_status();
 }
 
+// The shared-activation kernel for (B, P): one 1024-thread workgroup per CU
+// at most, each with at least 64 rows.
+template <int B, int R, int P, int NBUF, int FMT>
+nf4_status xlds_launch(const nf4_gemv_desc* descs, int count, int total_rows, int K, int lbs,
+                       int ls2, const uint16_t* code2, hipStream_t st) {
+  const int64_t cus = device_cus();
+  const int64_t want = (static_cast<int64_t>(total_rows) + 63) / 64;
+  const int64_t grid = want < cus ? (want > 0 ? want : 1) : cus;
+  hipLaunchKernelGGL((gemv_xlds_kernel<B, R, P, NBUF, FMT>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(kXlThreads), 0, st, descs, count, total_rows, K, lbs, ls2, code2);
+  return launch_status();
+}
+
 // Returns NF4_EUNSUPPORTED (without launching) when no wave-per-row
 // configuration covers (B, K, blocksize).
 template <int B, int FMT>
@@ -1710,12 +1930,19 @@ nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
     if (P == 1) return wave_launch<1, 2, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
   }
   // the other configurations serve grouped launches only
-  if constexpr (B == 1) {
-    if (P == 2) return wave_launch<1, 1, 2, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
-    if (P == 3) return wave_launch<1, 1, 3, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
-  } else if constexpr (B == 2) {
+  if constexpr (B == 2) {
     if (P == 1) return wave_launch<2, 1, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
-    if (P == 2) return wave_launch<2, 1, 2, 2, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+  }
+  if (descs == nullptr) return NF4_EUNSUPPORTED;
+  // more than one pass: the activations go to LDS (gemv_xlds_kernel)
+  if constexpr (B == 1) {
+    if (P == 2) return xlds_launch<1, 1, 2, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 3) return xlds_launch<1, 1, 3, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 4) return xlds_launch<1, 1, 4, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+  } else if constexpr (B == 2) {
+    if (P == 2) return xlds_launch<2, 1, 2, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 3) return xlds_launch<2, 1, 3, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 4) return xlds_launch<2, 1, 4, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
   }
   return NF4_EUNSUPPORTED;
 }

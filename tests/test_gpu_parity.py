@@ -364,6 +364,46 @@ def test_gemv_grouped_skips_bad_descriptors():
     assert G.gemv_within_tolerance(y, yr, S)[0]
 
 
+@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("K", [8192, 11008, 16384])
+def test_gemv_grouped_many_small_matrices(K, batch):
+    """More than one pass, many matrices of 1-9 rows with their own
+    activations: a workgroup's row range crosses many matrices, so the
+    activations are staged again for each one; a matrix with a bad N in the
+    middle is skipped (its y keeps its contents) and the others are computed."""
+    import numpy as np
+    rng = np.random.default_rng(K + batch)
+    shapes = [(int(n), 900 + i) for i, n in enumerate(rng.integers(1, 10, size=120))]
+    shapes[40] = (5, 940)
+    qs, items = [], []
+    for N, seed in shapes:
+        q = oracle.quantize(synth.weights(seed, N * K))
+        d = G.fmt_to_device(q)
+        w = nf4.NF4Tensor(d["packed"], d["absmax_q"], d["absmax2"], d["code2"], q.offset, q.n)
+        xb = synth.activations(seed + 7, batch, K)
+        base, yv = G.guarded(batch * N, torch.bfloat16)
+        items.append((w, N, G.x_to_device(xb), yv.view(batch, N)))
+        qs.append((q, N, xb, base))
+    grp = nf4.GemvGroup(items, K)
+    tab = grp.table.cpu().numpy().copy().view(np.int64).reshape(len(items), 8)
+    tab[40, 5] = 4                                    # N of item 40 no longer matches
+    grp.table.copy_(torch.from_numpy(tab.view(np.uint8).reshape(-1)))
+    items[40][3].fill_(3.0)
+    print(f"[gemv_grouped_many] K={K} B={batch} matrices={len(shapes)} rows={grp.total_rows}",
+          flush=True)
+    grp.launch()
+    torch.cuda.synchronize()
+    assert torch.all(items[40][3] == 3.0), "the bad matrix was written"
+    for i, ((q, N, xb, base), (_, _, _, yv)) in enumerate(zip(qs, items)):
+        assert G.guards_intact(base, batch * N), f"write outside y of item {i}"
+        if i == 40:
+            continue
+        y = G.bf16_to_f64(G.bits16(yv)).reshape(batch, N)
+        yr, S = oracle.gemv(q, N, K, xb)
+        ok, worst = G.gemv_within_tolerance(y, yr, S)
+        assert ok, f"item {i} N={N}: worst {worst:.3g}"
+
+
 def test_graph_replay_matches_eager():
     """A HIP graph holding a grouped GEMV and a dequant, replayed several
     times with eager work and synchronizations in between, reproduces the

@@ -102,41 +102,46 @@ struct GemmLane {
   int log2bs, log2s2;
 };
 
-// 4 x 4 transpose of 8-byte units across the four 16-lane rows of a wave:
-// before, unit p of lane row r is u[p]; after, u[b] of lane row g holds what
-// was unit g of lane row b.
-__device__ __forceinline__ void transpose_units(uint32_t (&u)[4][2]) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const auto s = __builtin_amdgcn_permlane32_swap(u[p][d], u[p + 2][d], false, false);
-      u[p][d] = s[0];
-      u[p + 2][d] = s[1];
-    }
+// The four blocks of a lane's row as loaded (see gemm_load): lane row g
+// holds the 8-byte units 2 (g & 1) and 2 (g & 1) + 1 of block g >> 1 in
+// u[0], u[1] and of block 2 + (g >> 1) in u[2], u[3].  One v_permlane32_swap
+// per dword of the slot pairs (0, 1) and (2, 3) exchanges the high bit of the
+// lane row with the low bit of the slot; afterwards u[b] of lane row g holds
+// unit unit_of_row(g) of block b.
+__device__ __forceinline__ void gather_units(uint32_t (&u)[4][2]) {
 #pragma unroll
   for (int p = 0; p < 4; p += 2)
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-      const auto s = __builtin_amdgcn_permlane16_swap(u[p][d], u[p + 1][d], false, false);
+      const auto s = __builtin_amdgcn_permlane32_swap(u[p][d], u[p + 1][d], false, false);
       u[p][d] = s[0];
       u[p + 1][d] = s[1];
     }
 }
+
+// The unit (k 16 u .. 16 u + 15 of a block) that lane row g holds after
+// gather_units: the two bits of g swapped.
+__device__ __forceinline__ int unit_of_row(int g) { return ((g & 1) << 1) | (g >> 1); }
 
 template <int MT>
 __device__ __forceinline__ void gemm_load(GemmStage<MT>& st, int grp, int kb1, const GemmLane& L) {
   constexpr int R = gemm_r<MT>();
   const uint32_t kbw = static_cast<uint32_t>(grp) * (2u * R) + L.half * R;  // the wave's first block
   if constexpr (R == 4) {
-    // block kbw + g of the lane's row, whole (its 4 units are transposed
-    // later); a block past kb1 is pushed out of range in the lane's VGPR
-    // offset: a lane-dependent scalar offset would make the compiler loop
-    // over its distinct values around every load
-    const uint32_t wo = L.wrow + (kbw + L.g) * 32u +
-                        (static_cast<int>(kbw + L.g) < kb1 ? 0u : kFar);
-    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(L.rp, wo, 0u, kStreamLoad);
-    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(L.rp, wo + 16u, 0u, kStreamLoad);
+    // the 128 bytes of blocks kbw .. kbw + 3 of the lane's row: lane row g
+    // loads bytes [16 g, +16) (block g >> 1) and [64 + 16 g, +16) (block 2 +
+    // (g >> 1)), so each load instruction reads 64 contiguous bytes of each
+    // of its 16 rows (two loads at 32 g and 32 g + 16 would each cover half
+    // of every line in 16-byte pieces, a slower pattern); gather_units then
+    // regroups the units.  A block past kb1 is pushed out of range in the
+    // lane's VGPR offset: a lane-dependent scalar offset would make the
+    // compiler loop over its distinct values around every load
+    const uint32_t b0 = kbw + (L.g >> 1), b1 = b0 + 2u;
+    const uint32_t base = L.wrow + kbw * 32u + 16u * L.g;
+    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(
+        L.rp, base + (static_cast<int>(b0) < kb1 ? 0u : kFar), 0u, kStreamLoad);
+    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(
+        L.rp, base + 64u + (static_cast<int>(b1) < kb1 ? 0u : kFar), 0u, kStreamLoad);
     st.w[0][0] = lo[0]; st.w[0][1] = lo[1]; st.w[1][0] = lo[2]; st.w[1][1] = lo[3];
     st.w[2][0] = hi[0]; st.w[2][1] = hi[1]; st.w[3][0] = hi[2]; st.w[3][1] = hi[3];
   } else {
@@ -178,16 +183,16 @@ __device__ __forceinline__ void gemm_stash(const GemmStage<MT>& st, char* buf, i
   }
 }
 
-// One block: w = the lane's 8 bytes in MFMA layout, xbuf = the block's
-// activation tile.
+// One block: w = the lane's 8 bytes in MFMA layout (unit `unit` of the
+// block: k 16 unit .. 16 unit + 15), xbuf = the block's activation tile.
 template <int MT>
 __device__ __forceinline__ void gemm_block(const uint32_t (&w)[2], uint32_t q, uint32_t a2,
                                            const char* tab, const char* xbuf, uint32_t copy_off,
-                                           int lane, const float* s_code2, float offset,
+                                           int lane, int unit, const float* s_code2, float offset,
                                            f32x4 (&acc)[MT]) {
-  const int i = lane & 15, g = lane >> 4;
-  // B operands: byte 4 t + e of the lane's 8 bytes holds k 16 g + 8 t + 2 e, + 1;
-  // one 8-byte table read gives its hi and lo pairs
+  const int i = lane & 15;
+  // B operands: byte 4 t + e of the lane's 8 bytes holds k 16 unit + 8 t + 2 e,
+  // + 1; one 8-byte table read gives its hi and lo pairs
   bf16x8 bhv[2], blv[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -204,8 +209,8 @@ __device__ __forceinline__ void gemm_block(const uint32_t (&w)[2], uint32_t q, u
   const float a = prod + offset;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    // A operands: row 16 mt + i, k 16 g + 8 t .. + 7
-    const char* row = xbuf + (16 * mt + i) * kGemmXRow + 32 * g;
+    // A operands: row 16 mt + i, k 16 unit + 8 t .. + 7
+    const char* row = xbuf + (16 * mt + i) * kGemmXRow + 32 * unit;
     const bf16x8 x0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row));
     const bf16x8 x1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16));
     f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -238,6 +243,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g = lane >> 4;
+  // the unit of each block the lane row holds: its own (one block per load)
+  // or the one gather_units leaves it (four blocks per load)
+  const int unit = gemm_r<MT>() == 4 ? unit_of_row(g) : g;
   const int n = blockIdx.x * 64 + (wave & 3) * 16 + j;  // the lane's column
   const int m0 = blockIdx.y * BM;
   const int split = blockIdx.z;
@@ -307,7 +315,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
         wl[r][0] = st[u].w[r][0];
         wl[r][1] = st[u].w[r][1];
       }
-      if constexpr (R == 4) transpose_units(wl);
+      if constexpr (R == 4) gather_units(wl);
       const char* xbuf = s_x + ((p - gp0) & 1) * XGROUP + L.half * (R * XTILE);
       const int kbw = p * 2 * R + static_cast<int>(L.half) * R;
       // (computing dead blocks too, with scale 0, measured 1.8x slower at
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(
       for (int r = 0; r < R; ++r)
         if (kbw + r < kb1)
           gemm_block<MT>(wl[r], st[u].q[r], st[u].a2[r], tab, xbuf + r * XTILE, copy_off, lane,
-                         s_code2, offset, acc);
+                         unit, s_code2, offset, acc);
       gemm_stash<MT>(st[(u + 1) % S], s_x + ((p + 1 - gp0) & 1) * XGROUP, tid);
       __syncthreads();
     }

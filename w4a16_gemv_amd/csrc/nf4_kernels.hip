@@ -977,9 +977,18 @@ struct WaveLane {
   uint32_t pk[P][2];
   uint32_t x[P][2];
   uint32_t c0[P];
+  // regular shapes (see load_wave_group): the lane's block and group inside
+  // its row, and the byte offsets of its scale entries relative to the row's
+  uint32_t sq[P], sa2[P];
 };
 
-template <int R, int P, int FMT>
+// REG (regular shapes: K a multiple of the block size, and the blocks of a
+// row and the s2 blocks of a group dividing one into the other): a row's first
+// block and first group are then the same for all lanes, so the row part of
+// every scale offset is wave-uniform and goes into the scalar offset, and the
+// lane's part is a constant (wl.sq, wl.sa2).  Otherwise the lane forms its
+// block index per row.
+template <int R, int P, int FMT, bool REG = false>
 __device__ __forceinline__ void load_wave_group(WaveGroup<R, P, FMT>& g, const LoadBufs& mb, int rl,
                                                 int len, const WaveLane<P>& wl, int K, int log2bs,
                                                 int log2s2) {
@@ -988,6 +997,29 @@ __device__ __forceinline__ void load_wave_group(WaveGroup<R, P, FMT>& g, const L
     const uint32_t row = static_cast<uint32_t>(rl + rr);
     const uint32_t srow = rr < len ? row * static_cast<uint32_t>(K >> 1) : kFar;
     const uint32_t sfar = rr < len ? 0u : kFar;
+    if constexpr (REG) {
+      const uint32_t rb = row * static_cast<uint32_t>(K >> log2bs);  // the row's first block
+      const uint32_t sq = rr < len ? rb * (FMT == kFmtAbsmax32 ? 4u : FMT == kFmtInt4 ? 2u : 1u)
+                                   : kFar;
+      const uint32_t sa = rr < len ? (FMT == kFmtInt4 ? rb * 2u : (rb >> log2s2) * 2u) : kFar;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        g.pk[rr][p][0] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p][0], srow,
+                                                                kStreamLoad);
+        g.pk[rr][p][1] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, wl.pk[p][1], srow,
+                                                                kStreamLoad);
+        if constexpr (FMT == kFmtAbsmax32) {
+          g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b32(mb.absmax_q, wl.sq[p], sq, 0);
+        } else if constexpr (FMT == kFmtInt4) {
+          g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax_q, wl.sq[p], sq, 0);
+          g.a2[rr][p] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, wl.sa2[p], sa, 0);
+        } else {
+          g.q[rr][p] = __builtin_amdgcn_raw_buffer_load_b8(mb.absmax_q, wl.sq[p], sq, 0);
+          g.a2[rr][p] = __builtin_amdgcn_raw_buffer_load_b16(mb.absmax2, wl.sa2[p], sa, 0);
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint32_t blk = (row * static_cast<uint32_t>(K) + wl.c0[p]) >> log2bs;
@@ -1190,7 +1222,7 @@ __device__ __forceinline__ int next_group_dyn(RowCursor& c, int& r_end, uint32_t
   return next_group<R>(c, r_end, rbeg, count, m_out, rl_out);
 }
 
-template <int B, int R, int P, int WPE, bool DYN, int FMT = kFmtDouble>
+template <int B, int R, int P, int WPE, bool DYN, int FMT = kFmtDouble, bool REG = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemv_wave_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
     int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2, unsigned* sched, int C) {
@@ -1275,8 +1307,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     }
     // the block this lane finishes: first load's (even) or second load's (odd)
     const int c0 = kWaveCols * p + (odd ? 2048 : 0) + 32 * (lane & ~1);
-    own_in[p] = c0 < K;
+    own_in[p] = REG || c0 < K;  // REG: K is a multiple of 4096
     wl.c0[p] = static_cast<uint32_t>(c0);
+    const uint32_t lb = static_cast<uint32_t>(c0) >> log2bs;  // its block inside the row
+    wl.sq[p] = lb * (FMT == kFmtAbsmax32 ? 4u : FMT == kFmtInt4 ? 2u : 1u);
+    wl.sa2[p] = FMT == kFmtInt4 ? lb * 2u : (lb >> log2s2) * 2u;
   }
 
   auto advance = [&](int* m_out, int* rl_out) {
@@ -1297,7 +1332,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   LoadBufs lb0 = load_bufs<FMT>(d0, K, log2bs, log2s2);
   OutBufs ob0 = out_bufs<B>(d0);
   WaveGroup<R, P, FMT> g0, g1, g2;
-  load_wave_group<R, P, FMT>(g0, lb0, rl0, len0, wl, K, log2bs, log2s2);
+  load_wave_group<R, P, FMT, REG>(g0, lb0, rl0, len0, wl, K, log2bs, log2s2);
   u32x4 xr[B][P][8];
   load_wave_x<B, P>(xr, x_buf<B>(d0, K), wl, K);
   float xs[B][P];  // INT4: the lane's activation sums per pass
@@ -1311,7 +1346,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     ob1 = out_bufs<B>(d1);
     mL = m1;
   }
-  load_wave_group<R, P, FMT>(g1, lbL, rl1, len1, wl, K, log2bs, log2s2);
+  load_wave_group<R, P, FMT, REG>(g1, lbL, rl1, len1, wl, K, log2bs, log2s2);
 
   if (FMT == kFmtDouble && tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
   const uint32_t copy_off = build_decode_table<FMT>(s_pairs, tid, blockDim.x, lane);
@@ -1351,7 +1386,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
       ob2 = out_bufs<B>(d2);
       mL = m2;
     }
-    load_wave_group<R, P, FMT>(fut, lbL, rl2, len2, wl, K, log2bs, log2s2);
+    load_wave_group<R, P, FMT, REG>(fut, lbL, rl2, len2, wl, K, log2bs, log2s2);
     __builtin_amdgcn_sched_barrier(0);
 
     // (a chunked range may end inside a round: empty groups skip the work)
@@ -1891,17 +1926,32 @@ nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, 
   int64_t grid = want < cus ? (want > 0 ? want : 1) : cus;
   if (WPE == 4 && want >= 4 * cus) grid = want < 2 * cus ? want : 2 * cus;
   const int64_t rows_per_wave = (static_cast<int64_t>(total_rows) + grid * 8 - 1) / (grid * 8);
-  if (WPE == 4 && sched != nullptr && rows_per_wave >= 64) {
-    int C = 4;
+  const bool dyn = WPE == 4 && sched != nullptr && rows_per_wave >= 64;
+  int C = 0;
+  if (dyn) {
+    C = 4;
     while (C < 32 && C * 2 * 16 <= rows_per_wave) C *= 2;
-    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, true, FMT>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2, sched,
-                       C);
-  } else {
-    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, false, FMT>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2,
-                       nullptr, 0);
   }
+  // regular shapes (see load_wave_group): whole 4096-column passes, whole
+  // blocks per row, and blocks per row and s2 dividing one into the other
+  const int64_t bs = int64_t(1) << lbs, s2 = int64_t(1) << ls2;
+  const int64_t nb = K / bs;  // blocks per row when K % bs == 0
+  const bool reg = K % kWaveCols == 0 && K % bs == 0 &&
+                   (FMT != kFmtDouble || nb % s2 == 0 || s2 % nb == 0);
+  const dim3 g(static_cast<uint32_t>(grid)), blk(512);
+  unsigned* sc = dyn ? sched : nullptr;
+  if (reg && dyn)
+    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, true, FMT, true>), g, blk, 0, st, descs,
+                       single, count, total_rows, K, lbs, ls2, code2, sc, C);
+  else if (reg)
+    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, false, FMT, true>), g, blk, 0, st, descs,
+                       single, count, total_rows, K, lbs, ls2, code2, sc, C);
+  else if (dyn)
+    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, true, FMT, false>), g, blk, 0, st, descs,
+                       single, count, total_rows, K, lbs, ls2, code2, sc, C);
+  else
+    hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, false, FMT, false>), g, blk, 0, st,
+                       descs, single, count, total_rows, K, lbs, ls2, code2, sc, C);
   return launch_status();
 }
 

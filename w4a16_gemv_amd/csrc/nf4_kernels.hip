@@ -1101,8 +1101,6 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
       for (int b = 0; b < B; ++b) xx[b] = s_x[((b * P + p) * 8 + hj) * 64 + lane];
     }
   };
-#pragma unroll
-  for (int v = 0; v < R * B; ++v) val[v] = 0.0f;
   float part[B], half0[B];
   fetch(0, t[0], xv[0]);
 #pragma unroll
@@ -1110,10 +1108,6 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
     if (u + 1 < U) fetch(u + 1, t[(u + 1) & 1], xv[(u + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
     const int rr = u / (P * 8), p = (u / 8) % P, hj = u % 8;
-    if ((hj & 3) == 0) {
-#pragma unroll
-      for (int b = 0; b < B; ++b) part[b] = 0.0f;
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint2 ti = t[u & 1][i];
@@ -1123,7 +1117,10 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
         // element 0 whatever the index
         const uint32_t xw = XL ? xv[u & 1][b][i] : xr[b][p][hj][i];
         const bf16x2 xp = __builtin_bit_cast(bf16x2, xw);
-        part[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.x), xp, part[b],
+        // the first product of each half starts from an immediate zero (no
+        // separate reset of the accumulator)
+        const float acc = (hj & 3) == 0 && i == 0 ? 0.0f : part[b];
+        part[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.x), xp, acc,
                                                   false);
         if constexpr (FMT != kFmtInt4)
           part[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.y), xp,
@@ -1151,7 +1148,8 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           const float zt = z * xs[b][p];
-          val[rr * B + b] += own_in[p] ? sc * (blk[b] - zt) : 0.0f;
+          const float c = own_in[p] ? sc * (blk[b] - zt) : 0.0f;
+          val[rr * B + b] = p == 0 ? c : val[rr * B + b] + c;  // the first pass assigns
         }
       } else {
         float a;
@@ -1162,7 +1160,10 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
           a = prod + offset;
         }
 #pragma unroll
-        for (int b = 0; b < B; ++b) val[rr * B + b] += own_in[p] ? a * blk[b] : 0.0f;
+        for (int b = 0; b < B; ++b) {
+          const float c = own_in[p] ? a * blk[b] : 0.0f;
+          val[rr * B + b] = p == 0 ? c : val[rr * B + b] + c;  // the first pass assigns
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -153,12 +153,12 @@ def build_workload(dev, fmt: str = "double"):
 
 
 DOMINANT_K = 4096
-DOMINANT_KERNEL = ("gemv_wave_kernel<1, 2, 1, 4, true, 0> (nf4_gemv_grouped, K=4096, "
+DOMINANT_KERNEL = ("gemv_wave_kernel<1, 2, 1, 4, true, 0, true> (nf4_gemv_grouped, K=4096, "
                    "192 matrices)")
 DOMINANT_KERNEL_FMT = {
-    "absmax32": "gemv_wave_kernel<1, 2, 1, 4, true, 1> (nf4_gemv_grouped_absmax32, K=4096, "
+    "absmax32": "gemv_wave_kernel<1, 2, 1, 4, true, 1, true> (nf4_gemv_grouped_absmax32, K=4096, "
                 "192 matrices)",
-    "int4": "gemv_wave_kernel<1, 2, 1, 4, true, 2> (int4_gemv_grouped, K=4096, 192 matrices)",
+    "int4": "gemv_wave_kernel<1, 2, 1, 4, true, 2, true> (int4_gemv_grouped, K=4096, 192 matrices)",
 }
 KERNEL_SOURCE = os.path.join(ROOT, "w4a16_gemv_amd", "csrc", "nf4_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_wave_k4096_sweep_traffic.txt")

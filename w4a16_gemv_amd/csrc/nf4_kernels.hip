@@ -1486,8 +1486,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 // workgroup.  The workgroup walks its range one matrix at a time: it stages
 // that matrix's activations (a barrier before and after), then its waves
 // claim groups of R rows from an LDS counter until the matrix's part of the
-// range is used up.  Each wave computes one group while the loads of its next
-// group are in flight (two register buffers, whole rounds of two steps).
+// range is used up.  Each wave keeps NBUF register buffers of row groups:
+// with three, the loads of the group after next are issued before the current
+// group is computed; with two (where registers are short), the buffer just
+// computed takes the group after next.  The loops run whole rounds of NBUF
+// steps.
 // ---------------------------------------------------------------------------
 constexpr int kXlThreads = 1024;
 

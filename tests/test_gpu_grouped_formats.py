@@ -58,7 +58,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("fmt", ["absmax32", "int4"])
-@pytest.mark.parametrize("batch", [1, 2, 5])
+@pytest.mark.parametrize("batch", [1, 2, 4, 5, 8])
 @pytest.mark.parametrize("K,shapes,bs", CASES)
 def test_grouped_formats_match_oracle(fmt, batch, K, shapes, bs):
     qs, items = [], []

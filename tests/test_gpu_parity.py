@@ -281,7 +281,7 @@ def _group_case(shapes_seeds, K, batch, x_seed):
     return qs, items
 
 
-@pytest.mark.parametrize("batch", [1, 2, 3, 8])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("K,shapes", [
     (4096, [(4096, 600), (4096, 601), (11008, 602), (256, 603), (1, 604), (37, 605)]),
     (1536, [(1536, 610), (256, 611), (256, 612), (8960, 613)]),

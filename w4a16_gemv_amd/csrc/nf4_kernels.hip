@@ -1470,8 +1470,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 }
 
 // ---------------------------------------------------------------------------
-// The shared-activation GEMV (grouped launches, batch 1-2, 4096 < K <= 16384,
-// K % 64 == 0, blocksize >= 64).
+// The shared-activation GEMV (grouped launches, K % 64 == 0, blocksize >= 64:
+// batch 1-2 with 4096 < K <= 16384, and batch 3-8 with K <= 4096).
 //
 // With more than one pass the wave kernel keeps 32 B P VGPRs of activations
 // per wave and fits only two waves per SIMD: too few independent instruction
@@ -1480,7 +1480,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 // matrix it works on in LDS, in the lane order in which the wave kernel holds
 // them in registers, so each ds_read_b128 of the 64 lanes reads 1 KiB of
 // consecutive banks.  The lane layout, decode and per-row arithmetic are the
-// wave kernel's (wave_rows with XL).
+// wave kernel's (wave_rows with XL).  At batch 3-8 the activations of every
+// batch row are in LDS (8 KiB each) and a wave computes one row per group.
 //
 // The concatenated rows are split evenly into one contiguous range per
 // workgroup.  The workgroup walks its range one matrix at a time: it stages
@@ -1498,7 +1499,7 @@ template <int B, int R, int P, int NBUF, int FMT>
 __global__ __launch_bounds__(kXlThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_xlds_kernel(
     const nf4_gemv_desc* __restrict__ descs, int count, int total_rows, int K, int log2bs,
     int log2s2, const uint16_t* __restrict__ code2) {
-  static_assert(R * B <= 4, "one pair or quad reduction per group");
+  static_assert(R * B <= 8, "at most two quad reductions per group");
   static_assert(NBUF == 2 || NBUF == 3, "two or three register buffers");
   __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
   __shared__ float s_code2[256];
@@ -1602,24 +1603,32 @@ __global__ __launch_bounds__(kXlThreads) __attribute__((amdgpu_waves_per_eu(4, 4
     // the group's rows and y: reduce the R B row values over the lanes and
     // store them
     auto finish = [&](const float (&val)[R * B], int rl, int len) {
-      float tot;
-      int v;
-      bool first;
-      if constexpr (R * B <= 2) {
-        tot = wave_sum_pair(val[0], R * B > 1 ? val[R * B - 1] : 0.0f);
-        v = lane >> 5;
-        first = (lane & 31) == 0;
-      } else {
-        tot = wave_sum_quad(val[0], val[1], val[2], R * B > 3 ? val[3] : 0.0f);
-        const int row16 = lane >> 4;
-        v = ((row16 & 1) << 1) | (row16 >> 1);
-        first = (lane & 15) == 0;
+      // one pair or quad reduction per four values
+      constexpr int NQ = R * B <= 4 ? 1 : 2;
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        float tot;
+        int v;
+        bool first;
+        if constexpr (R * B <= 2) {
+          tot = wave_sum_pair(val[0], R * B > 1 ? val[R * B - 1] : 0.0f);
+          v = lane >> 5;
+          first = (lane & 31) == 0;
+        } else {
+          const int o = 4 * qd;
+          tot = wave_sum_quad(val[o], o + 1 < R * B ? val[o + 1] : 0.0f,
+                              o + 2 < R * B ? val[o + 2] : 0.0f,
+                              o + 3 < R * B ? val[o + 3] : 0.0f);
+          const int row16 = lane >> 4;
+          v = o + (((row16 & 1) << 1) | (row16 >> 1));
+          first = (lane & 15) == 0;
+        }
+        const int rr = v / B, b = v % B;
+        const bool store = first && v < R * B && rr < len;
+        const uint32_t off = static_cast<uint32_t>((b * ob.N + rl + rr) * 2);
+        __builtin_amdgcn_raw_buffer_store_b16(to_half_bits<NF4_BF16>(tot), ob.y,
+                                              store ? off : kOutOfRange, 0, 0);
       }
-      const int rr = v / B, b = v % B;
-      const bool store = first && v < R * B && rr < len;
-      const uint32_t off = static_cast<uint32_t>((b * ob.N + rl + rr) * 2);
-      __builtin_amdgcn_raw_buffer_store_b16(to_half_bits<NF4_BF16>(tot), ob.y,
-                                            store ? off : kOutOfRange, 0, 0);
     };
     auto compute = [&](const WaveGroup<R, P, FMT>& g, int rl, int len) {
       if (len > 0) {
@@ -2005,6 +2014,13 @@ template <int B, int FMT>
 nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                          unsigned* sched, hipStream_t st) {
+  // grouped launches at batch 3-8 with one pass: the shared-activation kernel
+  // (four waves per SIMD, no barrier per row group; 16% faster than the team
+  // kernel at batch 4, 3% at batch 8)
+  if constexpr (B >= 3) {
+    if (descs != nullptr && K % 64 == 0 && K <= kWaveCols && lbs >= 6)
+      return xlds_launch<B, 1, 1, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+  }
   // Grouped launches (descs != NULL) at batch 1-2 take the wave kernel.  A
   // single matrix takes it only at batch 1, one pass and up to 2^24 weights:
   // there every wave has one or two rows and the wave kernel's lighter

@@ -368,13 +368,17 @@ def test_gemv_grouped_skips_bad_descriptors():
 @pytest.mark.parametrize("K", [8192, 11008, 16384])
 def test_gemv_grouped_many_small_matrices(K, batch):
     """More than one pass, many matrices of 1-9 rows with their own
-    activations: a workgroup's row range crosses many matrices, so the
-    activations are staged again for each one; a matrix with a bad N in the
-    middle is skipped (its y keeps its contents) and the others are computed."""
+    activations, and every tenth of 700-900 rows so that the launch has rows
+    enough for the shared-activation kernel: a workgroup's row range crosses
+    many matrices, so the activations are staged again for each one; a matrix
+    with a bad N in the middle is skipped (its y keeps its contents) and the
+    others are computed."""
     import numpy as np
     rng = np.random.default_rng(K + batch)
-    shapes = [(int(n), 900 + i) for i, n in enumerate(rng.integers(1, 10, size=120))]
-    shapes[40] = (5, 940)
+    sizes = rng.integers(1, 10, size=120)
+    sizes[::10] = rng.integers(700, 900, size=12)
+    shapes = [(int(n), 900 + i) for i, n in enumerate(sizes)]
+    shapes[41] = (5, 940)
     qs, items = [], []
     for N, seed in shapes:
         q = oracle.quantize(synth.weights(seed, N * K))
@@ -386,17 +390,18 @@ def test_gemv_grouped_many_small_matrices(K, batch):
         qs.append((q, N, xb, base))
     grp = nf4.GemvGroup(items, K)
     tab = grp.table.cpu().numpy().copy().view(np.int64).reshape(len(items), 8)
-    tab[40, 5] = 4                                    # N of item 40 no longer matches
+    tab[41, 5] = 4                                    # N of item 41 no longer matches
     grp.table.copy_(torch.from_numpy(tab.view(np.uint8).reshape(-1)))
-    items[40][3].fill_(3.0)
+    items[41][3].fill_(3.0)
     print(f"[gemv_grouped_many] K={K} B={batch} matrices={len(shapes)} rows={grp.total_rows}",
           flush=True)
     grp.launch()
     torch.cuda.synchronize()
-    assert torch.all(items[40][3] == 3.0), "the bad matrix was written"
+    assert grp.total_rows >= 2 * 16 * 256, "too few rows for the shared-activation kernel"
+    assert torch.all(items[41][3] == 3.0), "the bad matrix was written"
     for i, ((q, N, xb, base), (_, _, _, yv)) in enumerate(zip(qs, items)):
         assert G.guards_intact(base, batch * N), f"write outside y of item {i}"
-        if i == 40:
+        if i == 41:
             continue
         y = G.bf16_to_f64(G.bits16(yv)).reshape(batch, N)
         yr, S = oracle.gemv(q, N, K, xb)

@@ -1968,6 +1968,15 @@ nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, 
   return launch_status();
 }
 
+// Whether a grouped launch has rows enough for the shared-activation kernel:
+// at least two per wave of a full grid.  With fewer its waves have nothing to
+// pipeline and the team kernel, which splits each row over several waves, is
+// faster (one 4096 x 11008 matrix: 20.8 us against 12.8; two: 21.9 against
+// 23.0; four: 28.2 against 45.1).
+inline bool xlds_rows_ok(int total_rows) {
+  return static_cast<int64_t>(total_rows) >= 2 * (kXlThreads / 64) * device_cus();
+}
+
 // The shared-activation kernel for (B, P): one 1024-thread workgroup per CU
 // at most, each with at least 64 rows.
 template <int B, int R, int P, int NBUF, int FMT>
@@ -1996,8 +2005,9 @@ nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   if constexpr (B == 2) {
     if (P == 1) return wave_launch<2, 1, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
   }
-  if (descs == nullptr) return NF4_EUNSUPPORTED;
-  // more than one pass: the activations go to LDS (gemv_xlds_kernel)
+  // more than one pass: the activations go to LDS (gemv_xlds_kernel), for
+  // launches that give every wave two rows or more (see xlds_rows_ok)
+  if (descs == nullptr || !xlds_rows_ok(total_rows)) return NF4_EUNSUPPORTED;
   if constexpr (B == 1) {
     if (P == 2) return xlds_launch<1, 1, 2, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
     if (P == 3) return xlds_launch<1, 1, 3, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
@@ -2018,7 +2028,8 @@ nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   // (four waves per SIMD, no barrier per row group; 16% faster than the team
   // kernel at batch 4, 3% at batch 8)
   if constexpr (B >= 3) {
-    if (descs != nullptr && K % 64 == 0 && K <= kWaveCols && lbs >= 6)
+    if (descs != nullptr && K % 64 == 0 && K <= kWaveCols && lbs >= 6 &&
+        xlds_rows_ok(total_rows))
       return xlds_launch<B, 1, 1, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
   }
   // Grouped launches (descs != NULL) at batch 1-2 take the wave kernel.  A

@@ -48,6 +48,7 @@ CASES = [
     # K, [(N, seed)], block (group) size
     (4096, [(4096, 900), (256, 901), (1000, 902), (1, 903)], 64),
     (4096, [(512, 904), (77, 905)], 128),
+    (4096, [(8192, 906), (256, 907)], 64),         # rows enough for the shared-activation kernel
     (1536, [(1536, 910), (256, 911), (8960, 912)], 64),
     (11008, [(300, 920), (5, 921)], 64),          # three 4096-column passes
     (8192, [(200, 930)], 256),                     # two passes

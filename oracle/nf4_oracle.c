@@ -38,9 +38,8 @@
  *    f32(NF4[idx] * absmax_real); output = round-to-nearest-even to bf16/fp16.
  *  - quantizer: level-1 codes are chosen against the true fp32 block absmax;
  *    offset = f32(fp64 sum of block absmax / number of blocks), the sum taken
- *    over chunks of 1024 consecutive blocks, each chunk and then the chunk
- *    sums in index order (the pages give no order; this one is fixed so that
- *    an independent implementation can reach the same fp64 value);
+ *    in block-index order starting from +0 (the pages give no order; this is
+ *    the plainest one, and it is fixed so that the value is reproducible);
  *    level 2 centres each block absmax by offset, takes the group max of |.|
  *    rounded to fp16 as absmax2, and picks the nearest code2 entry of
  *    centred/absmax2 (fp32).  Ties go to the smaller index.  A block whose
@@ -230,16 +229,11 @@ int oracle_quantize(const float* w, int64_t n, int32_t bs, int32_t s2, const uin
         absmax[b] = m;
     }
 
-    /* offset: mean of the block absmax values.  fp64 sums over chunks of
-     * 1024 consecutive blocks (each chunk in index order), then the chunk
-     * sums in index order; the mean is rounded once to fp32. */
+    /* offset: mean of the block absmax values ([report] §1.2: one global
+     * fp32 offset).  One fp64 sum in block-index order, divided by the block
+     * count, rounded once to fp32. */
     double sum = 0.0;
-    for (int64_t c0 = 0; c0 < nb; c0 += 1024) {
-        double chunk = 0.0;
-        const int64_t c1 = c0 + 1024 < nb ? c0 + 1024 : nb;
-        for (int64_t b = c0; b < c1; ++b) chunk += (double)absmax[b];
-        sum += chunk;
-    }
+    for (int64_t b = 0; b < nb; ++b) sum += (double)absmax[b];
     const float off = (float)(sum / (double)nb);
     *offset = off;
 

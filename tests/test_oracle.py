@@ -412,6 +412,41 @@ def test_quantizer_zero_tensor():
     assert q.offset == 0.0 and np.all(q.absmax2 == 0)
 
 
+def _blocks_with_absmax(a, bs=64):
+    """Weights whose block b holds the single non-zero a[b] (so its absmax is
+    exactly a[b])."""
+    w = np.zeros((len(a), bs), np.float32)
+    w[:, 0] = np.asarray(a, np.float32)
+    return w.reshape(-1)
+
+
+def test_quantizer_offset_is_the_index_order_fp64_mean():
+    """offset = fp32(fp64 sum of the block absmax values in block order / nb).
+    Hand-derived cases (2048 blocks, so the division by nb is exact) where the
+    summation order shows in the fp32 result; the exact mean, a reverse-order
+    sum and per-1024-block partial sums all give the other answer in case 1.
+
+    Case 1: blocks 0, 1 = 1, 2^-24; blocks 1024-1026 = 2^-54; the rest 0.  In
+    block order 1 + 2^-24 is exact and each 2^-54 is a quarter of the fp64
+    ulp of 1, so it is lost: the sum is 1 + 2^-24 and the mean
+    2^-11 + 2^-35 is the midpoint of two fp32 neighbours, which rounds to
+    even, 2^-11.  Summed exactly (or the three 2^-54 first) the mean is
+    above the midpoint and rounds up to 2^-11 + 2^-34.
+
+    Case 2: blocks 0-2 = 2^-54 first, then 1 and 2^-24.  3 * 2^-54 is exact,
+    adding 1 rounds it up to one fp64 ulp (2^-52), so the sum is
+    1 + 2^-24 + 2^-52 and the mean rounds up to 2^-11 + 2^-34."""
+    a = np.zeros(2048)
+    a[0], a[1], a[1024:1027] = 1.0, 2.0 ** -24, 2.0 ** -54
+    q = oracle.quantize(_blocks_with_absmax(a))
+    assert np.float32(q.offset) == np.float32(2.0 ** -11)
+    b = np.zeros(2048)
+    b[0:3], b[3], b[4] = 2.0 ** -54, 1.0, 2.0 ** -24
+    q = oracle.quantize(_blocks_with_absmax(b))
+    assert np.float32(q.offset) == np.float32(2.0 ** -11 + 2.0 ** -34)
+    assert np.float32(2.0 ** -11 + 2.0 ** -34) != np.float32(2.0 ** -11)
+
+
 # ----------------------------------------------------------------------------
 # GEMV reference
 # ----------------------------------------------------------------------------
@@ -711,6 +746,25 @@ def test_int4_quantizer_constant_and_zero_groups():
     v = oracle.int4_dequant_f32(q).reshape(3, 128)
     assert np.all(v[0] == 0.0)
     assert np.all(np.abs(v[1:] - w.reshape(3, 128)[1:]) <= 0.5)
+
+
+def test_int4_quantizer_halves_round_away_from_zero():
+    """Exact halves.  One group of 16 with min -6.5 and max 8.5: the span is
+    15, so s = 1 exactly and -min / s = 6.5 rounds away from zero to z = 7
+    (round-half-even would give 6).  The formula rounds w / s first and then
+    adds z: w = -0.5 gives round(-0.5) + 7 = 6, where rounding w / s + z = 6.5
+    as one value would give 7; w = 0.5 gives 8, w = 2.5 gives 10 (half-even:
+    8 with z = 6), w = 1.5 gives 9, -6.5 gives 0 and 8.5 gives 16, clamped to
+    15."""
+    w = np.zeros(16, np.float32)
+    w[:8] = [-6.5, 8.5, -0.5, 0.5, 2.5, 1.5, -2.5, 0.0]
+    q = oracle.int4_quantize(w, 16)
+    assert q.scales.view(F16)[0] == 1.0
+    assert q.zeros.view(F16)[0] == 7.0
+    codes = np.empty(16, np.int64)
+    codes[0::2] = q.packed & 15
+    codes[1::2] = q.packed >> 4
+    assert codes[:8].tolist() == [0, 15, 6, 8, 10, 9, 4, 7]
 
 
 def test_int4_gemv_one_hot_and_magnitudes():

@@ -332,10 +332,11 @@ size_t nf4_quantize_workspace_size(int64_t n, int32_t blocksize);
  * absmax values are centred by offset (their mean), grouped by s2_blocksize,
  * absmax2 = fp16 of the group's largest |centred value|, absmax_q = index of
  * the nearest code2 entry to centred / absmax2.  Ties go to the smaller
- * index; an all-zero block gets code 7 (exact zero).  The mean is an fp64 sum
- * over chunks of 1024 consecutive blocks, each chunk and then the chunk sums
- * in index order, rounded once to fp32: the result does not depend on the
- * launch and is bit-identical on every run.
+ * index; an all-zero block gets code 7 (exact zero).  The mean is one fp64
+ * sum of the block absmax values in block-index order, divided by the block
+ * count and rounded once to fp32: the result does not depend on the launch
+ * and is bit-identical on every run.  That sum is one serial chain of adds
+ * (about 2 ms per 2^18 blocks); the encoder is not meant for a timed path.
  *
  *  w             : device fp32[n] (flattened weights).
  *  code2         : device fp16 bits [256] (e.g. nf4_code2_linear uploaded).

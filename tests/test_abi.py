@@ -103,7 +103,7 @@ def test_code2_linear_table_matches_oracle(lib):
 def test_quantize_workspace_size(lib):
     assert lib.nf4_quantize_workspace_size(0, 64) == 0
     ws = lib.nf4_quantize_workspace_size(1 << 20, 64)
-    assert ws >= (1 << 14) * 4 + 16 * 8
+    assert ws >= (1 << 14) * 4          # one fp32 absmax per block
 
 
 @pytest.mark.parametrize("kw", [dict(n=-1), dict(bs=3), dict(s2=0), dict(w=None),

@@ -1,8 +1,8 @@
 """GPU quantizer parity: nf4_quantize (through the C ABI) against the oracle
 quantizer on the same fp32 weights.  Every output -- packed codes, absmax_q,
 absmax2 and the offset -- must be bit-identical: each decision is an exact or
-correctly rounded fp32 operation on both sides and the offset's fp64 sum
-follows the same fixed order."""
+correctly rounded fp32 operation on both sides, and the offset is one fp64
+sum in block-index order on both."""
 import numpy as np
 import pytest
 import torch
@@ -40,6 +40,30 @@ def test_quantize_matches_oracle(n, bs, s2, outliers):
     assert np.array_equal(G.bits16(got.absmax2), ref.absmax2)
     assert np.array_equal(got.absmax_q.cpu().numpy(), ref.absmax_q)
     assert np.array_equal(got.packed.cpu().numpy(), ref.packed)
+
+
+@pytest.mark.parametrize("case", ["big_first", "tiny_first"])
+def test_quantize_offset_sums_in_block_order(case):
+    """Block absmax values for which the order of the fp64 sum shows in the
+    fp32 offset (the cases of the oracle pin
+    test_quantizer_offset_is_the_index_order_fp64_mean): the device must
+    reach the same bits, 2^-11 and 2^-11 + 2^-34."""
+    a = np.zeros(2048, np.float32)
+    if case == "big_first":
+        a[0], a[1], a[1024:1027] = 1.0, 2.0 ** -24, 2.0 ** -54
+        expect = np.float32(2.0 ** -11)
+    else:
+        a[0:3], a[3], a[4] = 2.0 ** -54, 1.0, 2.0 ** -24
+        expect = np.float32(2.0 ** -11 + 2.0 ** -34)
+    w = np.zeros((2048, 64), np.float32)
+    w[:, 0] = a
+    w = w.reshape(-1)
+    ref = oracle.quantize(w)
+    got = quantize_on_gpu(w, 64, 256)
+    assert np.float32(ref.offset) == expect
+    assert np.float32(got.offset).view(np.uint32) == expect.view(np.uint32)
+    assert np.array_equal(G.bits16(got.absmax2), ref.absmax2)
+    assert np.array_equal(got.absmax_q.cpu().numpy(), ref.absmax_q)
 
 
 def test_quantize_zero_blocks_and_exact_grid_points():

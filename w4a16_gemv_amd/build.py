@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnf4.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # the scheduling claims are single-lane atomics whose result is read much
@@ -41,14 +41,36 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", LIB + ".tmp", *SRCS]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build libnf4.so")
-    os.replace(LIB + ".tmp", LIB)
+    """Compile each source to an object in parallel (one hipcc per file), then
+    link the shared library; the result replaces LIB atomically."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    tmp = tempfile.mkdtemp(prefix="nf4_build_")
+    try:
+        objs = [os.path.join(tmp, os.path.basename(src) + ".o") for src in SRCS]
+        cmds = [[hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-c", "-o", obj, src]
+                for src, obj in zip(SRCS, objs)]
+        if verbose:
+            for cmd in cmds:
+                print(" ".join(cmd), flush=True)
+        with ThreadPoolExecutor(len(cmds)) as pool:
+            results = list(pool.map(lambda c: subprocess.run(c, capture_output=True, text=True),
+                                    cmds))
+        for res in results:
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError("hipcc failed to build libnf4.so")
+        link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+        if verbose:
+            print(" ".join(link), flush=True)
+        res = subprocess.run(link, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError("hipcc failed to link libnf4.so")
+        os.replace(LIB + ".tmp", LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
     return LIB
 
 

@@ -11,9 +11,9 @@
 // Readings fixed here (the pages leave them open):
 //  - level-1 codes are chosen against the true fp32 block absmax; a zero block
 //    gets code 7 (the exact zero); ties go to the smaller code index;
-//  - offset = mean of the block absmax values: fp64 sums over chunks of 1024
-//    consecutive blocks in index order, then the chunk sums in index order,
-//    divided by the number of blocks and rounded once to fp32;
+//  - offset = mean of the block absmax values: one fp64 sum in block-index
+//    order starting from +0, divided by the number of blocks and rounded once
+//    to fp32;
 //  - level 2 centres each block absmax by offset, absmax2 = fp16 (nearest) of
 //    the group's largest |centred|, and absmax_q = the nearest code2 entry to
 //    centred / absmax2 (0 when absmax2 is 0), all in fp32;
@@ -33,7 +33,7 @@ namespace {
 using namespace nf4dev;
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 1024;  // blocks per partial sum of the offset
+constexpr int kSumTile = 4096;  // block absmax values per LDS tile of the offset sum
 
 uint32_t grid_for(int64_t items) {
   const int64_t g = (items + kThreads - 1) / kThreads;
@@ -56,26 +56,45 @@ __global__ __launch_bounds__(kThreads) void block_absmax_kernel(const float* __r
   }
 }
 
-__global__ __launch_bounds__(kThreads) void chunk_sum_kernel(const float* __restrict__ absmax,
-                                                              int64_t nb,
-                                                              double* __restrict__ sums) {
-  const int64_t nc = (nb + kChunk - 1) / kChunk;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; c < nc; c += stride) {
-    const int64_t b1 = (c + 1) * kChunk < nb ? (c + 1) * kChunk : nb;
-    double s = 0.0;
-    for (int64_t b = c * kChunk; b < b1; ++b) s += static_cast<double>(absmax[b]);
-    sums[c] = s;
+// offset = fp32(fp64 sum of absmax[0..nb) in index order / nb).  The sum is
+// one dependent chain of fp64 adds, so one thread does it; the workgroup
+// streams the values into two LDS tiles so that the next tile's loads are in
+// flight while thread 0 adds the current one.
+__global__ __launch_bounds__(kThreads) void offset_kernel(const float* __restrict__ absmax,
+                                                          int64_t nb, float* __restrict__ offset) {
+  __shared__ float s_tile[2][kSumTile];
+  const int t = threadIdx.x;
+  const int64_t ntiles = (nb + kSumTile - 1) / kSumTile;
+  constexpr int kPer = kSumTile / kThreads;  // values each thread stages per tile
+  float v[kPer];
+  auto fetch = [&](int64_t tile) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t b = tile * kSumTile + i * kThreads + t;
+      v[i] = b < nb ? absmax[b] : 0.0f;
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) s_tile[buf][i * kThreads + t] = v[i];
+  };
+  fetch(0);
+  put(0);
+  __syncthreads();
+  double sum = 0.0;
+  for (int64_t c = 0; c < ntiles; ++c) {
+    const bool more = c + 1 < ntiles;
+    if (more) fetch(c + 1);  // in flight during the adds below
+    if (t == 0) {
+      const float* tile = s_tile[c & 1];
+      const int64_t left = nb - c * kSumTile;
+      const int cnt = left < kSumTile ? static_cast<int>(left) : kSumTile;
+      for (int i = 0; i < cnt; ++i) sum += static_cast<double>(tile[i]);
+    }
+    if (more) put((c + 1) & 1);  // the other tile: thread 0 read it before the last barrier
+    __syncthreads();
   }
-}
-
-__global__ void offset_kernel(const double* __restrict__ sums, int64_t nb,
-                              float* __restrict__ offset) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  const int64_t nc = (nb + kChunk - 1) / kChunk;
-  double s = 0.0;
-  for (int64_t c = 0; c < nc; ++c) s += sums[c];
-  offset[0] = static_cast<float>(s / static_cast<double>(nb));
+  if (t == 0) offset[0] = static_cast<float>(sum / static_cast<double>(nb));
 }
 
 // absmax2[g] = fp16(max over the group's blocks of |absmax - offset|)
@@ -234,8 +253,7 @@ void nf4_code2_linear(uint16_t out[256]) {
 size_t nf4_quantize_workspace_size(int64_t n, int32_t blocksize) {
   if (n <= 0 || blocksize < 1) return 0;
   const int64_t nb = (n + blocksize - 1) / blocksize;
-  const int64_t nc = (nb + kChunk - 1) / kChunk;
-  return align256(static_cast<size_t>(nb) * sizeof(float)) + static_cast<size_t>(nc) * sizeof(double);
+  return align256(static_cast<size_t>(nb) * sizeof(float));
 }
 
 nf4_status nf4_quantize(const float* w, int64_t n, int32_t blocksize, int32_t s2_blocksize,
@@ -252,16 +270,11 @@ nf4_status nf4_quantize(const float* w, int64_t n, int32_t blocksize, int32_t s2
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return NF4_EINVAL;
   const int64_t nb = (n + blocksize - 1) / blocksize;
   const int64_t ng = (nb + s2_blocksize - 1) / s2_blocksize;
-  const int64_t nc = (nb + kChunk - 1) / kChunk;
   float* absmax = static_cast<float*>(workspace);
-  double* sums = reinterpret_cast<double*>(static_cast<char*>(workspace) +
-                                           align256(static_cast<size_t>(nb) * sizeof(float)));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(block_absmax_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, st, w, n, lbs,
                      absmax);
-  hipLaunchKernelGGL(chunk_sum_kernel, dim3(grid_for(nc)), dim3(kThreads), 0, st, absmax, nb,
-                     sums);
-  hipLaunchKernelGGL(offset_kernel, dim3(1), dim3(64), 0, st, sums, nb, offset);
+  hipLaunchKernelGGL(offset_kernel, dim3(1), dim3(kThreads), 0, st, absmax, nb, offset);
   hipLaunchKernelGGL(group_scale_kernel, dim3(grid_for(ng)), dim3(kThreads), 0, st, absmax, nb,
                      ls2, offset, absmax2);
   hipLaunchKernelGGL(block_code_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, st, absmax, nb,

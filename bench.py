@@ -131,16 +131,20 @@ def build_workload(dev, fmt: str = "double"):
             ws = torch.empty(need, dtype=torch.uint8, device=dev)
         return nf4.nf4_quantize(w, 64, 256, code2=code2, workspace=ws)
 
-    xs = {K: synth.activations_device(synth.SWEEP_X_SEED, 1, K, dev) for K in (4096, 11008)}
+    # each layer reads its own activations: xs[(layer, slot)], see synth.SWEEP_X_SLOT
+    xs = {}
     layers = []
     for L in range(synth.SWEEP_LAYERS):
         mats = []
         for g in synth.sweep_layer(L):
+            slot = synth.SWEEP_X_SLOT[g.name.split("_", 1)[1]]
+            if (L, slot) not in xs:
+                xs[(L, slot)] = synth.activations_device(synth.sweep_x_seed(L, slot), 1, g.K, dev)
             w = synth.weights_device(g.seed, g.N * g.K, dev)
             t = encode(w)
             del w
             y = torch.empty(1, g.N, dtype=torch.bfloat16, device=dev)
-            mats.append((g, t, y))
+            mats.append((g, t, y, xs[(L, slot)]))
         layers.append(mats)
     big = synth.DEQUANT_BIG
     wb = synth.weights_device(big.seed, big.n, dev)
@@ -190,18 +194,18 @@ def committed_traffic():
 def make_step(wl, schedule):
     """Returns (gemv_fns, dequant_fn, gemv_launches)."""
     import w4a16_gemv_amd as nf4
-    xs = wl["xs"]
     groups = []
     if schedule == "stream":
         for K in (4096, 11008):
-            items = [(t, g.N, xs[K], y) for mats in wl["layers"] for (g, t, y) in mats if g.K == K]
+            items = [(t, g.N, x, y) for mats in wl["layers"] for (g, t, y, x) in mats
+                     if g.K == K]
             groups.append(nf4.GemvGroup(items, K))
     else:
         for mats in wl["layers"]:
             q, k, v, o, gate, up, down = mats
             for sel in ((q, k, v), (o,), (gate, up), (down,)):
                 K = sel[0][0].K
-                groups.append(nf4.GemvGroup([(t, g.N, xs[K], y) for (g, t, y) in sel], K))
+                groups.append(nf4.GemvGroup([(t, g.N, x, y) for (g, t, y, x) in sel], K))
     big, tb, out = wl["big"]
 
     def gemvs():
@@ -446,15 +450,14 @@ def cpu_baseline(wl, seconds: float):
 
     import oracle
     threads = oracle.max_threads()
-    xs = {K: x.view(torch.int16).cpu().numpy().view(np.uint16) for K, x in wl["xs"].items()}
     done_bytes, elapsed, ngemv = 0, 0.0, 0
     for mats in wl["layers"]:
-        for (g, t, y) in mats:
+        for (g, t, y, x) in mats:
             q = oracle.Quantized(t.packed.cpu().numpy(), t.absmax_q.cpu().numpy(),
                                  t.absmax2.cpu().numpy().view(np.uint16),
                                  t.code2.cpu().numpy().view(np.uint16), t.offset, t.n)
             s = time.perf_counter()
-            oracle.gemv(q, g.N, g.K, xs[g.K])
+            oracle.gemv(q, g.N, g.K, x.view(torch.int16).cpu().numpy().view(np.uint16))
             elapsed += time.perf_counter() - s
             done_bytes += gemv_bytes(g.N, g.K)
             ngemv += 1
@@ -551,7 +554,7 @@ def main():
     dq_owner = make_step(wl, "stream")
     g_dq = capture(dq_owner[1], stream)
 
-    n_gemv_bytes = sum(gv_bytes_f(g.N, g.K) for mats in wl["layers"] for (g, _, _) in mats)
+    n_gemv_bytes = sum(gv_bytes_f(g.N, g.K) for mats in wl["layers"] for (g, *_) in mats)
     big = wl["big"][0]
     n_dq_bytes = dq_bytes_f(big.n)
     step_bytes = n_gemv_bytes + n_dq_bytes
@@ -674,7 +677,7 @@ def main():
         "config": {
             "workload": "decode_sweep_7b_32layers_224gemv_b1+dequant_8192x28672"
                         + ("" if fmt == "double" else "_" + fmt),
-            "gemv_weights": sum(g.N * g.K for mats in wl["layers"] for (g, _, _) in mats),
+            "gemv_weights": sum(g.N * g.K for mats in wl["layers"] for (g, *_) in mats),
             "batch": 1, "blocksize": 128 if fmt == "int4" else 64,
             "s2_blocksize": 256 if fmt == "double" else None,
             "dequant_elems": big.n, "dequant_out": "bf16",

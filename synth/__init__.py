@@ -135,6 +135,16 @@ def llama_x_seed(batch: int) -> int:
 SWEEP_LAYERS = 32
 SWEEP_X_SEED = 5999
 
+# Which activation vector of its layer each sweep GEMV reads: q, k and v read
+# the attention input, o the attention output, gate and up the MLP input,
+# down the MLP's inner activation (K = 11008).
+SWEEP_X_SLOT = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
+
+
+def sweep_x_seed(layer: int, slot: int) -> int:
+    """Seed of activation vector `slot` (0..3) of sweep layer `layer`."""
+    return SWEEP_X_SEED + 4 * layer + slot
+
 
 def sweep_layer(layer: int) -> list[Gemv]:
     """The 7 GEMVs of one 7B-shaped decoder layer (q, k, v, o, gate, up, down)."""

@@ -58,10 +58,31 @@ CASES = [
 ]
 
 
+# Several 4096-column passes with rows enough (>= 8192) for the
+# shared-activation kernel, which serves these launches at batch 1-2.
+XLDS_CASES = [
+    (11008, [(8192, 970), (300, 971)], 64),
+    (11008, [(8192, 972)], 128),
+    (8192, [(8192, 975), (40, 976)], 64),
+    (8192, [(8200, 977)], 128),
+]
+
+
 @pytest.mark.parametrize("fmt", ["absmax32", "int4"])
-@pytest.mark.parametrize("batch", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("K,shapes,bs", CASES)
 def test_grouped_formats_match_oracle(fmt, batch, K, shapes, bs):
+    _grouped_case(fmt, batch, K, shapes, bs)
+
+
+@pytest.mark.parametrize("fmt", ["absmax32", "int4"])
+@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("K,shapes,bs", XLDS_CASES)
+def test_grouped_formats_several_passes_match_oracle(fmt, batch, K, shapes, bs):
+    _grouped_case(fmt, batch, K, shapes, bs)
+
+
+def _grouped_case(fmt, batch, K, shapes, bs):
     qs, items = [], []
     for N, seed in shapes:
         q, t = _encode(fmt, seed, N, K, bs)

@@ -94,7 +94,10 @@ def test_int4_dequant_special_values(g):
     n = 512 * 40
     ng = n // g
     packed = np.tile(np.arange(256, dtype=np.uint8), n // 512)
-    s = (rng.standard_normal(ng) * 2.0 ** rng.integers(-24, 16, ng)).astype(np.float16)
+    # finite fp16 scales only (|s| <= 65504): the draw is clipped before the cast
+    s = np.clip(rng.standard_normal(ng) * 2.0 ** rng.integers(-24, 16, ng), -65504.0,
+                65504.0).astype(np.float16)
+    assert np.all(np.isfinite(s))
     z = (rng.standard_normal(ng) * 20).astype(np.float16)
     s[:4] = [0.0, -0.0, 6e-8, 65504.0]
     q = oracle.QuantizedInt4(packed, s.view(np.uint16), z.view(np.uint16), n, g)

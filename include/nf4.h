@@ -264,7 +264,8 @@ typedef struct nf4_gemv_desc {
  * ranges above.  The descriptors are read on the device: a matrix whose
  * packed or x pointer is not 16-byte aligned, whose pointers are NULL, or
  * whose N disagrees with the row_begin sequence is skipped (its y is left
- * unwritten).
+ * unwritten).  The kernel cannot report a skipped matrix; check the table
+ * with nf4_gemv_desc_check on the host before uploading it.
  */
 nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t total_rows,
                             int64_t K, int32_t blocksize, int32_t s2_blocksize,
@@ -276,6 +277,31 @@ nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t t
  * takes (host function).
  */
 size_t nf4_gemv_sched_size(void);
+
+/*
+ * nf4_gemv_desc_check -- host-side check of a grouped GEMV descriptor table
+ * before it is uploaded (host function, no GPU work).  The grouped kernels
+ * skip a descriptor they cannot use, leaving its y unwritten, and have no way
+ * to report it; this function finds exactly those descriptors.
+ *
+ *  descs      : HOST array of `count` descriptors for nf4_gemv_grouped
+ *               (format 0), nf4_gemv_grouped_absmax32
+ *               (format 1) or int4_gemv_grouped (format 2); the three layouts
+ *               are the same 64 bytes.
+ *  total_rows, K : as they will be passed to the grouped call.
+ *  first_bad  : optional output: the index of the first unusable descriptor,
+ *               `count` when the N values do not add up to total_rows, or -1
+ *               when every descriptor is usable.
+ * A descriptor is usable when its packed, scale, x and y pointers are not
+ * NULL (the second scale slot may be NULL in format 1), packed and x are
+ * 16-byte aligned, an fp32 absmax array is 4-byte and fp16 scale / zero-point
+ * arrays are 2-byte aligned, 0 <= N and N * K < 2^31, and row_begin is the
+ * sum of N over the descriptors before it.
+ * Returns NF4_OK when all are usable, NF4_EINVAL otherwise (also for a NULL
+ * table with count > 0, negative sizes or an unknown format).
+ */
+nf4_status nf4_gemv_desc_check(const void* descs, int32_t count, int64_t total_rows, int64_t K,
+                               int32_t format, int32_t* first_bad);
 
 /*
  * One matrix of a grouped single-level GEMV (64 bytes, the layout of

@@ -273,3 +273,65 @@ def test_probes_validate_arguments(lib):
     assert lib.nf4_probe_expand_copy(FAKE, 64, None, None) == 1
     assert lib.nf4_probe_expand_copy(FAKE, 64, C.c_void_p(0x1008), None) == 1   # dst misaligned
     assert lib.nf4_probe_expand_copy(FAKE, 6, FAKE, None) == 1                   # not 4 * k
+
+
+def _desc_table(Ns, K, align=16):
+    """A host descriptor table with fake, suitably aligned pointers."""
+    import numpy as np
+
+    from w4a16_gemv_amd._binding import _DESC_DTYPE
+    t = np.zeros(len(Ns), dtype=np.dtype(_DESC_DTYPE))
+    row = 0
+    for i, N in enumerate(Ns):
+        base = 0x100000 * (i + 1)
+        t[i] = (base, base + 0x40000, base + 0x80000, base + 0xC0000, base + 0xE0000, N, row,
+                0.0, 0)
+        row += N
+    return t, row
+
+
+def _check(lib, t, total, K, fmt=0):
+    bad = C.c_int32(-7)
+    rc = lib.nf4_gemv_desc_check(t.ctypes.data if t is not None else None,
+                                 0 if t is None else len(t), total, K, fmt, C.byref(bad))
+    return rc, bad.value
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_gemv_desc_check_accepts_a_good_table(lib, fmt):
+    t, total = _desc_table([64, 3, 0, 4096], 4096)
+    assert _check(lib, t, total, 4096, fmt) == (0, -1)
+
+
+@pytest.mark.parametrize("field,value,fmt,index", [
+    ("packed", 0x200008, 0, 1),      # packed not 16-byte aligned
+    ("x", 0x2C0004, 0, 1),           # x not 16-byte aligned
+    ("y", 0, 0, 1),                  # NULL y
+    ("absmax2", 0, 0, 1),            # NULL second scale (formats 0 and 2)
+    ("absmax2", 0, 2, 1),
+    ("absmax2", 0x280001, 0, 1),     # fp16 absmax2 misaligned
+    ("absmax_q", 0x240002, 1, 1),    # fp32 absmax not 4-byte aligned
+    ("absmax_q", 0x240001, 2, 1),    # fp16 scales misaligned
+    ("N", -1, 0, 1),
+    ("row_begin", 63, 0, 1),         # not the running sum of N
+    ("N", 1 << 20, 0, 1),            # N * K >= 2^31
+])
+def test_gemv_desc_check_finds_the_bad_descriptor(lib, field, value, fmt, index):
+    t, total = _desc_table([64, 3, 5], 4096)
+    t[index][field] = value
+    if field == "N":
+        total = int(t["N"].sum())
+        t[2]["row_begin"] = int(t[0]["N"] + t[1]["N"])
+    rc, bad = _check(lib, t, total, 4096, fmt)
+    assert (rc, bad) == (1, index)
+
+
+def test_gemv_desc_check_other_cases(lib):
+    t, total = _desc_table([64, 3], 4096)
+    assert _check(lib, t, total + 1, 4096) == (1, 2)        # N does not add up
+    t1, total1 = _desc_table([64], 4096)
+    t1[0]["absmax2"] = 0
+    assert _check(lib, t1, total1, 4096, 1) == (0, -1)      # format 1: second slot unused
+    assert _check(lib, t, total, 4096, 3)[0] == 1           # unknown format
+    assert _check(lib, None, 0, 4096) == (0, -1)            # empty table
+    assert lib.nf4_gemv_desc_check(None, 2, 10, 4096, 0, None) == 1

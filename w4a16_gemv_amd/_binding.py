@@ -23,7 +23,8 @@ EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv", "
             "nf4_dequant_absmax32", "nf4_gemv_absmax32", "nf4_gemv_grouped",
             "nf4_gemv_grouped_absmax32", "int4_gemv_grouped",
             "nf4_probe_stream_read", "nf4_probe_expand_copy",
-            "nf4_gemv_sched_size", "nf4_code2_linear", "nf4_quantize_workspace_size",
+            "nf4_gemv_sched_size", "nf4_gemv_desc_check",
+            "nf4_code2_linear", "nf4_quantize_workspace_size",
             "nf4_quantize", "nf4_quantize_absmax32", "int4_dequant", "int4_gemv",
             "int4_quantize")
 
@@ -74,6 +75,8 @@ def load() -> C.CDLL:
     lib.int4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, C.c_size_t, p]
     lib.nf4_gemv_sched_size.restype = C.c_size_t
     lib.nf4_gemv_sched_size.argtypes = []
+    lib.nf4_gemv_desc_check.restype = C.c_int
+    lib.nf4_gemv_desc_check.argtypes = [p, i32, i64, i64, i32, C.POINTER(C.c_int32)]
     lib.nf4_code2_linear.restype = None
     lib.nf4_code2_linear.argtypes = [p]
     lib.nf4_quantize_workspace_size.restype = C.c_size_t
@@ -494,6 +497,7 @@ class GemvGroup:
     that rows go to the waves in chunks as they free up; False: fixed split.
     The results are bit-identical either way.  The group's workspace serves
     one launch at a time: do not run the same group on two streams at once.
+    The table is checked on the host by nf4_gemv_desc_check before upload.
     """
 
     def __init__(self, items, K: int, dynamic: bool = True):
@@ -559,6 +563,12 @@ class GemvGroup:
             table[i] = entry
             row += N
         self.total_rows = row
+        fmt = 2 if self.kind is Int4Tensor else 1 if self.kind is NF4Absmax32Tensor else 0
+        bad = C.c_int32(-1)
+        st = load().nf4_gemv_desc_check(table.ctypes.data, len(items), row, self.K, fmt,
+                                        C.byref(bad))
+        if st != NF4_OK:
+            raise ValueError(f"descriptor {bad.value} is not usable by the grouped kernels")
         dev = items[0][0].packed.device
         self.table = torch.from_numpy(table.view(np.uint8)).to(dev)
         if self.code2 is not None:

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "nf4.h"
 
 namespace nf4dev {
@@ -110,20 +112,21 @@ __device__ __forceinline__ void build_pair_table(uint2* s_pairs, int tid, int nt
 
 // --- host helpers ---
 
-// Compute units of the current device (cached per device id; a benign race
-// writes the same value).
+// Compute units of the current device, cached per device id.  The cache
+// entries are atomics: threads that race on the first call of a device each
+// query the attribute and store the same value.
 inline int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // zero-initialized (static storage)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int cus = 0;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cache[dev] = cus;
+    cache[dev].store(cus, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return cus;
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

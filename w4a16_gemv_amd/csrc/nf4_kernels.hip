@@ -2433,4 +2433,35 @@ nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t t
   }
 }
 
+nf4_status nf4_gemv_desc_check(const void* descs, int32_t count, int64_t total_rows, int64_t K,
+                               int32_t format, int32_t* first_bad) {
+  if (first_bad) *first_bad = -1;
+  if (count < 0 || total_rows < 0 || K < 0 || format < 0 || format > 2) return NF4_EINVAL;
+  if (count == 0) return total_rows == 0 ? NF4_OK : NF4_EINVAL;
+  if (descs == nullptr) return NF4_EINVAL;
+  const nf4_gemv_desc* d = static_cast<const nf4_gemv_desc*>(descs);
+  int64_t row = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const nf4_gemv_desc& e = d[i];
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(e.absmax_q);
+    const uintptr_t za = reinterpret_cast<uintptr_t>(e.absmax2);
+    const bool scales_ok = format == kFmtAbsmax32 ? (sa & 3) == 0
+                           : format == kFmtInt4   ? ((sa | za) & 1) == 0
+                                                  : (za & 1) == 0;
+    const bool ok = e.packed && e.absmax_q && (format == kFmtAbsmax32 || e.absmax2) && e.x &&
+                    e.y && aligned(e.packed, 16) && aligned(e.x, 16) && scales_ok && e.N >= 0 &&
+                    e.N <= 0x7FFFFFFF && e.N * K < (int64_t(1) << 31) && e.row_begin == row;
+    if (!ok) {
+      if (first_bad) *first_bad = i;
+      return NF4_EINVAL;
+    }
+    row += e.N;
+  }
+  if (row != total_rows) {
+    if (first_bad) *first_bad = count;
+    return NF4_EINVAL;
+  }
+  return NF4_OK;
+}
+
 }  // extern "C"

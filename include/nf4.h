@@ -279,13 +279,46 @@ nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t t
 size_t nf4_gemv_sched_size(void);
 
 /*
+ * nf4_gemv_grouped_noalloc -- nf4_gemv_grouped with chunked row scheduling and
+ * no workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It allocates nothing.  The scheduling counters live in the
+ * library's own scratch: a fixed array of nf4_gemv_sched_size() = 2 KiB of
+ * device memory, one per GPU, which each GPU the library runs on holds until
+ * the process ends.  The caller passes inputs and outputs as for
+ * nf4_gemv_grouped, and the results are bit-identical to it.
+ *
+ *  Arguments : those of nf4_gemv_grouped without sched / sched_bytes.  The
+ *              current device must be the device of `stream`.
+ *  Scratch   : its device address is looked up once per device
+ *              (hipGetSymbolAddress, with that device current) on the first
+ *              call there.  A launch that uses the counters first clears them
+ *              with a small kernel on `stream`; both kernels are only
+ *              enqueued.  Every call on one GPU shares that GPU's scratch,
+ *              which keeps the last call's contents: calls that overlap in
+ *              time on one GPU (other streams, unordered host threads) race
+ *              and may compute wrong rows.  Order them on one stream.
+ *  Limits    : one scratch serves every launch size the grouped entry point
+ *              accepts (up to 1024 matrices, 2^31 - 1 rows, K <= 16384, batch
+ *              1..8); beyond those the call returns NF4_EUNSUPPORTED without
+ *              launching, as nf4_gemv_grouped does.
+ * Returns the status codes of nf4_gemv_grouped (NF4_EINVAL for bad arguments,
+ * before any HIP call), and NF4_EHIP when the scratch address cannot be
+ * obtained or a launch fails.
+ */
+nf4_status nf4_gemv_grouped_noalloc(const nf4_gemv_desc* descs, int32_t count,
+                                    int64_t total_rows, int64_t K, int32_t blocksize,
+                                    int32_t s2_blocksize, const uint16_t* code2, int32_t batch,
+                                    void* stream);
+
+/*
  * nf4_gemv_desc_check -- host-side check of a grouped GEMV descriptor table
  * before it is uploaded (host function, no GPU work).  The grouped kernels
  * skip a descriptor they cannot use, leaving its y unwritten, and have no way
  * to report it; this function finds exactly those descriptors.
  *
- *  descs      : HOST array of `count` descriptors for nf4_gemv_grouped
- *               (format 0), nf4_gemv_grouped_absmax32
+ *  descs      : HOST array of `count` descriptors for nf4_gemv_grouped /
+ *               nf4_gemv_grouped_noalloc (format 0), nf4_gemv_grouped_absmax32
  *               (format 1) or int4_gemv_grouped (format 2); the three layouts
  *               are the same 64 bytes.
  *  total_rows, K : as they will be passed to the grouped call.

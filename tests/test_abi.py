@@ -275,6 +275,25 @@ def test_probes_validate_arguments(lib):
     assert lib.nf4_probe_expand_copy(FAKE, 6, FAKE, None) == 1                   # not 4 * k
 
 
+@pytest.mark.parametrize("kw,expect", [
+    (dict(K=63), 1), (dict(bs=3), 1), (dict(s2=0), 1), (dict(count=-1), 1),
+    (dict(descs=None), 1), (dict(code2=None), 1), (dict(descs=C.c_void_p(0x1004)), 1),
+    (dict(bs=16), 2), (dict(K=96 + 16), 2), (dict(batch=9), 2), (dict(count=1025), 2),
+])
+def test_gemv_grouped_noalloc_rejects_bad_arguments(lib, kw, expect):
+    """Argument errors come back before any HIP call (and before the scratch
+    is looked up)."""
+    rc = lib.nf4_gemv_grouped_noalloc(kw.get("descs", FAKE), kw.get("count", 2), 100,
+                                      kw.get("K", 64), kw.get("bs", 64), kw.get("s2", 256),
+                                      kw.get("code2", FAKE), kw.get("batch", 1), None)
+    assert rc == expect
+
+
+def test_gemv_grouped_noalloc_empty_is_a_no_op(lib):
+    assert lib.nf4_gemv_grouped_noalloc(None, 0, 0, 64, 64, 256, None, 1, None) == 0
+    assert lib.nf4_gemv_grouped_noalloc(None, 3, 0, 64, 64, 256, None, 1, None) == 0
+
+
 def _desc_table(Ns, K, align=16):
     """A host descriptor table with fake, suitably aligned pointers."""
     import numpy as np

@@ -23,7 +23,7 @@ EXPORTED = ("nf4_abi_version", "nf4_status_string", "nf4_dequant", "nf4_gemv", "
             "nf4_dequant_absmax32", "nf4_gemv_absmax32", "nf4_gemv_grouped",
             "nf4_gemv_grouped_absmax32", "int4_gemv_grouped",
             "nf4_probe_stream_read", "nf4_probe_expand_copy",
-            "nf4_gemv_sched_size", "nf4_gemv_desc_check",
+            "nf4_gemv_sched_size", "nf4_gemv_grouped_noalloc", "nf4_gemv_desc_check",
             "nf4_code2_linear", "nf4_quantize_workspace_size",
             "nf4_quantize", "nf4_quantize_absmax32", "int4_dequant", "int4_gemv",
             "int4_quantize")
@@ -75,6 +75,8 @@ def load() -> C.CDLL:
     lib.int4_gemv_grouped.argtypes = [p, i32, i64, i64, i32, i32, p, C.c_size_t, p]
     lib.nf4_gemv_sched_size.restype = C.c_size_t
     lib.nf4_gemv_sched_size.argtypes = []
+    lib.nf4_gemv_grouped_noalloc.restype = C.c_int
+    lib.nf4_gemv_grouped_noalloc.argtypes = [p, i32, i64, i64, i32, i32, p, i32, p]
     lib.nf4_gemv_desc_check.restype = C.c_int
     lib.nf4_gemv_desc_check.argtypes = [p, i32, i64, i64, i32, C.POINTER(C.c_int32)]
     lib.nf4_code2_linear.restype = None
@@ -497,10 +499,13 @@ class GemvGroup:
     that rows go to the waves in chunks as they free up; False: fixed split.
     The results are bit-identical either way.  The group's workspace serves
     one launch at a time: do not run the same group on two streams at once.
+    noalloc: NF4Tensor items only; launch through nf4_gemv_grouped_noalloc,
+    which schedules rows in chunks with the library's own per-GPU scratch
+    (no workspace tensor; launches on one GPU must not overlap in time).
     The table is checked on the host by nf4_gemv_desc_check before upload.
     """
 
-    def __init__(self, items, K: int, dynamic: bool = True):
+    def __init__(self, items, K: int, dynamic: bool = True, noalloc: bool = False):
         import numpy as np
         if not 1 <= len(items) <= MAX_GROUP:
             raise ValueError(f"a group holds 1..{MAX_GROUP} matrices")
@@ -573,8 +578,11 @@ class GemvGroup:
         self.table = torch.from_numpy(table.view(np.uint8)).to(dev)
         if self.code2 is not None:
             _dev(self.code2, "code2", _HALF_BITS, 256)
+        self.noalloc = bool(noalloc)
+        if self.noalloc and self.kind is not NF4Tensor:
+            raise ValueError("noalloc grouped launches take NF4Tensor items only")
         self.sched = None
-        if dynamic:
+        if dynamic and not self.noalloc:
             nbytes = int(load().nf4_gemv_sched_size())
             self.sched = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=dev)
             if self.sched.data_ptr() % 256:
@@ -593,6 +601,12 @@ class GemvGroup:
             st = lib.nf4_gemv_grouped_absmax32(self.table.data_ptr(), len(self.items),
                                                self.total_rows, self.K, self.blocksize,
                                                self.batch, sp, sn, _stream(self.table))
+        elif self.noalloc:
+            name = "nf4_gemv_grouped_noalloc"
+            st = lib.nf4_gemv_grouped_noalloc(self.table.data_ptr(), len(self.items),
+                                              self.total_rows, self.K, self.blocksize,
+                                              self.s2_blocksize, self.code2.data_ptr(),
+                                              self.batch, _stream(self.table))
         else:
             name = "nf4_gemv_grouped"
             st = lib.nf4_gemv_grouped(self.table.data_ptr(), len(self.items), self.total_rows,

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "int4.h"
 #include "nf4.h"
 #include "nf4_device.h"
@@ -1856,6 +1858,11 @@ __global__ __launch_bounds__(256) void gemv_any_kernel(
 }
 
 // y = 0 for an empty reduction (K == 0).
+// Zeroes a scheduling workspace of `count` counters (one small workgroup).
+__global__ void sched_clear_kernel(unsigned* __restrict__ sched, int count) {
+  for (int i = threadIdx.x; i < count; i += blockDim.x) sched[i] = 0u;
+}
+
 __global__ void fill_zero_kernel(uint16_t* __restrict__ y, int64_t count) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
@@ -1929,7 +1936,7 @@ void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, i
 template <int B, int R, int P, int WPE, int FMT>
 nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                        int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
-                       unsigned* sched, hipStream_t st) {
+                       unsigned* sched, bool sched_clear, hipStream_t st) {
   // One row per wave at most one 512-lane workgroup per CU; a second one per
   // CU (four waves per SIMD) only once every wave gets two rows or more: with
   // one row per wave the younger workgroup mostly waits behind the older one
@@ -1953,6 +1960,11 @@ nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, 
                    (FMT != kFmtDouble || nb % s2 == 0 || s2 % nb == 0);
   const dim3 g(static_cast<uint32_t>(grid)), blk(512);
   unsigned* sc = dyn ? sched : nullptr;
+  // a workspace whose contents are not known to be zero (the library's own
+  // scratch) is cleared by a kernel on the same stream first
+  if (dyn && sched_clear)
+    hipLaunchKernelGGL(sched_clear_kernel, dim3(1), dim3(256), 0, st, sched,
+                       kSchedRegions * kSchedStride);
   if (reg && dyn)
     hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, true, FMT, true>), g, blk, 0, st, descs,
                        single, count, total_rows, K, lbs, ls2, code2, sc, C);
@@ -1995,15 +2007,15 @@ nf4_status xlds_launch(const nf4_gemv_desc* descs, int count, int total_rows, in
 template <int B, int FMT>
 nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
-                         unsigned* sched, hipStream_t st) {
+                         unsigned* sched, bool sched_clear, hipStream_t st) {
   if (K % 64 != 0 || lbs < 6) return NF4_EUNSUPPORTED;
   const int P = (K + kWaveCols - 1) / kWaveCols;
   if constexpr (B == 1) {
-    if (P == 1) return wave_launch<1, 2, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 1) return wave_launch<1, 2, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, sched_clear, st);
   }
   // the other configurations serve grouped launches only
   if constexpr (B == 2) {
-    if (P == 1) return wave_launch<2, 1, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+    if (P == 1) return wave_launch<2, 1, 1, 4, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, sched_clear, st);
   }
   // more than one pass: the activations go to LDS (gemv_xlds_kernel), for
   // launches that give every wave two rows or more (see xlds_rows_ok)
@@ -2023,7 +2035,7 @@ nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
 template <int B, int FMT>
 nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                          int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
-                         unsigned* sched, hipStream_t st) {
+                         unsigned* sched, hipStream_t st, bool sched_clear = false) {
   // grouped launches at batch 3-8 with one pass: the shared-activation kernel
   // (four waves per SIMD, no barrier per row group; 16% faster than the team
   // kernel at batch 4, 3% at batch 8)
@@ -2047,7 +2059,8 @@ nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
         B == 1 && K <= kWaveCols && static_cast<int64_t>(total_rows) * K <= (int64_t(1) << 24);
     if (descs != nullptr || single_ok) {
       const nf4_status ws =
-          wave_dispatch<B, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched, st);
+          wave_dispatch<B, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched,
+                                sched_clear, st);
       if (ws != NF4_EUNSUPPORTED) return ws;
     }
   }
@@ -2166,6 +2179,74 @@ nf4_status grouped_other(const void* descs, int32_t count, int64_t total_rows, i
     case 6: return stream_launch<6, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
     case 7: return stream_launch<7, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
     default: return stream_launch<8, FMT>(d, none, count, tr, k, lbs, 0, nullptr, sc, st);
+  }
+}
+
+}  // namespace
+
+// The scheduling counters of nf4_gemv_grouped_noalloc: the library's own
+// scratch, kSchedRegions regions of kSchedStride counters (2 KiB).  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code this name is not a device address: the address of the current GPU's
+// copy comes from scratch_address().
+static __device__ __align__(256) unsigned scratch[kSchedRegions * kSchedStride];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<unsigned*> g_scratch_addr[kMaxDevices];  // per device; zero-initialized
+
+// The device address of the current GPU's copy of `scratch`, looked up with
+// hipGetSymbolAddress on the first call for each device (with that device
+// current) and kept; nullptr if the lookup fails.  Threads racing on the first
+// call store the same address.
+unsigned* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  unsigned* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+      return nullptr;
+    p = static_cast<unsigned*>(addr);
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// The checks and dispatch shared by nf4_gemv_grouped and its no-allocation
+// variant.  sc: the caller's scheduling workspace (already validated) or
+// NULL; use_scratch: take the library's scratch instead (looked up only once
+// the arguments have passed their checks) and clear it before use.
+nf4_status grouped_double(const nf4_gemv_desc* descs, int32_t count, int64_t total_rows,
+                          int64_t K, int32_t blocksize, int32_t s2_blocksize,
+                          const uint16_t* code2, int32_t batch, unsigned* sc, bool use_scratch,
+                          void* stream) {
+  int lbs = 0, ls2 = 0;
+  if (!pow2_log2(blocksize, &lbs) || !pow2_log2(s2_blocksize, &ls2)) return NF4_EINVAL;
+  if (count < 0 || total_rows < 0 || K < 0 || (K & 1)) return NF4_EINVAL;
+  if (count == 0 || total_rows == 0) return NF4_OK;
+  if (!descs || !code2 || (reinterpret_cast<uintptr_t>(descs) & 7)) return NF4_EINVAL;
+  if (count > kMaxDescs || total_rows >= 0x7FFFFFFF || K == 0 || K % 32 != 0 ||
+      K > 8 * kSlab || lbs < 5 || batch < 1 || batch > 8)
+    return NF4_EUNSUPPORTED;
+  const bool sched_clear = use_scratch;
+  if (use_scratch) {
+    sc = scratch_address();
+    if (sc == nullptr) return NF4_EHIP;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const nf4_gemv_desc none{};
+  const int tr = static_cast<int>(total_rows), k = static_cast<int>(K);
+  switch (batch) {
+    case 1: return stream_launch<1, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st, sched_clear);
+    case 2: return stream_launch<2, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st, sched_clear);
+    case 3: return stream_launch<3, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st, sched_clear);
+    case 4: return stream_launch<4, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st, sched_clear);
+    case 5: return stream_launch<5, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st, sched_clear);
+    case 6: return stream_launch<6, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st, sched_clear);
+    case 7: return stream_launch<7, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st, sched_clear);
+    default: return stream_launch<8, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st, sched_clear);
   }
 }
 
@@ -2407,30 +2488,23 @@ nf4_status nf4_gemv_grouped(const nf4_gemv_desc* descs, int32_t count, int64_t t
                             int64_t K, int32_t blocksize, int32_t s2_blocksize,
                             const uint16_t* code2, int32_t batch, void* sched,
                             size_t sched_bytes, void* stream) {
-  int lbs = 0, ls2 = 0;
-  if (!pow2_log2(blocksize, &lbs) || !pow2_log2(s2_blocksize, &ls2)) return NF4_EINVAL;
-  if (count < 0 || total_rows < 0 || K < 0 || (K & 1)) return NF4_EINVAL;
   if (sched != nullptr && (!aligned(sched, 256) || sched_bytes < nf4_gemv_sched_size()))
     return NF4_EINVAL;
-  if (count == 0 || total_rows == 0) return NF4_OK;
-  if (!descs || !code2 || (reinterpret_cast<uintptr_t>(descs) & 7)) return NF4_EINVAL;
-  if (count > kMaxDescs || total_rows >= 0x7FFFFFFF || K == 0 || K % 32 != 0 ||
-      K > 8 * kSlab || lbs < 5 || batch < 1 || batch > 8)
-    return NF4_EUNSUPPORTED;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const nf4_gemv_desc none{};
-  unsigned* sc = static_cast<unsigned*>(sched);
-  const int tr = static_cast<int>(total_rows), k = static_cast<int>(K);
-  switch (batch) {
-    case 1: return stream_launch<1, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 2: return stream_launch<2, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 3: return stream_launch<3, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 4: return stream_launch<4, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 5: return stream_launch<5, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 6: return stream_launch<6, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    case 7: return stream_launch<7, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-    default: return stream_launch<8, kFmtDouble>(descs, none, count, tr, k, lbs, ls2, code2, sc, st);
-  }
+  return grouped_double(descs, count, total_rows, K, blocksize, s2_blocksize, code2, batch,
+                        static_cast<unsigned*>(sched), false, stream);
+}
+
+nf4_status nf4_gemv_grouped_noalloc(const nf4_gemv_desc* descs, int32_t count,
+                                    int64_t total_rows, int64_t K, int32_t blocksize,
+                                    int32_t s2_blocksize, const uint16_t* code2, int32_t batch,
+                                    void* stream) {
+  static_assert(sizeof(scratch) == sizeof(unsigned) * kSchedRegions * kSchedStride,
+                "the scratch holds exactly one scheduling workspace");
+  // the workspace a launch needs is the same fixed size for every launch, so
+  // no launch size can exceed the scratch; the grouped limits still apply
+  if (nf4_gemv_sched_size() > sizeof(scratch)) return NF4_EUNSUPPORTED;
+  return grouped_double(descs, count, total_rows, K, blocksize, s2_blocksize, code2, batch,
+                        nullptr, true, stream);
 }
 
 nf4_status nf4_gemv_desc_check(const void* descs, int32_t count, int64_t total_rows, int64_t K,

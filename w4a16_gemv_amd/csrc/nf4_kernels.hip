@@ -1471,6 +1471,107 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   }
 }
 
+// One pass (4096 columns) of R rows for one lane, with the activations read
+// from the workgroup's LDS copy: s_xp points at the lane's entry of dword 0 of
+// the pass for batch row 0, and batch row b is bstride entries further.  The
+// lane's eight packed dwords per row (two loads of four) are walked in order,
+// rows inner: the B activation quads of a dword are read once and serve all R
+// rows, and the table entries of the next (dword, row) are read before the
+// current one's products.  At the end of each load the two half sums of a
+// block are completed across the lane pair and the lane scales the block it
+// owns (odd lanes: the second load's).  val is assigned when `first` (the
+// row's first pass), accumulated otherwise.
+template <int B, int R, int FMT>
+__device__ __forceinline__ void xpass_rows(const WaveGroup<R, 1, FMT>& g, uint32_t copy_off,
+                                           const uint2* s_pairs, const float* s_code2,
+                                           float offset, bool odd, bool own_in,
+                                           const float (&xs)[B], float (&val)[R * B], bool first,
+                                           const u32x4* s_xp, int bstride) {
+  constexpr int U = 8 * R;
+  const char* tab = reinterpret_cast<const char*>(s_pairs);
+  uint2 t[2][4];
+  u32x4 xv[2][B];
+  auto fetch = [&](int u, uint2 (&tt)[4]) {
+    const int hj = u / R, rr = u % R;
+    const uint32_t d = g.pk[rr][0][hj >> 2][hj & 3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t addr = __builtin_amdgcn_perm(copy_off, d, 0x0C0C0004u | (uint32_t(i) << 8));
+      if constexpr (FMT == kFmtInt4)
+        tt[i].x = *reinterpret_cast<const uint32_t*>(tab + addr);  // one exact code pair
+      else
+        tt[i] = *reinterpret_cast<const uint2*>(tab + addr);
+    }
+    if (rr == 0) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) xv[hj & 1][b] = s_xp[b * bstride + hj * 64];
+    }
+  };
+  float part[R][B], half0[R][B];
+  fetch(0, t[0]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u + 1 < U) fetch(u + 1, t[(u + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int hj = u / R, rr = u % R;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 ti = t[u & 1][i];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        // copied out first: a bit_cast of a vector-element lvalue reads
+        // element 0 whatever the index
+        const uint32_t xw = xv[hj & 1][b][i];
+        const bf16x2 xp = __builtin_bit_cast(bf16x2, xw);
+        // the first product of each half starts from an immediate zero
+        const float acc = (hj & 3) == 0 && i == 0 ? 0.0f : part[rr][b];
+        part[rr][b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.x), xp, acc,
+                                                      false);
+        if constexpr (FMT != kFmtInt4)
+          part[rr][b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ti.y), xp,
+                                                        part[rr][b], false);
+      }
+    }
+    if (hj == 3) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) half0[rr][b] = part[rr][b];
+    }
+    if (hj == 7) {
+      float blk[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float s0 = pair_lane_sum(half0[rr][b]);
+        const float s1 = pair_lane_sum(part[rr][b]);
+        blk[b] = odd ? s1 : s0;
+      }
+      if constexpr (FMT == kFmtInt4) {
+        const float sc = f16_to_f32(g.q[rr][0]);
+        const float z = f16_to_f32(g.a2[rr][0]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const float zt = z * xs[b];
+          const float c = own_in ? sc * (blk[b] - zt) : 0.0f;
+          val[rr * B + b] = first ? c : val[rr * B + b] + c;
+        }
+      } else {
+        float a;
+        if constexpr (FMT == kFmtAbsmax32) {
+          a = __builtin_bit_cast(float, g.q[rr][0]);
+        } else {
+          const float prod = s_code2[g.q[rr][0]] * f16_to_f32(g.a2[rr][0]);
+          a = prod + offset;
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const float c = own_in ? a * blk[b] : 0.0f;
+          val[rr * B + b] = first ? c : val[rr * B + b] + c;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The shared-activation GEMV (grouped launches, K % 64 == 0, blocksize >= 64:
 // batch 1-2 with 4096 < K <= 16384, and batch 3-8 with K <= 4096).
@@ -1489,20 +1590,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 // workgroup.  The workgroup walks its range one matrix at a time: it stages
 // that matrix's activations (a barrier before and after), then its waves
 // claim groups of R rows from an LDS counter until the matrix's part of the
-// range is used up.  Each wave keeps NBUF register buffers of row groups:
-// with three, the loads of the group after next are issued before the current
-// group is computed; with two (where registers are short), the buffer just
-// computed takes the group after next.  The loops run whole rounds of NBUF
-// steps.
+// range is used up.  A wave's unit of work is one pass of its R rows: for
+// every packed dword it reads the activations once and applies them to all R
+// rows, so the activation reads from LDS per weight byte fall by R (the LDS
+// bandwidth, shared by the decode table reads, bounds this kernel).  Each wave
+// keeps NB register buffers of units, NB a multiple of P, so that buffer j
+// always holds pass j % P: the loads of the unit NB - 1 ahead are issued
+// before the current unit is computed, and a new row group is claimed when
+// its first pass is loaded.  The loops run whole rounds of NB units.
 // ---------------------------------------------------------------------------
 constexpr int kXlThreads = 1024;
 
-template <int B, int R, int P, int NBUF, int FMT>
+template <int B, int R, int P, int NB, int FMT>
 __global__ __launch_bounds__(kXlThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_xlds_kernel(
     const nf4_gemv_desc* __restrict__ descs, int count, int total_rows, int K, int log2bs,
     int log2s2, const uint16_t* __restrict__ code2) {
   static_assert(R * B <= 8, "at most two quad reductions per group");
-  static_assert(NBUF == 2 || NBUF == 3, "two or three register buffers");
+  static_assert(NB >= 2 && NB % P == 0, "whole passes per round, at least two buffers");
   __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
   __shared__ float s_code2[256];
   __shared__ int s_rowbeg[kMaxDescs + 1];
@@ -1547,7 +1651,6 @@ __global__ __launch_bounds__(kXlThreads) __attribute__((amdgpu_waves_per_eu(4, 4
     }
     m = a;
   }
-  u32x4 xr_unused[B][P][8];  // wave_rows reads the LDS copy instead
   for (; m < count && rbeg(m) < hi; ++m) {
     const int beg = rbeg(m), end = rbeg(m + 1);
     const int s0 = max(lo, beg), s1 = min(hi, end);
@@ -1632,48 +1735,48 @@ __global__ __launch_bounds__(kXlThreads) __attribute__((amdgpu_waves_per_eu(4, 4
                                               store ? off : kOutOfRange, 0, 0);
       }
     };
-    auto compute = [&](const WaveGroup<R, P, FMT>& g, int rl, int len) {
-      if (len > 0) {
-        float val[R * B];
-        wave_rows<B, R, P, FMT, true>(g, xr_unused, copy_off, s_pairs, s_code2, ob.offset, odd,
-                                      own_in, xs, val, s_x, lane);
-        finish(val, rl, len);
-      }
+    // the lane's columns of pass q as a one-pass lane description
+    auto pass_lane = [&](int q) {
+      WaveLane<1> w1;
+      w1.pk[0][0] = wl.pk[q][0];
+      w1.pk[0][1] = wl.pk[q][1];
+      w1.x[0][0] = w1.x[0][1] = kFar;
+      w1.c0[0] = wl.c0[q];
+      w1.sq[0] = w1.sa2[0] = 0u;
+      return w1;
     };
-    WaveGroup<R, P, FMT> ga, gb;
-    int rla, lena, rlb, lenb;
-    claim(&rla, &lena);
-    load_wave_group<R, P, FMT>(ga, lb, rla, lena, wl, K, log2bs, log2s2);
-    claim(&rlb, &lenb);
-    load_wave_group<R, P, FMT>(gb, lb, rlb, lenb, wl, K, log2bs, log2s2);
-    if constexpr (NBUF == 2) {
-      // compute a group, then load the group after next into its buffer
-      auto step = [&](WaveGroup<R, P, FMT>& g, int& rl, int& len) {
-        compute(g, rl, len);
-        claim(&rl, &len);
-        load_wave_group<R, P, FMT>(g, lb, rl, len, wl, K, log2bs, log2s2);
+    WaveGroup<R, 1, FMT> gb[NB];
+    int rlb[NB], lenb[NB];
+    int crl = 0, clen = 0;  // the row group claimed last
+    // prologue: the first NB - 1 units
+#pragma unroll
+    for (int j = 0; j + 1 < NB; ++j) {
+      if (j % P == 0) claim(&crl, &clen);
+      rlb[j] = crl;
+      lenb[j] = clen;
+      load_wave_group<R, 1, FMT>(gb[j], lb, crl, clen, pass_lane(j % P), K, log2bs, log2s2);
+    }
+    float val[R * B];
+    while (lenb[0] > 0) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        // the unit NB - 1 ahead goes into the buffer computed last
+        const int f = (j + NB - 1) % NB;
+        if (f % P == 0) claim(&crl, &clen);
+        rlb[f] = crl;
+        lenb[f] = clen;
+        load_wave_group<R, 1, FMT>(gb[f], lb, crl, clen, pass_lane(f % P), K, log2bs, log2s2);
         __builtin_amdgcn_sched_barrier(0);
-      };
-      while (lena > 0 || lenb > 0) {
-        step(ga, rla, lena);
-        step(gb, rlb, lenb);
-      }
-    } else {
-      // load the group after next into the third buffer, then compute; the
-      // buffers change roles over a round of three steps
-      WaveGroup<R, P, FMT> gc;
-      int rlc = 0, lenc = 0;
-      auto step = [&](WaveGroup<R, P, FMT>& cur, int rl, int len, WaveGroup<R, P, FMT>& fut,
-                      int& rlf, int& lenf) {
-        claim(&rlf, &lenf);
-        load_wave_group<R, P, FMT>(fut, lb, rlf, lenf, wl, K, log2bs, log2s2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(cur, rl, len);
-      };
-      while (lena > 0) {
-        step(ga, rla, lena, gc, rlc, lenc);
-        step(gb, rlb, lenb, ga, rla, lena);
-        step(gc, rlc, lenc, gb, rlb, lenb);
+        constexpr int kPassEntries = 8 * 64;
+        const int q = j % P;
+        if (lenb[j] > 0) {
+          float xsq[B];
+#pragma unroll
+          for (int bb = 0; bb < B; ++bb) xsq[bb] = xs[bb][q];
+          xpass_rows<B, R, FMT>(gb[j], copy_off, s_pairs, s_code2, ob.offset, odd, own_in[q], xsq,
+                                val, q == 0, s_x + q * kPassEntries + lane, P * kPassEntries);
+          if (q == P - 1) finish(val, rlb[j], lenb[j]);
+        }
       }
     }
   }
@@ -1991,13 +2094,13 @@ inline bool xlds_rows_ok(int total_rows) {
 
 // The shared-activation kernel for (B, P): one 1024-thread workgroup per CU
 // at most, each with at least 64 rows.
-template <int B, int R, int P, int NBUF, int FMT>
+template <int B, int R, int P, int NB, int FMT>
 nf4_status xlds_launch(const nf4_gemv_desc* descs, int count, int total_rows, int K, int lbs,
                        int ls2, const uint16_t* code2, hipStream_t st) {
   const int64_t cus = device_cus();
   const int64_t want = (static_cast<int64_t>(total_rows) + 63) / 64;
   const int64_t grid = want < cus ? (want > 0 ? want : 1) : cus;
-  hipLaunchKernelGGL((gemv_xlds_kernel<B, R, P, NBUF, FMT>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((gemv_xlds_kernel<B, R, P, NB, FMT>), dim3(static_cast<uint32_t>(grid)),
                      dim3(kXlThreads), 0, st, descs, count, total_rows, K, lbs, ls2, code2);
   return launch_status();
 }
@@ -2021,13 +2124,13 @@ nf4_status wave_dispatch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   // launches that give every wave two rows or more (see xlds_rows_ok)
   if (descs == nullptr || !xlds_rows_ok(total_rows)) return NF4_EUNSUPPORTED;
   if constexpr (B == 1) {
-    if (P == 2) return xlds_launch<1, 1, 2, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
-    if (P == 3) return xlds_launch<1, 1, 3, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
-    if (P == 4) return xlds_launch<1, 1, 4, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 2) return xlds_launch<1, 2, 2, 4, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 3) return xlds_launch<1, 2, 3, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 4) return xlds_launch<1, 1, 4, 4, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
   } else if constexpr (B == 2) {
-    if (P == 2) return xlds_launch<2, 1, 2, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
-    if (P == 3) return xlds_launch<2, 1, 3, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
-    if (P == 4) return xlds_launch<2, 1, 4, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 2) return xlds_launch<2, 2, 2, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 3) return xlds_launch<2, 2, 3, 3, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+    if (P == 4) return xlds_launch<2, 1, 4, 4, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
   }
   return NF4_EUNSUPPORTED;
 }
@@ -2042,7 +2145,7 @@ nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
   if constexpr (B >= 3) {
     if (descs != nullptr && K % 64 == 0 && K <= kWaveCols && lbs >= 6 &&
         xlds_rows_ok(total_rows))
-      return xlds_launch<B, 1, 1, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
+      return xlds_launch<B, (B <= 4 && FMT != kFmtInt4 ? 2 : 1), 1, 2, FMT>(descs, count, total_rows, K, lbs, ls2, code2, st);
   }
   // Grouped launches (descs != NULL) at batch 1-2 take the wave kernel.  A
   // single matrix takes it only at batch 1, one pass and up to 2^24 weights:

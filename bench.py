@@ -68,6 +68,11 @@ CONTEXT_WORKLOADS = ("dequant_1k", "dequant_4k", "qwen_b1", "llama_b1", "llama_b
 GEMM_WORKLOADS = ("llama_b16", "llama_b64", "llama_b128")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "NF4 dequant & fused GEMV: achieved HBM GB/s and % of MI355X peak (1 GPU)"
+# what the path computes in: the GEMV multiplies bf16 activations by each
+# weight written exactly as two bf16 terms (hi + lo, within 2^-16 of the fp32
+# weight) with fp32 accumulation; the dequant computes in fp32 and rounds once
+DTYPE_NOTE = ("GEMV: bf16 x bf16 products (weight as an exact hi + lo bf16 pair), fp32 "
+              "accumulation, bf16 y; dequant: fp32 arithmetic, RNE to bf16")
 
 
 def log(*a):
@@ -441,44 +446,171 @@ def bench_context(args, dev):
                 step_tflops=wl["flops"] / (ms * 1e-3) / 1e12 if wl["flops"] else None)
 
 
+def dequant_4k_context(dev, reps: int, warmup: int):
+    """The 4096 x 4096 dequant (config 2: with outliers, bs 64 / s2 256) as a
+    single launch per call, bf16 and fp16 outputs, timed from HIP graphs over
+    enough copies of the data to read past the MALL (cold HBM), beside three
+    plain streams of the same size on the same rotation: the library's 1 : 4
+    expand copy probe (read R, write 4 R with streaming stores), torch's
+    elementwise uint8 -> int32 cast (the same R in, 4 R out; an independent
+    kernel), and a device-to-device memcpy (torch copy_) of the same total
+    bytes.  Returns per-launch microseconds and GB/s of each."""
+    import torch
+
+    import synth
+    import w4a16_gemv_amd as nf4
+    cfg = synth.DEQUANT_4K
+    n = cfg.n
+    code2 = nf4.nf4_code2_linear().to(dev)
+    w = synth.weights_device(cfg.seed, n, dev, outliers=cfg.outliers)
+    ws = torch.empty(nf4.load().nf4_quantize_workspace_size(n, 64), dtype=torch.uint8,
+                     device=dev)
+    base = nf4.nf4_quantize(w, 64, 256, code2=code2, workspace=ws)
+    del w, ws
+    nbytes = dequant_bytes(n)
+    nsets = max(2, -(-2 * MALL_BYTES // nbytes))
+    sets = [nf4.NF4Tensor(base.packed.clone(), base.absmax_q.clone(), base.absmax2.clone(),
+                          code2, base.offset, n) for _ in range(nsets)]
+    outs = {dt: [torch.empty(n, dtype=dt, device=dev) for _ in range(nsets)]
+            for dt in (torch.bfloat16, torch.float16)}
+    rb = (n // 2) // 16 * 16                          # the packed bytes (read side)
+    src = [torch.full((rb,), 7, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    dst = [torch.empty(4 * rb, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    dst32 = [torch.empty(rb, dtype=torch.int32, device=dev) for _ in range(nsets)]
+    half = nbytes // 2 // 16 * 16                     # memcpy: read half, write half
+    msrc = [torch.full((half,), 3, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    mdst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    stream = torch.cuda.Stream(dev)
+    runs = {
+        "dequant_bf16": (lambda: [t.dequant(out=o) for t, o in zip(sets, outs[torch.bfloat16])],
+                         nbytes),
+        "dequant_fp16": (lambda: [t.dequant(out=o) for t, o in zip(sets, outs[torch.float16])],
+                         nbytes),
+        "expand_copy_1to4": (lambda: [nf4.probe_expand_copy(a, b) for a, b in zip(src, dst)],
+                             5 * rb),
+        "torch_cast_u8_to_i32": (lambda: [b.copy_(a) for a, b in zip(src, dst32)], 5 * rb),
+        "memcpy_d2d": (lambda: [b.copy_(a) for a, b in zip(msrc, mdst)], 2 * half),
+    }
+    res = {}
+    for name, (fn, nb) in runs.items():
+        g = capture(fn, stream)
+        us = 1e3 * time_graph(g, max(1, reps // nsets), warmup, stream) / nsets
+        res[name] = {"us": round(us, 3), "bytes": nb, "gbs": round(nb / (us * 1e-6) / 1e9, 1)}
+        del g
+    res["rotating_sets"] = nsets
+    res["dequant_bf16"]["frac"] = round(res["dequant_bf16"]["gbs"] / HBM_PEAK_GBS, 4)
+    res["dequant_fp16"]["frac"] = round(res["dequant_fp16"]["gbs"] / HBM_PEAK_GBS, 4)
+    log(f"[bench] dequant 4096^2: bf16 {res['dequant_bf16']['us']:.2f} us, fp16 "
+        f"{res['dequant_fp16']['us']:.2f} us; same-size streams: expand copy "
+        f"{res['expand_copy_1to4']['us']:.2f} us, torch u8->i32 cast "
+        f"{res['torch_cast_u8_to_i32']['us']:.2f} us, memcpy {res['memcpy_d2d']['us']:.2f} us")
+    return res
+
+
+def cpu_info():
+    """Host description for the CPU baseline: logical CPUs (and those this
+    process may run on) and the model name from /proc/cpuinfo."""
+    model = None
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def gemv_outputs_ok(y_gpu_bits, y_ref, S):
+    """The GEMV acceptance rule (as in the tests): each bf16 output must be the
+    round-to-nearest-even bf16 of some real within 2^-14 S of the fp64 oracle
+    value.  Returns (ok, number of outputs outside)."""
+    import numpy as np
+    import torch
+
+    def bf16(v):
+        return torch.from_numpy(np.ascontiguousarray(v, np.float64)).to(torch.bfloat16) \
+            .to(torch.float64).numpy()
+    y = (y_gpu_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    lo, hi = bf16(y_ref - 2.0 ** -14 * S), bf16(y_ref + 2.0 ** -14 * S)
+    bad = int(np.count_nonzero(~((y >= lo) & (y <= hi))))
+    return bad == 0, bad
+
+
 def cpu_baseline(wl, seconds: float):
     """The oracle (plain C, OpenMP over outputs) timed on the host cores on a
     bounded sample of the same workload: the sweep's GEMVs in order, then a
-    slice of the big dequant, until about `seconds` of CPU time is spent."""
+    slice of the big dequant, until about `seconds` of wall time is spent,
+    with all threads; then a smaller sample on one thread.  Every GEMV the
+    oracle computes is also checked against the GPU's output of the last
+    timed step (the acceptance rule of the tests)."""
     import numpy as np
     import torch
 
     import oracle
     threads = oracle.max_threads()
-    done_bytes, elapsed, ngemv = 0, 0.0, 0
-    for mats in wl["layers"]:
-        for (g, t, y, x) in mats:
-            q = oracle.Quantized(t.packed.cpu().numpy(), t.absmax_q.cpu().numpy(),
-                                 t.absmax2.cpu().numpy().view(np.uint16),
-                                 t.code2.cpu().numpy().view(np.uint16), t.offset, t.n)
-            s = time.perf_counter()
-            oracle.gemv(q, g.N, g.K, x.view(torch.int16).cpu().numpy().view(np.uint16))
-            elapsed += time.perf_counter() - s
-            done_bytes += gemv_bytes(g.N, g.K)
-            ngemv += 1
-            if elapsed >= 0.8 * seconds:
-                break
-        if elapsed >= 0.8 * seconds:
-            break
-    big, tb, _ = wl["big"]
-    n_slice = min(big.n, 1 << 24)
-    q = oracle.Quantized(tb.packed[: (n_slice + 1) // 2].cpu().numpy(),
-                         tb.absmax_q[: -(-n_slice // 64)].cpu().numpy(),
-                         tb.absmax2[: -(-n_slice // 16384)].cpu().numpy().view(np.uint16),
-                         tb.code2.cpu().numpy().view(np.uint16), tb.offset, n_slice)
-    s = time.perf_counter()
-    oracle.dequant(q)
-    elapsed += time.perf_counter() - s
-    done_bytes += dequant_bytes(n_slice)
-    return {"value": round(done_bytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads,
+
+    def host_q(t, n=None):
+        n = t.n if n is None else n
+        return oracle.Quantized(t.packed[: (n + 1) // 2].cpu().numpy(),
+                                t.absmax_q[: -(-n // 64)].cpu().numpy(),
+                                t.absmax2[: -(-n // 16384)].cpu().numpy().view(np.uint16),
+                                t.code2.cpu().numpy().view(np.uint16), t.offset, n)
+
+    def run(budget_s, max_gemvs, n_dq, check):
+        done_bytes, elems, elapsed, ngemv, checked, bad = 0, 0, 0.0, 0, 0, 0
+        for mats in wl["layers"]:
+            for (g, t, y, x) in mats:
+                if ngemv >= max_gemvs or elapsed >= budget_s:
+                    break
+                q = host_q(t)
+                xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+                s0 = time.perf_counter()
+                yr, S = oracle.gemv(q, g.N, g.K, xb)
+                elapsed += time.perf_counter() - s0
+                done_bytes += gemv_bytes(g.N, g.K)
+                elems += g.N * g.K
+                ngemv += 1
+                if check:
+                    ok, nbad = gemv_outputs_ok(
+                        y.view(torch.int16).cpu().numpy().view(np.uint16), yr, S)
+                    checked += 1
+                    bad += nbad
+        big, tb, _ = wl["big"]
+        n_slice = min(big.n, n_dq)
+        q = host_q(tb, n_slice)
+        s0 = time.perf_counter()
+        oracle.dequant(q)
+        elapsed += time.perf_counter() - s0
+        done_bytes += dequant_bytes(n_slice)
+        elems += n_slice
+        return dict(bytes=done_bytes, elems=elems, s=elapsed, ngemv=ngemv, n_dq=n_slice,
+                    checked=checked, bad=bad)
+
+    full = run(0.8 * seconds, 224, 1 << 24, check=True)
+    oracle.set_threads(1)
+    try:
+        one = run(0.15 * seconds, 8, 1 << 22, check=False)
+    finally:
+        oracle.set_threads(threads)
+    return {"value": round(full["bytes"] / full["s"] / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"first {ngemv} of the 224 sweep GEMVs (fp64 oracle GEMV) + the first "
-                      f"{n_slice} elements of the 8192x28672 dequant; {elapsed:.1f} s of wall time"}
+            "elements_per_s": round(full["elems"] / full["s"], 1),
+            "sample": f"first {full['ngemv']} of the 224 sweep GEMVs (fp64 oracle GEMV, all "
+                      f"rows) + the first {full['n_dq']} elements of the 8192x28672 dequant; "
+                      f"{full['s']:.1f} s of wall time",
+            "gemv_outputs_checked": {"gemvs": full["checked"],
+                                     "outputs_outside_tolerance": full["bad"]},
+            "single_thread": {"value": round(one["bytes"] / one["s"] / 1e9, 4), "unit": "GB/s",
+                              "elements_per_s": round(one["elems"] / one["s"], 1), "cores": 1,
+                              "sample": f"first {one['ngemv']} sweep GEMVs + the first "
+                                        f"{one['n_dq']} dequant elements; {one['s']:.1f} s"},
+            **cpu_info()}
 
 
 def main():
@@ -524,7 +656,7 @@ def main():
             "metric": METRIC, "value": round(r["value"], 1), "unit": "GB/s", "n_gpus": 1,
             "steps": r["steps"], "warmup": args.warmup, "ms_per_step": round(r["ms"], 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "bf16" if args.workload in GEMM_WORKLOADS else "f32",
+            "dtype": "bf16", "dtype_note": DTYPE_NOTE,
             "data": "synthetic",
             "config": {"workload": args.workload, "batch": r["batch"], "blocksize": args.blocksize,
                        "s2_blocksize": None if args.workload.endswith(("_absmax32", "_int4"))
@@ -656,6 +788,10 @@ def main():
         f"{launches} launches); dequant {dq_ms * 1e3:.1f} us ({dq_gbs:.0f} GB/s); "
         f"{other} schedule step {other_ms:.3f} ms")
 
+    dq4k = None
+    if not args.no_context and fmt == "double":
+        dq4k = dequant_4k_context(dev, max(200, args.steps), 20)
+
     cpu = None
     if not args.no_cpu_baseline and fmt == "double":
         cpu = cpu_baseline(wl, args.cpu_seconds)
@@ -672,7 +808,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
+        "dtype_note": DTYPE_NOTE,
         "data": "synthetic",
         "config": {
             "workload": "decode_sweep_7b_32layers_224gemv_b1+dequant_8192x28672"
@@ -708,6 +845,7 @@ def main():
             "frac_of_copy_ceiling": None if ceiling is None else
             round(dq_gbs / ceiling["expand_copy_1to4"]["gbs"], 4)},
         "ceiling": ceiling,
+        "dequant_4096x4096": dq4k,
         f"{other}_schedule": None if args.no_context else {
             "ms_per_step": round(other_ms, 4),
             "value": round(step_bytes / (other_ms * 1e-3) / 1e9, 1)},

@@ -1186,6 +1186,7 @@ struct SchedRegion {
   unsigned* claims;  // claims made on this region (kept by the workspace)
   unsigned* done;    // waves of this region that have finished
   int lo, hi;        // rows of the region
+  int dyn_lo;        // first row handed out in chunks (after the static shares)
   int W;             // waves serving the region
 };
 constexpr int kSchedStride = 64;  // uint32 per region (256 bytes): counters on separate lines
@@ -1211,13 +1212,13 @@ __device__ __forceinline__ int next_group_dyn(RowCursor& c, int& r_end, uint32_t
     // wait for every load issued before the atomic
     uint32_t cl;
     asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(cl) : "v"(claim));
-    const uint32_t ch = static_cast<uint32_t>(sr.W) + cl;
+    const uint32_t ch = cl;
     const uint32_t nch =
-        (static_cast<uint32_t>(sr.hi - sr.lo) + static_cast<uint32_t>(C) - 1u) >> log2C;
+        (static_cast<uint32_t>(sr.hi - sr.dyn_lo) + static_cast<uint32_t>(C) - 1u) >> log2C;
     if (ch >= nch) {
       c.r = r_end = sr.hi;
     } else {
-      c.r = sr.lo + static_cast<int>(ch << log2C);
+      c.r = sr.dyn_lo + static_cast<int>(ch << log2C);
       r_end = min(c.r + C, sr.hi);
       if (r_end < sr.hi) claim_chunk(claim, sr.claims, lane);
     }
@@ -1228,7 +1229,8 @@ __device__ __forceinline__ int next_group_dyn(RowCursor& c, int& r_end, uint32_t
 template <int B, int R, int P, int WPE, bool DYN, int FMT = kFmtDouble, bool REG = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemv_wave_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
-    int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2, unsigned* sched, int C) {
+    int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2, unsigned* sched, int C,
+    int S) {
   static_assert(R * B <= 4, "one pair or quad reduction per group");
   const int log2C = C > 0 ? __builtin_ctz(static_cast<unsigned>(C)) : 0;  // C is a power of two
   __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
@@ -1267,9 +1269,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     sr.W = waves * ((static_cast<int>(gridDim.x) - 1 - region) / nreg + 1);
     const int wr = (static_cast<int>(blockIdx.x) / nreg) * waves + wave;  // index in the region
     const uint32_t rows = static_cast<uint32_t>(sr.hi - sr.lo);
-    const uint32_t first = static_cast<uint32_t>(wr) << log2C;  // wr < 2^13, C <= 32
+    // a contiguous static share of S rows per wave first (wr < 2^13, S < 2^18),
+    // then chunks of C from the rest of the region
+    const uint32_t first = static_cast<uint32_t>(wr) * static_cast<uint32_t>(S);
+    const uint32_t shares = static_cast<uint32_t>(sr.W) * static_cast<uint32_t>(S);
+    sr.dyn_lo = sr.lo + static_cast<int>(shares < rows ? shares : rows);
     r_begin = sr.lo + static_cast<int>(first < rows ? first : rows);
-    r_end = sr.lo + static_cast<int>(first + C < rows ? first + C : rows);
+    r_end = sr.lo + static_cast<int>(first + S < rows ? first + S : rows);
     if (r_end < sr.hi) claim_chunk(claim, sr.claims, lane);
   } else {
     split_rows(static_cast<uint32_t>(total_rows), gridDim.x * static_cast<uint32_t>(waves),
@@ -2031,6 +2037,21 @@ void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, i
                      dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2);
 }
 
+// Rows of the contiguous static share each wave takes before it claims
+// chunks of C: half its even share, rounded down to whole chunks (at least
+// one).  Claimed chunks lie far apart in the row space, so nearly every one
+// starts another matrix, and a matrix with other activations makes the wave
+// reload them behind a full wait; a contiguous share crosses at most one or
+// two matrices.  The chunked other half still evens out the waves' unequal
+// progress.  Measured on the 192-matrix K = 4096 sweep launch with per-layer
+// activations (two boxes, two runs each): static shares of 1/4, 2/5, 1/2,
+// 11/20, 3/5 and 3/4 against one chunk (the previous scheme): 1/2 best, 442
+// -> 432 us and 433 -> 423 us; 3/4 slower than one chunk.
+inline int dyn_static_rows(int64_t rows_per_wave, int C) {
+  const int64_t s = rows_per_wave / 2 / C * C;
+  return s > C ? static_cast<int>(s) : C;
+}
+
 // The wave-per-row kernel for (B, P): rows per group and waves per SIMD are
 // set by registers: the activations take 32 B P VGPRs, each row group 10 R P,
 // and three groups are in flight.  With a scheduling workspace, four waves per
@@ -2050,10 +2071,11 @@ nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, 
   if (WPE == 4 && want >= 4 * cus) grid = want < 2 * cus ? want : 2 * cus;
   const int64_t rows_per_wave = (static_cast<int64_t>(total_rows) + grid * 8 - 1) / (grid * 8);
   const bool dyn = WPE == 4 && sched != nullptr && rows_per_wave >= 64;
-  int C = 0;
+  int C = 0, S = 0;
   if (dyn) {
     C = 4;
     while (C < 32 && C * 2 * 16 <= rows_per_wave) C *= 2;
+    S = dyn_static_rows(rows_per_wave, C);
   }
   // regular shapes (see load_wave_group): whole 4096-column passes, whole
   // blocks per row, and blocks per row and s2 dividing one into the other
@@ -2070,16 +2092,16 @@ nf4_status wave_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, 
                        kSchedRegions * kSchedStride);
   if (reg && dyn)
     hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, true, FMT, true>), g, blk, 0, st, descs,
-                       single, count, total_rows, K, lbs, ls2, code2, sc, C);
+                       single, count, total_rows, K, lbs, ls2, code2, sc, C, S);
   else if (reg)
     hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, false, FMT, true>), g, blk, 0, st, descs,
-                       single, count, total_rows, K, lbs, ls2, code2, sc, C);
+                       single, count, total_rows, K, lbs, ls2, code2, sc, C, S);
   else if (dyn)
     hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, true, FMT, false>), g, blk, 0, st, descs,
-                       single, count, total_rows, K, lbs, ls2, code2, sc, C);
+                       single, count, total_rows, K, lbs, ls2, code2, sc, C, S);
   else
     hipLaunchKernelGGL((gemv_wave_kernel<B, R, P, WPE, false, FMT, false>), g, blk, 0, st,
-                       descs, single, count, total_rows, K, lbs, ls2, code2, sc, C);
+                       descs, single, count, total_rows, K, lbs, ls2, code2, sc, C, S);
   return launch_status();
 }
 

@@ -697,11 +697,18 @@ __device__ __forceinline__ int next_group(RowCursor& c, int r_end, const RowBegi
 // computes the current one.  All loads and the y stores are branch-free
 // buffer operations.
 // ---------------------------------------------------------------------------
-template <int B, int R, int NW, int WPE, int FMT = kFmtDouble>
+// SINGLE: one matrix given by value (descs NULL, count 1), known at compile
+// time: no descriptor walk, no matrix or activation switches, so the loop
+// keeps far less scalar state.
+template <int B, int R, int NW, int WPE, int FMT = kFmtDouble, bool SINGLE = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemv_stream_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
     int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2) {
   constexpr int nw = NW;  // waves per team: one per 2048-column slab of K
+  if constexpr (SINGLE) {
+    descs = nullptr;
+    count = 1;
+  }
   __shared__ uint2 s_pairs[256 * kPairCopies];  // 64 KiB decode table
   __shared__ float s_code2[256];
   __shared__ float s_red[2][8][R * B];
@@ -759,23 +766,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // workgroup maximum: every wave runs that many iterations
   {
     int ng = 0;
-    for (int mm = cur_c.m; mm < count && rbeg(mm) < r_end; ++mm) {
-      const int lo = max(r_begin, rbeg(mm));
-      const int hi = min(r_end, rbeg(mm + 1));
-      if (hi > lo) ng += (hi - lo + R - 1) / R;
+    if constexpr (SINGLE) {
+      ng = (r_end - r_begin + R - 1) / R;
+    } else {
+      for (int mm = cur_c.m; mm < count && rbeg(mm) < r_end; ++mm) {
+        const int lo = max(r_begin, rbeg(mm));
+        const int hi = min(r_end, rbeg(mm + 1));
+        if (hi > lo) ng += (hi - lo + R - 1) / R;
+      }
     }
     if (lane == 0 && slab == 0 && in_team) atomicMax(&s_iters, ng);
   }
+  // the next group of the team's range: a single matrix needs no cursor walk
+  auto advance = [&](int* m_out, int* rl_out) {
+    if constexpr (SINGLE) {
+      const int len = cur_c.r < r_end ? min(R, r_end - cur_c.r) : 0;
+      *m_out = len > 0 ? 0 : -1;
+      *rl_out = cur_c.r;
+      cur_c.r += len;
+      return len;
+    } else {
+      return next_group<R>(cur_c, r_end, rbeg, count, m_out, rl_out);
+    }
+  };
 
   // the first two groups (prefetch depth 2: the loads of group i + 2 are
   // issued before group i is computed).  Scalar state: the load-side buffers
   // of the newest group's matrix (mL), and the output side of the two groups
   // in compute order; descriptors are re-read only when the matrix changes.
   int m0, rl0, m1, rl1;
-  int len0 = next_group<R>(cur_c, r_end, rbeg, count, &m0, &rl0);
+  int len0 = advance(&m0, &rl0);
   m0 = __builtin_amdgcn_readfirstlane(m0);
-  const nf4_gemv_desc d0 = open_desc<FMT>(descs, single, m0, len0, rbeg, K);
-  int len1 = next_group<R>(cur_c, r_end, rbeg, count, &m1, &rl1);
+  // a single matrix: the whole team range's descriptor (valid for any length)
+  const nf4_gemv_desc d0 = SINGLE ? open_desc<FMT>(nullptr, single, 0, total_rows, rbeg, K)
+                                  : open_desc<FMT>(descs, single, m0, len0, rbeg, K);
+  int len1 = advance(&m1, &rl1);
   m1 = __builtin_amdgcn_readfirstlane(m1);
   LoadBufs lb0 = load_bufs<FMT>(d0, K, log2bs, log2s2);
   OutBufs ob0 = out_bufs<B>(d0);
@@ -791,7 +816,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   int mL = m0;            // matrix of lbL
   LoadBufs lbL = lb0;
   OutBufs ob1 = ob0;
-  if (len1 > 0 && m1 != m0) {
+  if (!SINGLE && len1 > 0 && m1 != m0) {
     const nf4_gemv_desc d1 = open_desc<FMT>(descs, single, m1, len1, rbeg, K);
     lbL = load_bufs<FMT>(d1, K, log2bs, log2s2);
     ob1 = out_bufs<B>(d1);
@@ -827,10 +852,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   int buf = 0;
   auto step = [&](RowGroup<R, FMT>& cur, RowGroup<R, FMT>& fut) {
     int m2, rl2;
-    const int len2 = next_group<R>(cur_c, r_end, rbeg, count, &m2, &rl2);
+    const int len2 = advance(&m2, &rl2);
     m2 = __builtin_amdgcn_readfirstlane(m2);
     OutBufs ob2 = ob1;
-    if (len2 > 0 && m2 != mL) {
+    if (!SINGLE && len2 > 0 && m2 != mL) {
       const nf4_gemv_desc d2 = open_desc<FMT>(descs, single, m2, len2, rbeg, K);
       lbL = load_bufs<FMT>(d2, K, log2bs, log2s2);
       ob2 = out_bufs<B>(d2);
@@ -906,7 +931,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     buf ^= 1;
     // the next group starts a new matrix: fetch its activations now that the
     // current ones are no longer needed
-    if (len1 > 0 && m1 != m0) {
+    if (!SINGLE && len1 > 0 && m1 != m0) {
       load_x<B>(xr, x_buf<B>(open_desc<FMT>(descs, single, m1, len1, rbeg, K), K), lo, K);
       // drain here (rare: once per matrix change) so that the loads of this
       // branch are not assumed outstanding on the common path, where they
@@ -2032,9 +2057,14 @@ template <int B, int NW, int FMT>
 void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, int count,
                       int total_rows, int K, int lbs, int ls2, const uint16_t* code2,
                       int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>(), NW, stream_wpe<B>(), FMT>),
-                     dim3(static_cast<uint32_t>(grid)),
-                     dim3(512), 0, st, descs, single, count, total_rows, K, lbs, ls2, code2);
+  if (descs == nullptr)
+    hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>(), NW, stream_wpe<B>(), FMT, true>),
+                       dim3(static_cast<uint32_t>(grid)), dim3(512), 0, st, descs, single, 1,
+                       total_rows, K, lbs, ls2, code2);
+  else
+    hipLaunchKernelGGL((gemv_stream_kernel<B, stream_rows<B>(), NW, stream_wpe<B>(), FMT>),
+                       dim3(static_cast<uint32_t>(grid)), dim3(512), 0, st, descs, single, count,
+                       total_rows, K, lbs, ls2, code2);
 }
 
 // Rows of the contiguous static share each wave takes before it claims

@@ -28,7 +28,8 @@ milliseconds of load while its clocks settle.
 `sweep` is the headline): sweep_absmax32 / sweep_int4 (the same sweep and big
 dequant in the single-level and INT4 formats, grouped launches of
 nf4_gemv_grouped_absmax32 / int4_gemv_grouped; no CPU baseline), dequant_1k /
-dequant_4k (1024^2 and 4096^2 bf16 dequant), qwen_b1 (the 7 Qwen2.5-1.5B-shaped GEMVs), llama_b1 / llama_b4 /
+dequant_4k (1024^2 and 4096^2 bf16 dequant), qwen_b1 (the 7 Qwen2.5-1.5B-shaped GEMVs),
+qwen_b1_grouped (the same 7 as 4 launches: q/k/v and gate/up grouped), llama_b1 / llama_b4 /
 llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8), llama_b16 / llama_b64
 / llama_b128 (the same 3 matrices times 16, 64, 128 activation rows through
 nf4_gemm, the matrix-core product; roofline against the bf16 MFMA peak), and
@@ -64,6 +65,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 CONTEXT_WORKLOADS = ("dequant_1k", "dequant_4k", "qwen_b1", "llama_b1", "llama_b4", "llama_b8")
+# the Qwen2.5-1.5B layer in four launches: q/k/v grouped, o, gate/up grouped,
+# down (double-quantized format)
+GROUPED_WORKLOADS = ("qwen_b1_grouped",)
+QWEN_LAUNCHES = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 # batched products on the matrix cores (nf4_gemm), double-quantized format only
 GEMM_WORKLOADS = ("llama_b16", "llama_b64", "llama_b128")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -330,6 +335,39 @@ def build_context(dev, name, bs=None):
                     dominant=f"dequant_vec_kernel ({cfg.rows}x{cfg.cols}"
                              f"{', fp32 absmax' if single else ''}{', int4' if int4 else ''})",
                     dominant_bytes=set_bytes, dominant_flops=0)
+
+    if name == "qwen_b1_grouped":
+        gemvs, batch = synth.QWEN_GEMVS, 1
+        xs = {K: synth.activations_device(synth.QWEN_X_SEED, 1, K, dev)
+              for K in {g.K for g in gemvs}}
+        base = {g.name.split("_")[1]: (g, encode(g.seed, g.N * g.K)) for g in gemvs}
+        set_bytes = sum(gv_bytes(g.N, g.K, 1) for g in gemvs)
+        nsets = max(2, -(-2 * MALL_BYTES // set_bytes))
+        sets = []
+        for _ in range(nsets):
+            launches = []
+            for sel in QWEN_LAUNCHES:
+                items = []
+                for nm in sel:
+                    g, t = base[nm]
+                    items.append((clone(t), g.N, xs[g.K],
+                                  torch.empty(1, g.N, dtype=torch.bfloat16, device=dev)))
+                launches.append(nf4.GemvGroup(items, items[0][0].n // items[0][1]))
+            sets.append(launches)
+        dom = 2   # gate/up, the largest launch
+        dom_rows = sum(base[nm][0].N for nm in QWEN_LAUNCHES[dom])
+        K_dom = base["gate"][0].K
+
+        def run(st, dominant_only=False):
+            for i, grp in enumerate(st):
+                if not dominant_only or i == dom:
+                    grp.launch()
+        return dict(sets=sets, step_bytes=set_bytes, flops=sum(2 * g.N * g.K for g in gemvs),
+                    launches=len(QWEN_LAUNCHES), run=run, batch=1, blocksize=bs,
+                    dominant=f"nf4_gemv_grouped gate+up {dom_rows}x{K_dom} batch 1",
+                    dominant_bytes=sum(gv_bytes(base[nm][0].N, K_dom, 1)
+                                       for nm in QWEN_LAUNCHES[dom]),
+                    dominant_flops=2 * dom_rows * K_dom)
 
     if base_name == "qwen_b1":
         gemvs, batch, xseed = synth.QWEN_GEMVS, 1, synth.QWEN_X_SEED
@@ -620,7 +658,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--schedule", choices=("stream", "layered"), default="stream")
     ap.add_argument("--workload", default="sweep",
-                    choices=SWEEP_WORKLOADS + CONTEXT_WORKLOADS + GEMM_WORKLOADS
+                    choices=SWEEP_WORKLOADS + CONTEXT_WORKLOADS + GEMM_WORKLOADS + GROUPED_WORKLOADS
                     + tuple(w + "_absmax32" for w in CONTEXT_WORKLOADS)
                     + tuple(w + "_int4" for w in CONTEXT_WORKLOADS))
     ap.add_argument("--blocksize", type=int, default=None,

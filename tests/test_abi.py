@@ -354,3 +354,37 @@ def test_gemv_desc_check_other_cases(lib):
     assert _check(lib, t, total, 4096, 3)[0] == 1           # unknown format
     assert _check(lib, None, 0, 4096) == (0, -1)            # empty table
     assert lib.nf4_gemv_desc_check(None, 2, 10, 4096, 0, None) == 1
+
+
+def test_hot_path_kernels_do_not_spill():
+    """The build's resource table (from the compiler's kernel-resource-usage
+    remarks) lists every hot-path instance with zero scratch; the build itself
+    refuses a spilling one, so this checks the table is there and complete."""
+    from w4a16_gemv_amd import build
+    if not os.path.exists(build.RESOURCES):
+        pytest.skip("kernel_resources.txt not written (library built elsewhere)")
+    rows = {}
+    with open(build.RESOURCES, encoding="utf-8") as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            vgpr, agpr, scratch, occ, lds, name = line.split(None, 5)
+            rows[name.strip()] = int(scratch)
+    for hot in build.NO_SPILL:
+        hits = [n for n in rows if hot in n]
+        assert hits, f"{hot} missing from the resource table"
+        assert all(rows[n] == 0 for n in hits), f"{hot} spills"
+
+
+def test_resource_remarks_are_parsed():
+    from w4a16_gemv_amd import build
+    text = ("x.hip:1:1: remark: Function Name: _Z3foov [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     VGPRs: 108 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     AGPRs: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     Occupancy [waves/SIMD]: 4 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     LDS Size [bytes/block]: 95248 [-Rpass-analysis=kernel-resource-usage]\n")
+    res = build.parse_resources(text)
+    (name, r), = res.items()
+    assert name in ("foo()", "_Z3foov")
+    assert r == {"vgpr": 108, "agpr": 0, "scratch": 16, "occupancy": 4, "lds": 95248}

@@ -6,6 +6,9 @@ Flags:
                             fp32 on its own; GEMV code uses explicit fmaf.
   -target-feature -packed-fp32-ops
                             no packed fp32 VALU instructions.
+The compiler's kernel-resource-usage remarks are parsed into
+kernel_resources.txt (registers, scratch, occupancy, LDS per kernel); the
+build fails when an instance on the measured hot path (NO_SPILL) spills.
 """
 from __future__ import annotations
 
@@ -33,6 +36,67 @@ HIPCC_FLAGS = [
 ]
 
 
+# Kernel instances on the measured hot path that must keep everything in
+# registers (a spill to scratch memory inside their loops costs bandwidth):
+# the decode-sweep GEMVs and the dequant.  The build fails if one spills.
+NO_SPILL = (
+    "gemv_wave_kernel<1, 2, 1, 4, true, 0, true>",
+    "gemv_wave_kernel<1, 2, 1, 4, false, 0, true>",
+    "gemv_xlds_kernel<1, 2, 3, 3, 0>",
+    "gemv_xlds_kernel<1, 2, 3, 3, 1>",
+    "gemv_xlds_kernel<1, 2, 3, 3, 2>",
+    "dequant_vec_kernel<0, 4, 0>",
+    "dequant_vec_kernel<1, 4, 0>",
+)
+RESOURCES = os.path.join(PKG, "kernel_resources.txt")
+REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def parse_resources(text: str) -> dict:
+    """Kernel name -> {VGPRs, AGPRs, ScratchSize, Occupancy, LDS} from the
+    compiler's kernel-resource-usage remarks (names demangled by c++filt)."""
+    import re
+    out, cur = {}, None
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
+            "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            out.setdefault(cur, {})
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                      r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]): (\d+)", line)
+        if m and cur:
+            out[cur][keys[m.group(1)]] = int(m.group(2))
+    names = list(out)
+    if names and shutil.which("c++filt"):
+        res = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True)
+        demangled = res.stdout.splitlines()
+        if len(demangled) == len(names):
+            out = {d: out[n] for n, d in zip(names, demangled)}
+    return out
+
+
+def write_resources(res: dict) -> list:
+    """Writes the per-kernel table to kernel_resources.txt; returns the hot
+    instances (NO_SPILL) that use scratch."""
+    rows = sorted(res.items())
+    with open(RESOURCES, "w", encoding="utf-8") as f:
+        f.write("# per-kernel resources from the compiler (hipcc -Rpass-analysis="
+                "kernel-resource-usage)\n# vgpr agpr scratch[B/lane] occupancy[waves/SIMD] "
+                "lds[B/block]  kernel\n")
+        for name, r in rows:
+            f.write(f"{r.get('vgpr', -1):4d} {r.get('agpr', -1):4d} {r.get('scratch', -1):5d} "
+                    f"{r.get('occupancy', -1):2d} {r.get('lds', -1):7d}  {name}\n")
+    bad = []
+    for hot in NO_SPILL:
+        for name, r in rows:
+            if hot in name and r.get("scratch", 0) > 0:
+                bad.append(f"{name}: {r['scratch']} bytes of scratch per lane")
+    return bad
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -49,7 +113,7 @@ def build(verbose: bool = False) -> str:
     tmp = tempfile.mkdtemp(prefix="nf4_build_")
     try:
         objs = [os.path.join(tmp, os.path.basename(src) + ".o") for src in SRCS]
-        cmds = [[hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-c", "-o", obj, src]
+        cmds = [[hipcc(), *HIPCC_FLAGS, REMARKS, "-I", INCLUDE, "-c", "-o", obj, src]
                 for src, obj in zip(SRCS, objs)]
         if verbose:
             for cmd in cmds:
@@ -61,6 +125,17 @@ def build(verbose: bool = False) -> str:
             if res.returncode != 0:
                 sys.stderr.write(res.stdout + res.stderr)
                 raise RuntimeError("hipcc failed to build libnf4.so")
+        resources = {}
+        for res in results:
+            resources.update(parse_resources(res.stderr))
+        spills = write_resources(resources)
+        if verbose:
+            spilling = sum(1 for r in resources.values() if r.get("scratch", 0) > 0)
+            print(f"{len(resources)} kernels, {spilling} with scratch; table in {RESOURCES}",
+                  flush=True)
+        if spills:
+            raise RuntimeError("hot-path kernel instances spill to scratch:\n  " +
+                               "\n  ".join(spills))
         link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
         if verbose:
             print(" ".join(link), flush=True)

@@ -104,23 +104,56 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libnf4)")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, cached: bool = False) -> str:
     """Compile each source to an object in parallel (one hipcc per file), then
-    link the shared library; the result replaces LIB atomically."""
+    link the shared library; the result replaces LIB atomically.  cached:
+    reuse the object of a source whose content, headers and flags are
+    unchanged since it was last compiled (off by default: a build compiles
+    every source)."""
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
 
+    import hashlib
     tmp = tempfile.mkdtemp(prefix="nf4_build_")
+    # objects (and their compiler remarks) are kept per content hash of the
+    # source, every header and the flags, so an unchanged source is not
+    # recompiled
+    cache = os.path.join(tempfile.gettempdir(), "nf4_build_cache")
+    os.makedirs(cache, exist_ok=True)
+    headers = b""
+    for d in (os.path.join(PKG, "csrc"), INCLUDE):
+        for fn in sorted(os.listdir(d)):
+            if fn.endswith(".h"):
+                with open(os.path.join(d, fn), "rb") as f:
+                    headers += fn.encode() + f.read()
     try:
-        objs = [os.path.join(tmp, os.path.basename(src) + ".o") for src in SRCS]
-        cmds = [[hipcc(), *HIPCC_FLAGS, REMARKS, "-I", INCLUDE, "-c", "-o", obj, src]
-                for src, obj in zip(SRCS, objs)]
-        if verbose:
-            for cmd in cmds:
-                print(" ".join(cmd), flush=True)
+        objs, cmds, keys = [], [], []
+        for src in SRCS:
+            with open(src, "rb") as f:
+                h = hashlib.sha256(f.read() + headers + " ".join(HIPCC_FLAGS).encode() +
+                                   hipcc().encode()).hexdigest()[:24]
+            keys.append(os.path.join(cache, f"{os.path.basename(src)}.{h}"))
+            objs.append(os.path.join(tmp, os.path.basename(src) + ".o"))
+            cmds.append([hipcc(), *HIPCC_FLAGS, REMARKS, "-I", INCLUDE, "-c", "-o", objs[-1], src])
+
+        def compile_one(i):
+            key = keys[i]
+            if cached and os.path.exists(key + ".o") and os.path.exists(key + ".remarks"):
+                shutil.copyfile(key + ".o", objs[i])
+                with open(key + ".remarks", encoding="utf-8") as f:
+                    return subprocess.CompletedProcess(cmds[i], 0, "", f.read())
+            if verbose:
+                print(" ".join(cmds[i]), flush=True)
+            res = subprocess.run(cmds[i], capture_output=True, text=True)
+            if res.returncode == 0:
+                shutil.copyfile(objs[i], key + ".o.tmp")
+                os.replace(key + ".o.tmp", key + ".o")
+                with open(key + ".remarks", "w", encoding="utf-8") as f:
+                    f.write(res.stderr)
+            return res
+
         with ThreadPoolExecutor(len(cmds)) as pool:
-            results = list(pool.map(lambda c: subprocess.run(c, capture_output=True, text=True),
-                                    cmds))
+            results = list(pool.map(compile_one, range(len(cmds))))
         for res in results:
             if res.returncode != 0:
                 sys.stderr.write(res.stdout + res.stderr)
@@ -150,4 +183,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, cached="--cached" in sys.argv))

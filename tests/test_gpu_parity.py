@@ -307,6 +307,41 @@ def test_gemv_grouped_matches_oracle(K, shapes, batch):
         assert ok, f"grouped N={N} K={K}: worst {worst:.3g}"
 
 
+@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("K,N", [(4096, 4096), (4096, 11008), (11008, 4096), (1536, 256)])
+def test_gemv_group_of_one_matrix(K, N, batch):
+    """A group of one matrix launches through nf4_gemv (its descriptor in the
+    kernel arguments): the same bits as nf4_gemv called directly, within
+    tolerance of the oracle; nf4_gemv_grouped on the group's uploaded table
+    (the grouped kernels) meets the oracle too."""
+    qs, items = _group_case([(N, 690)], K, batch, 795)
+    grp = nf4.GemvGroup(items, K)
+    assert grp.single is not None and grp.sched is None
+    (q, _, xb, base), (w, _, x, yv) = qs[0], items[0]
+    print(f"[gemv_group_of_one] K={K} N={N} B={batch}", flush=True)
+    yv.fill_(float("nan"))
+    grp.launch()
+    torch.cuda.synchronize()
+    y_group = G.bits16(yv).copy()
+    yv.fill_(float("nan"))
+    w.gemv(N, K, x, yv)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.bits16(yv), y_group), "group of one differs from nf4_gemv"
+    yv.fill_(float("nan"))
+    st = nf4.load().nf4_gemv_grouped(grp.table.data_ptr(), 1, N, K, 64, 256,
+                                     w.code2.data_ptr(), batch, None, 0,
+                                     torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    y_grouped = G.bits16(yv).copy()
+    assert G.guards_intact(base, batch * N), "write outside y"
+    yr, S = oracle.gemv(q, N, K, xb)
+    for name, bits in (("group of one", y_group), ("grouped kernels", y_grouped)):
+        y = G.bf16_to_f64(bits).reshape(batch, N)
+        ok, worst = G.gemv_within_tolerance(y, yr, S)
+        assert ok, f"{name} N={N} K={K} B={batch}: worst {worst:.3g}"
+
+
 def test_gemv_grouped_dynamic_schedule():
     """Enough rows (>= 64 per wave) for chunked row distribution: the
     results match the oracle, are bit-identical to the fixed split, stay the

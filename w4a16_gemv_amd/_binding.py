@@ -503,6 +503,14 @@ class GemvGroup:
     which schedules rows in chunks with the library's own per-GPU scratch
     (no workspace tensor; launches on one GPU must not overlap in time).
     The table is checked on the host by nf4_gemv_desc_check before upload.
+
+    A group of one matrix at batch 1-2 whose rows are too few for chunked
+    scheduling launches through the format's single-matrix entry point
+    (nf4_gemv, nf4_gemv_absmax32, int4_gemv): its kernels take the descriptor
+    as a kernel argument, so their first weight loads do not wait for the
+    descriptor table to be read from memory (about 0.8 us per launch).  Such
+    a group's results come from the single-matrix kernels, within the same
+    tolerance (the bits can differ from a grouped launch of the same matrix).
     """
 
     def __init__(self, items, K: int, dynamic: bool = True, noalloc: bool = False):
@@ -581,14 +589,25 @@ class GemvGroup:
         self.noalloc = bool(noalloc)
         if self.noalloc and self.kind is not NF4Tensor:
             raise ValueError("noalloc grouped launches take NF4Tensor items only")
+        # chunked scheduling needs 64 rows per wave of a full grid (two
+        # 512-lane workgroups per compute unit)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        self.single = None
+        if len(self.items) == 1 and not self.noalloc and self.batch <= 2 and (
+                not dynamic or self.total_rows < 64 * 16 * cus):
+            self.single = self.items[0]
         self.sched = None
-        if dynamic and not self.noalloc:
+        if dynamic and not self.noalloc and self.single is None:
             nbytes = int(load().nf4_gemv_sched_size())
             self.sched = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=dev)
             if self.sched.data_ptr() % 256:
                 raise RuntimeError("scheduling workspace is not 256-byte aligned")
 
     def launch(self) -> None:
+        if self.single is not None:
+            w, N, x, y = self.single
+            w.gemv(N, self.K, x, y)
+            return
         sp, sn = (self.sched.data_ptr(), self.sched.numel() * 4) if self.sched is not None else (None, 0)
         lib = load()
         if self.kind is Int4Tensor:

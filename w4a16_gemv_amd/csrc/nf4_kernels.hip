@@ -1204,9 +1204,10 @@ __device__ __forceinline__ void wave_rows(const WaveGroup<R, P, FMT>& g, const u
 // the region starts with chunk w, and the chunks after the first W go to
 // whichever wave claims them from the region's counter.  Each wave claims one
 // chunk ahead (the claim's result is read only when the current chunk is
-// done), so the atomic's latency is hidden.  Waves on one SIMD are not issued
-// fairly (the older wave wins), so a static split leaves the younger waves
-// with the tail; claiming evens out the finishing times.
+// done).  Waves on one SIMD are not issued fairly (the older wave wins), so a
+// static split leaves the younger waves with the tail; the rotating wave
+// priority (rotate_priority) evens out most of it and the claimed chunks the
+// rest.
 struct SchedRegion {
   unsigned* claims;  // claims made on this region (kept by the workspace)
   unsigned* done;    // waves of this region that have finished
@@ -1249,6 +1250,25 @@ __device__ __forceinline__ int next_group_dyn(RowCursor& c, int& r_end, uint32_t
     }
   }
   return next_group<R>(c, r_end, rbeg, count, m_out, rl_out);
+}
+
+// Rotating wave priority.  A SIMD issues its ready waves oldest first, so
+// with equal priorities the younger waves of a SIMD fall behind and finish
+// last.  Each round of three row groups a wave moves its priority one level
+// (0-3) along a cycle that starts at its wave slot on the SIMD, so the waves
+// of a SIMD take turns at the top and progress evenly.  (A wave's issue
+// priority only: the queue and its streams keep the default priority.)
+constexpr int kHwRegWaveSlot = 4 | (0 << 6) | (3 << 11);  // HW_ID bits 3:0, the wave's slot
+__device__ __forceinline__ void rotate_priority(int round, int slot) {
+  const int lvl = __builtin_amdgcn_readfirstlane((round + slot) & 3);
+  if (lvl == 0)
+    __builtin_amdgcn_s_setprio(0);
+  else if (lvl == 1)
+    __builtin_amdgcn_s_setprio(1);
+  else if (lvl == 2)
+    __builtin_amdgcn_s_setprio(2);
+  else
+    __builtin_amdgcn_s_setprio(3);
 }
 
 template <int B, int R, int P, int WPE, bool DYN, int FMT = kFmtDouble, bool REG = false>
@@ -1472,8 +1492,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // Whole rounds of three steps (see gemv_stream_kernel for why no step ends
   // the loop); with DYN the number of groups is not known in advance, and
   // the at most two empty steps of the last round skip their work.
+  const int slot = static_cast<int>(__builtin_amdgcn_s_getreg(kHwRegWaveSlot));
   if constexpr (DYN) {
-    while (len0 > 0) {
+    for (int it = 0; len0 > 0; ++it) {
+      rotate_priority(it, slot);
       step(g0, g2);
       step(g1, g0);
       step(g2, g1);
@@ -1492,6 +1514,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   } else {
     const int rounds = iters / 3;
     for (int it = 0; it < rounds; ++it) {
+      rotate_priority(it, slot);
       step(g0, g2);
       step(g1, g0);
       step(g2, g1);
@@ -2068,17 +2091,17 @@ void stream_launch_nw(const nf4_gemv_desc* descs, const nf4_gemv_desc& single, i
 }
 
 // Rows of the contiguous static share each wave takes before it claims
-// chunks of C: half its even share, rounded down to whole chunks (at least
-// one).  Claimed chunks lie far apart in the row space, so nearly every one
-// starts another matrix, and a matrix with other activations makes the wave
-// reload them behind a full wait; a contiguous share crosses at most one or
-// two matrices.  The chunked other half still evens out the waves' unequal
-// progress.  Measured on the 192-matrix K = 4096 sweep launch with per-layer
-// activations (two boxes, two runs each): static shares of 1/4, 2/5, 1/2,
-// 11/20, 3/5 and 3/4 against one chunk (the previous scheme): 1/2 best, 442
-// -> 432 us and 433 -> 423 us; 3/4 slower than one chunk.
+// chunks of C: three quarters of its even share, rounded down to whole chunks
+// (at least one).  Every claim costs the claiming wave: the atomic's reply
+// returns in order with the wave's loads, and under a full memory stream it
+// holds up the loads issued after it.  With the rotating wave priority the
+// waves progress nearly evenly through their static shares, so the chunked
+// quarter is enough to even out the rest.  Measured on the 192-matrix K = 4096
+// sweep launch (three runs each): 1/2 static share without rotation 430 us,
+// with rotation 1/2 -> 421, 2/3 -> 421, 3/4 -> 418, 7/8 -> 429; the same
+// launch with the loads alone and a static split streams in 385 us.
 inline int dyn_static_rows(int64_t rows_per_wave, int C) {
-  const int64_t s = rows_per_wave / 2 / C * C;
+  const int64_t s = rows_per_wave * 3 / 4 / C * C;
   return s > C ? static_cast<int>(s) : C;
 }
 

@@ -508,7 +508,7 @@ class GemvGroup:
     scheduling launches through the format's single-matrix entry point
     (nf4_gemv, nf4_gemv_absmax32, int4_gemv): its kernels take the descriptor
     as a kernel argument, so their first weight loads do not wait for the
-    descriptor table to be read from memory (about 0.8 us per launch).  Such
+    descriptor table to be read from memory (0.3-1 us per launch).  Such
     a group's results come from the single-matrix kernels, within the same
     tolerance (the bits can differ from a grouped launch of the same matrix).
     """

@@ -51,7 +51,7 @@ CASES = [
     (4096, [(8192, 906), (256, 907)], 64),         # rows enough for the shared-activation kernel
     (1536, [(1536, 910), (256, 911), (8960, 912)], 64),
     (11008, [(300, 920), (5, 921)], 64),          # three 4096-column passes
-    (8192, [(200, 930)], 256),                     # two passes
+    (8192, [(200, 930), (7, 931)], 256),           # two passes
     (4160, [(64, 935), (3, 936)], 64),             # second pass: one 64-column block
     (12352, [(40, 950), (3, 951)], 64),            # four passes: the team kernel
     (96, [(33, 940), (7, 941)], 32),               # the team kernel only
@@ -62,9 +62,9 @@ CASES = [
 # shared-activation kernel, which serves these launches at batch 1-2.
 XLDS_CASES = [
     (11008, [(8192, 970), (300, 971)], 64),
-    (11008, [(8192, 972)], 128),
+    (11008, [(8192, 972), (3, 973)], 128),
     (8192, [(8192, 975), (40, 976)], 64),
-    (8192, [(8200, 977)], 128),
+    (8192, [(8200, 977), (5, 978)], 128),
 ]
 
 

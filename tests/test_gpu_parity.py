@@ -290,8 +290,8 @@ def _group_case(shapes_seeds, K, batch, x_seed):
     # block past it (no wave configuration: the team kernel)
     (8192, [(300, 640), (7, 641)]),
     (12288, [(40, 650), (9, 651)]),
-    (12352, [(33, 655)]),
-    (96, [(5, 630)]),
+    (12352, [(33, 655), (2, 656)]),
+    (96, [(5, 630), (3, 631)]),
 ])
 def test_gemv_grouped_matches_oracle(K, shapes, batch):
     qs, items = _group_case(shapes, K, batch, 700)
@@ -307,7 +307,7 @@ def test_gemv_grouped_matches_oracle(K, shapes, batch):
         assert ok, f"grouped N={N} K={K}: worst {worst:.3g}"
 
 
-@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
 @pytest.mark.parametrize("K,N", [(4096, 4096), (4096, 11008), (11008, 4096), (1536, 256)])
 def test_gemv_group_of_one_matrix(K, N, batch):
     """A group of one matrix launches through nf4_gemv (its descriptor in the

@@ -504,13 +504,16 @@ class GemvGroup:
     (no workspace tensor; launches on one GPU must not overlap in time).
     The table is checked on the host by nf4_gemv_desc_check before upload.
 
-    A group of one matrix at batch 1-2 whose rows are too few for chunked
-    scheduling launches through the format's single-matrix entry point
-    (nf4_gemv, nf4_gemv_absmax32, int4_gemv): its kernels take the descriptor
-    as a kernel argument, so their first weight loads do not wait for the
-    descriptor table to be read from memory (0.3-1 us per launch).  Such
-    a group's results come from the single-matrix kernels, within the same
-    tolerance (the bits can differ from a grouped launch of the same matrix).
+    A group of one matrix with fewer rows than 1024 per compute unit launches
+    through the format's single-matrix entry point (nf4_gemv,
+    nf4_gemv_absmax32, int4_gemv): its kernels take the descriptor as a kernel
+    argument, so their first weight loads do not wait for the descriptor
+    table to be read from memory (0.3-1 us per launch at batch 1-2), and at
+    batch 3-8 one matrix runs faster on the single-matrix team kernel than on
+    the grouped shared-activation kernel (11008 x 4096: 13.2 / 14.5 / 21.7 us
+    against 15.7 / 17.3 / 26.0 us at batch 3 / 4 / 8).  Such a group's
+    results come from the single-matrix kernels, within the same tolerance
+    (the bits can differ from a grouped launch of the same matrix).
     """
 
     def __init__(self, items, K: int, dynamic: bool = True, noalloc: bool = False):
@@ -589,12 +592,12 @@ class GemvGroup:
         self.noalloc = bool(noalloc)
         if self.noalloc and self.kind is not NF4Tensor:
             raise ValueError("noalloc grouped launches take NF4Tensor items only")
-        # chunked scheduling needs 64 rows per wave of a full grid (two
-        # 512-lane workgroups per compute unit)
+        # below 1024 rows per compute unit: chunked scheduling (64 rows per
+        # wave of a full grid of two 512-lane workgroups per compute unit)
+        # would not start, and the single-matrix kernels are faster
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         self.single = None
-        if len(self.items) == 1 and not self.noalloc and self.batch <= 2 and (
-                not dynamic or self.total_rows < 64 * 16 * cus):
+        if len(self.items) == 1 and not self.noalloc and self.total_rows < 64 * 16 * cus:
             self.single = self.items[0]
         self.sched = None
         if dynamic and not self.noalloc and self.single is None:

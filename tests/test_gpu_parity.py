@@ -220,6 +220,23 @@ def test_gemv_edge_shapes(N, K, bs, s2, batch):
     check_gemv(q, N, K, synth.activations(N + K + batch, batch, K))
 
 
+# One matrix at batch 3-8 with K <= 4096 takes the fp32-product team kernel
+# (16 columns per lane, one row per group at batch 3-4, two at 5-8): slabs cut
+# short by K, row counts that leave a group half empty, and small blocks.
+GEMV_FP32_PRODUCTS = [
+    # N, K, bs, s2
+    (37, 4096, 64, 256), (130, 1056, 32, 4), (9, 64, 64, 256), (515, 3072, 128, 2),
+    (2, 2048, 64, 1), (1, 4096, 4096, 1),
+]
+
+
+@pytest.mark.parametrize("N,K,bs,s2", GEMV_FP32_PRODUCTS)
+@pytest.mark.parametrize("batch", [3, 4, 5, 6, 7, 8])
+def test_gemv_fp32_products_batch3_to_8(N, K, bs, s2, batch):
+    q = oracle.quantize(synth.weights(N * 11 + K + 3, N * K, outliers=True), bs, s2)
+    check_gemv(q, N, K, synth.activations(N + 3 * K + batch, batch, K))
+
+
 @pytest.mark.parametrize("batch", [1, 4, 6, 7, 8])
 def test_gemv_unaligned_x(batch):
     N, K = 40, 4096

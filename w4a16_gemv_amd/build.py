@@ -47,6 +47,8 @@ NO_SPILL = (
     "gemv_xlds_kernel<1, 2, 3, 3, 2>",
     "dequant_vec_kernel<0, 4, 0>",
     "dequant_vec_kernel<1, 4, 0>",
+    "gemv_stream_kernel<4, 1, 4, 4, 0, true, 2, true>",
+    "gemv_stream_kernel<8, 2, 4, 2, 0, true, 2, true>",
 )
 RESOURCES = os.path.join(PKG, "kernel_resources.txt")
 REMARKS = "-Rpass-analysis=kernel-resource-usage"

@@ -470,7 +470,7 @@ struct LaneOffsets {
   uint32_t k0;
 };
 
-template <int R, int FMT>
+template <int R, int FMT, int LW = 4>
 __device__ __forceinline__ void load_row_group(RowGroup<R, FMT>& rg, const LoadBufs& mb, int rl,
                                                int len, const LaneOffsets& lo, int K, int log2bs,
                                                int log2s2) {
@@ -481,7 +481,13 @@ __device__ __forceinline__ void load_row_group(RowGroup<R, FMT>& rg, const LoadB
     const uint32_t srow = rr < len ? row * static_cast<uint32_t>(K >> 1) : kFar;
     const uint32_t sfar = rr < len ? 0u : kFar;
     const uint32_t blk = (row * static_cast<uint32_t>(K) + lo.k0) >> log2bs;
-    rg.pk[rr] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, lo.pk, srow, kStreamLoad);
+    if constexpr (LW == 4) {
+      rg.pk[rr] = __builtin_amdgcn_raw_buffer_load_b128(mb.packed, lo.pk, srow, kStreamLoad);
+    } else {  // 16 columns per lane: dwords 0 and 1
+      const uint2 v = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(mb.packed, lo.pk, srow, kStreamLoad));
+      rg.pk[rr] = u32x4{v.x, v.y, 0u, 0u};
+    }
     if constexpr (FMT == kFmtAbsmax32) {
       rg.q[rr] = __builtin_amdgcn_raw_buffer_load_b32(mb.absmax_q, blk * 4u, sfar, 0);
     } else if constexpr (FMT == kFmtInt4) {
@@ -494,14 +500,14 @@ __device__ __forceinline__ void load_row_group(RowGroup<R, FMT>& rg, const LoadB
   }
 }
 
-// The lane's 32 activations per batch row (raw bf16 pairs).
-template <int B>
+// The lane's 8 LW activations per batch row (raw bf16 pairs; dwords j < LW).
+template <int B, int LW = 4>
 __device__ __forceinline__ void load_x(u32x4 (&xr)[B][4], __amdgpu_buffer_rsrc_t xb,
                                        const LaneOffsets& lo, int K) {
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < LW; ++j)
       xr[b][j] = __builtin_amdgcn_raw_buffer_load_b128(xb, lo.x + 16u * j,
                                                         static_cast<uint32_t>(b * K * 2), 0);
 }
@@ -553,6 +559,46 @@ __device__ __forceinline__ void dot_columns(const RowGroup<R, FMT>& rg, const u3
       }
     }
   }
+}
+
+// The fp32 table: entry b = (NF4[b >> 4], NF4[b & 15]) as fp32 bits, even
+// column first, copies placed as in build_pair_table.
+__device__ __forceinline__ void build_f32_pair_table(uint2* s_pairs, int tid, int nthreads) {
+  for (int w = tid; w < 512; w += nthreads) {
+    const int b = w & 255, half = w >> 8;
+    const uint2 entry = make_uint2(__builtin_bit_cast(uint32_t, nf4_value(b >> 4)),
+                                   __builtin_bit_cast(uint32_t, nf4_value(b & 15)));
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s_pairs[b * kPairCopies + ((b + 16 * half + k) & 31)] = entry;
+  }
+}
+
+// part[rr][b] += the lane's 8 LW weights of row rr times their activations
+// in fp32: one table read per packed byte gives both NF4 values exactly, and
+// each product is one fp32 FMA (a wave64 v_fma_f32 issues in about 2/3 of
+// the time of a v_dot2c_f32_bf16, and one replaces the hi and lo dot2 pair).
+template <int B, int R, int LW, int FMT>
+__device__ __forceinline__ void dot_columns_f32(const RowGroup<R, FMT>& rg,
+                                                const float (&xf)[B][8 * LW], uint32_t copy_off,
+                                                const uint2* s_pairs, float (&part)[R][B]) {
+  const char* tab = reinterpret_cast<const char*>(s_pairs);
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+    for (int j = 0; j < LW; ++j) {
+      const uint32_t d = rg.pk[rr][j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t addr = __builtin_amdgcn_perm(copy_off, d, 0x0C0C0004u | (uint32_t(i) << 8));
+        const uint2 t = *reinterpret_cast<const uint2*>(tab + addr);
+        const float w0 = __builtin_bit_cast(float, t.x), w1 = __builtin_bit_cast(float, t.y);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          part[rr][b] = __builtin_fmaf(w0, xf[b][8 * j + 2 * i], part[rr][b]);
+          part[rr][b] = __builtin_fmaf(w1, xf[b][8 * j + 2 * i + 1], part[rr][b]);
+        }
+      }
+    }
 }
 
 // A descriptor the streaming kernel can read: 16-byte aligned packed weights
@@ -700,11 +746,17 @@ __device__ __forceinline__ int next_group(RowCursor& c, int r_end, const RowBegi
 // SINGLE: one matrix given by value (descs NULL, count 1), known at compile
 // time: no descriptor walk, no matrix or activation switches, so the loop
 // keeps far less scalar state.
-template <int B, int R, int NW, int WPE, int FMT = kFmtDouble, bool SINGLE = false>
+// LW: packed dwords per lane (8 LW columns, slabs of 512 LW columns).
+// XF (with LW = 2, one matrix at batch 3-8): the table holds each byte's two
+// NF4 values as exact fp32, the activations are widened to fp32 once, and
+// every product is one fp32 FMA instead of the hi and lo dot2 pair.
+template <int B, int R, int NW, int WPE, int FMT = kFmtDouble, bool SINGLE = false, int LW = 4,
+          bool XF = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemv_stream_kernel(
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
     int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2) {
-  constexpr int nw = NW;  // waves per team: one per 2048-column slab of K
+  constexpr int nw = NW;  // waves per team: one per slab of 512 LW columns of K
+  static_assert(!XF || FMT == kFmtDouble, "fp32 products: NF4 codes only");
   if constexpr (SINGLE) {
     descs = nullptr;
     count = 1;
@@ -728,7 +780,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   const int team = wave / nw;           // == teams for helper waves
   const int slab = wave - team * nw;
   const bool in_team = team < teams;
-  const int k0 = slab * kSlab + lane * 32;
+  const int k0 = slab * (512 * LW) + lane * (8 * LW);
   const bool active = in_team && k0 < K;
 
   // descriptor row offsets, code2 and the NF4 table into LDS
@@ -809,9 +861,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   lo.x = active ? static_cast<uint32_t>(k0 * 2) : kFar;
   lo.k0 = static_cast<uint32_t>(k0);
   RowGroup<R, FMT> g0, g1;
-  load_row_group<R, FMT>(g0, lb0, rl0, len0, lo, K, log2bs, log2s2);
+  load_row_group<R, FMT, LW>(g0, lb0, rl0, len0, lo, K, log2bs, log2s2);
   u32x4 xr[B][4];
-  load_x<B>(xr, x_buf<B>(d0, K), lo, K);
+  load_x<B, LW>(xr, x_buf<B>(d0, K), lo, K);
   float xs[B];  // INT4: the lane's activation sums (computed before the loop)
   int mL = m0;            // matrix of lbL
   LoadBufs lbL = lb0;
@@ -822,18 +874,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     ob1 = out_bufs<B>(d1);
     mL = m1;
   }
-  load_row_group<R, FMT>(g1, lbL, rl1, len1, lo, K, log2bs, log2s2);
+  load_row_group<R, FMT, LW>(g1, lbL, rl1, len1, lo, K, log2bs, log2s2);
 
   // the 256 x 32 pair table: (bf16 hi pair, bf16 lo pair) of each byte
   if (FMT == kFmtDouble && tid < 256) s_code2[tid] = f16_to_f32(code2_bits);
-  const uint32_t copy_off = build_decode_table<FMT>(s_pairs, tid, blockDim.x, lane);
+  uint32_t copy_off;
+  if constexpr (XF) {
+    build_f32_pair_table(s_pairs, tid, blockDim.x);
+    copy_off = static_cast<uint32_t>(lane % kPairCopies) * 8u;
+  } else {
+    copy_off = build_decode_table<FMT>(s_pairs, tid, blockDim.x, lane);
+  }
+  // XF: the lane's activations widened to fp32 once (even column: low half)
+  float xf[XF ? B : 1][XF ? 8 * LW : 1];
+  if constexpr (XF) {
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb)
+#pragma unroll
+      for (int j = 0; j < LW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = xr[bb][j][i];
+          xf[bb][8 * j + 2 * i] = __builtin_bit_cast(float, w << 16);
+          xf[bb][8 * j + 2 * i + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+        }
+  }
   auto sum_x = [&]() {
     if constexpr (FMT == kFmtInt4) {
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        uint32_t w[16];
+        uint32_t w[4 * LW];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < LW; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) w[4 * j + i] = xr[b][j][i];
         xs[b] = pair_sum(w);
@@ -861,7 +933,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
       ob2 = out_bufs<B>(d2);
       mL = m2;
     }
-    load_row_group<R, FMT>(fut, lbL, rl2, len2, lo, K, log2bs, log2s2);
+    load_row_group<R, FMT, LW>(fut, lbL, rl2, len2, lo, K, log2bs, log2s2);
     // issue these loads here: sunk below the first wait for the current group
     // they would turn that wait into a wait for the group after it as well
     __builtin_amdgcn_sched_barrier(0);
@@ -876,8 +948,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     for (int rr = 0; rr < R; ++rr)
 #pragma unroll
       for (int b = 0; b < B; ++b) part[rr][b] = 0.0f;
+    if constexpr (XF) {
+      dot_columns_f32<B, R, LW, FMT>(cur, xf, copy_off, s_pairs, part);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dot_columns<B, R, FMT>(cur, xr, j, copy_off, s_pairs, part);
+      for (int j = 0; j < LW; ++j) dot_columns<B, R, FMT>(cur, xr, j, copy_off, s_pairs, part);
+    }
     float val[R * B];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
@@ -932,7 +1008,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     // the next group starts a new matrix: fetch its activations now that the
     // current ones are no longer needed
     if (!SINGLE && len1 > 0 && m1 != m0) {
-      load_x<B>(xr, x_buf<B>(open_desc<FMT>(descs, single, m1, len1, rbeg, K), K), lo, K);
+      load_x<B, LW>(xr, x_buf<B>(open_desc<FMT>(descs, single, m1, len1, rbeg, K), K), lo, K);
       // drain here (rare: once per matrix change) so that the loads of this
       // branch are not assumed outstanding on the common path, where they
       // would make every wait for the current group also wait for the next
@@ -2240,6 +2316,35 @@ nf4_status stream_launch(const nf4_gemv_desc* descs, const nf4_gemv_desc& single
           wave_dispatch<B, FMT>(descs, single, count, total_rows, K, lbs, ls2, code2, sched,
                                 sched_clear, st);
       if (ws != NF4_EUNSUPPORTED) return ws;
+    }
+  }
+  // one matrix at batch 3-8 with K <= 4096: fp32 products (see
+  // dot_columns_f32) with 16 columns per lane, so the fp32 activations take
+  // 16 B VGPRs; one row per group at batch 3-4, two at 5-8
+  if constexpr (B >= 3 && FMT == kFmtDouble) {
+    if (descs == nullptr && K <= 4096) {
+      constexpr int RX = B <= 4 ? 1 : 2;
+      constexpr int WX = B <= 4 ? 4 : 2;
+      const int nwx = (K + 1023) / 1024;
+      const int teams_x = 8 / nwx;
+      const int64_t cap = static_cast<int64_t>(device_cus()) * (WX / 2);
+      const int64_t want_x = (static_cast<int64_t>(total_rows) + teams_x * RX - 1) / (teams_x * RX);
+      const int64_t gx = want_x < cap ? (want_x > 0 ? want_x : 1) : cap;
+      const dim3 g(static_cast<uint32_t>(gx)), blk(512);
+      switch (nwx) {
+#define NF4_XF_CASE(NWX)                                                                          \
+  case NWX:                                                                                       \
+    hipLaunchKernelGGL((gemv_stream_kernel<B, RX, NWX, WX, FMT, true, 2, true>), g, blk, 0, st,   \
+                       nullptr, single, 1, total_rows, K, lbs, ls2, code2);                       \
+    break;
+        NF4_XF_CASE(1)
+        NF4_XF_CASE(2)
+        NF4_XF_CASE(3)
+        NF4_XF_CASE(4)
+#undef NF4_XF_CASE
+        default: return NF4_EUNSUPPORTED;
+      }
+      return launch_status();
     }
   }
   const int nw = (K + kSlab - 1) / kSlab;

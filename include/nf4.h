@@ -113,8 +113,9 @@ nf4_status nf4_dequant(const uint8_t* packed, const uint8_t* absmax_q, const uin
  *                  the fp32 sum rounded to nearest even.
  *  stream        : hipStream_t.
  * Weights are never rounded to 16 bits: each NF4 value enters the products
- * as the sum of two bf16 values (within 2^-16 of its fp32 value), the block
- * scale is applied in fp32, and the sum is accumulated in fp32: each output
+ * as its exact fp32 value (one matrix at batch 3-8 with K <= 4096) or as the
+ * sum of two bf16 values (within 2^-16 of its fp32 value), the block scale is
+ * applied in fp32, and the sum is accumulated in fp32: each output
  * is the bf16 rounding (nearest even)
  * of a value within 2^-14 * sum_k |w x| of the exact sum, so
  * |y - exact| <= 2^-8 |exact| + (1 + 2^-8) 2^-14 sum_k |w x|.  Deterministic:

@@ -76,8 +76,9 @@ METRIC = "NF4 dequant & fused GEMV: achieved HBM GB/s and % of MI355X peak (1 GP
 # what the path computes in: the GEMV multiplies bf16 activations by each
 # weight written exactly as two bf16 terms (hi + lo, within 2^-16 of the fp32
 # weight) with fp32 accumulation; the dequant computes in fp32 and rounds once
-DTYPE_NOTE = ("GEMV: bf16 x bf16 products (weight as an exact hi + lo bf16 pair), fp32 "
-              "accumulation, bf16 y; dequant: fp32 arithmetic, RNE to bf16")
+DTYPE_NOTE = ("GEMV: bf16 x bf16 products (weight as an exact hi + lo bf16 pair; single "
+              "launches at batch 3-8 with K <= 4096: exact fp32 weight x widened bf16 activation "
+              "in fp32 FMAs), fp32 accumulation, bf16 y; dequant: fp32 arithmetic, RNE to bf16")
 
 
 def log(*a):

@@ -756,7 +756,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     const nf4_gemv_desc* __restrict__ descs, nf4_gemv_desc single, int count, int total_rows,
     int K, int log2bs, int log2s2, const uint16_t* __restrict__ code2) {
   constexpr int nw = NW;  // waves per team: one per slab of 512 LW columns of K
-  static_assert(!XF || FMT == kFmtDouble, "fp32 products: NF4 codes only");
+  // (XF widens the activations once: a launch over several matrices would
+  // have to widen them again at every switch)
+  static_assert(!XF || (SINGLE && LW == 2 && FMT == kFmtDouble),
+                "fp32 products: one matrix, NF4 codes, 16 columns per lane");
   if constexpr (SINGLE) {
     descs = nullptr;
     count = 1;

@@ -2148,10 +2148,12 @@ nf4_status dequant_launch(const uint8_t* packed, const uint8_t* absmax_q, const 
 
 // rows per group: 4 at batch 1, 2 at batch 2 (four values per wave
 // reduction; with prefetch depth 2 this stays within the 128 VGPRs of four
-// waves per SIMD), 1 above.  Waves per SIMD: the activations take 16 B VGPRs,
-// so batches above 4 run at two waves per SIMD (one workgroup per CU).
+// waves per SIMD), 1 at batch 3-4, 2 at batch 5-8 (half the reductions and
+// barriers per row; 192-249 VGPRs, within the two waves per SIMD these
+// batches run at).  Waves per SIMD: the activations take 16 B VGPRs, so
+// batches above 4 run at two waves per SIMD (one workgroup per CU).
 template <int B>
-constexpr int stream_rows() { return B == 1 ? 4 : (B == 2 ? 2 : 1); }
+constexpr int stream_rows() { return B == 1 ? 4 : (B == 2 ? 2 : (B >= 5 ? 2 : 1)); }
 template <int B>
 constexpr int stream_wpe() { return B <= 4 ? 4 : 2; }
 

@@ -30,7 +30,8 @@ dequant in the single-level and INT4 formats, grouped launches of
 nf4_gemv_grouped_absmax32 / int4_gemv_grouped; no CPU baseline), dequant_1k /
 dequant_4k (1024^2 and 4096^2 bf16 dequant), qwen_b1 (the 7 Qwen2.5-1.5B-shaped GEMVs),
 qwen_b1_grouped (the same 7 as 4 launches: q/k/v and gate/up grouped), llama_b1 / llama_b4 /
-llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8), llama_b16 / llama_b64
+llama_b8 (the 3 Llama-7B-shaped GEMVs at batch 1, 4, 8; llama_b2 / b3 / b5 / b6 / b7 at
+the other batches), llama_b16 / llama_b64
 / llama_b128 (the same 3 matrices times 16, 64, 128 activation rows through
 nf4_gemm, the matrix-core product; roofline against the bf16 MFMA peak), and
 each of the first six with the suffix _absmax32 for the single-level format (one fp32 absmax per
@@ -65,6 +66,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 CONTEXT_WORKLOADS = ("dequant_1k", "dequant_4k", "qwen_b1", "llama_b1", "llama_b4", "llama_b8")
+# the same Llama-shaped GEMVs at the other batches of the GEMV (nf4 format only)
+LLAMA_OTHER_BATCHES = ("llama_b2", "llama_b3", "llama_b5", "llama_b6", "llama_b7")
 # the Qwen2.5-1.5B layer in four launches: q/k/v grouped, o, gate/up grouped,
 # down (double-quantized format)
 GROUPED_WORKLOADS = ("qwen_b1_grouped",)
@@ -666,7 +669,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--schedule", choices=("stream", "layered"), default="stream")
     ap.add_argument("--workload", default="sweep",
-                    choices=SWEEP_WORKLOADS + CONTEXT_WORKLOADS + GEMM_WORKLOADS + GROUPED_WORKLOADS
+                    choices=SWEEP_WORKLOADS + CONTEXT_WORKLOADS + LLAMA_OTHER_BATCHES + GEMM_WORKLOADS
+                    + GROUPED_WORKLOADS
                     + tuple(w + "_absmax32" for w in CONTEXT_WORKLOADS)
                     + tuple(w + "_int4" for w in CONTEXT_WORKLOADS))
     ap.add_argument("--blocksize", type=int, default=None,

@@ -510,8 +510,11 @@ class GemvGroup:
     argument, so their first weight loads do not wait for the descriptor
     table to be read from memory (0.3-1 us per launch at batch 1-2), and at
     batch 3-8 one matrix runs faster on the single-matrix team kernel than on
-    the grouped shared-activation kernel (11008 x 4096: 13.2 / 14.5 / 21.7 us
-    against 15.7 / 17.3 / 26.0 us at batch 3 / 4 / 8).  Such a group's
+    the grouped shared-activation kernel (11008 x 4096: 11.8 / 12.8 / 20.0 us
+    against 15.7 / 17.3 / 26.0 us at batch 3 / 4 / 8).  Groups of two or more
+    matrices stay one grouped launch, which is faster than their single
+    launches at every batch (2 x 11008 x 4096 at batch 8: 39.3 against
+    42.5 us; 3 x 4096 x 4096: 26.3 against 30.2 us).  Such a group's
     results come from the single-matrix kernels, within the same tolerance
     (the bits can differ from a grouped launch of the same matrix).
     """

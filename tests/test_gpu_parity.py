@@ -237,6 +237,25 @@ def test_gemv_fp32_products_batch3_to_8(N, K, bs, s2, batch):
     check_gemv(q, N, K, synth.activations(N + 3 * K + batch, batch, K))
 
 
+@pytest.mark.parametrize("scale", [1e-36, 1e-39])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_gemv_tiny_activations(scale, batch):
+    """Activations near and below the smallest normal bf16 (1e-39: most are
+    bf16 subnormals, and so are the outputs): the dot2 decode (batch 1-2) and
+    the fp32-product decode (batch 4, 8) both stay within the bf16 rounding
+    of the tolerance band (on the subnormal grid that band is wide in
+    relative terms)."""
+    N, K = 64, 4096
+    q = oracle.quantize(synth.weights(5, N * K))
+    xf = (np.random.default_rng(batch).standard_normal((batch, K)) * scale).astype(np.float32)
+    xb = oracle.bf16_from_f32(xf).reshape(batch, K)
+    y = run_gemv(q, N, K, xb)
+    yr, S = oracle.gemv(q, N, K, xb, None)
+    ok, _ = G.gemv_within_tolerance(y, yr, S)
+    assert ok, f"scale {scale} batch {batch}"
+    assert np.count_nonzero(yr) > 0
+
+
 @pytest.mark.parametrize("batch", [1, 4, 6, 7, 8])
 def test_gemv_unaligned_x(batch):
     N, K = 40, 4096
